@@ -1,0 +1,122 @@
+"""Python face of the CPU oracle (``oracle.c``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the bench's
+CPU-baseline leg are the only callers.  The product path never imports this
+package.  Arrays are numpy: fp32 activations as ``float32``, bf16 activations as
+their raw bits in ``uint16``.  Every function returns the status code of the
+call (0 on success) and writes its outputs into the arrays passed in, exactly
+as the C functions do.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+F32, BF16 = 0, 1
+
+OK, INVALID_ARGUMENT, SLOT_OUT_OF_RANGE, SLOT_SHARED, RUN_LENGTHS = 0, 1, 2, 3, 4
+
+
+def build(force: bool = False) -> str:
+    """Compile oracle.c with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(
+            ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
+             _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        vp, i32, f32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        L.oracle_conv1d.argtypes = [vp, vp, vp, vp, vp, i32, i32, vp, vp, vp, i32, i32, i32, i32]
+        L.oracle_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
+                                  i32, i32, i32, i32, i32, i32, vp, i32]
+        L.oracle_gated_rmsnorm.argtypes = [vp, vp, vp, vp, i32, f32, i32, i32, i32]
+        L.oracle_check_batch.argtypes = [i32, i32, vp, vp, i32, i32]
+        for f in (L.oracle_conv1d, L.oracle_scan, L.oracle_gated_rmsnorm, L.oracle_check_batch,
+                  L.oracle_max_threads):
+            f.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [i32]
+        L.oracle_set_threads.restype = None
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    if a is None:
+        return None
+    assert isinstance(a, np.ndarray) and a.flags.c_contiguous, "oracle arrays must be C-contiguous numpy"
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _act_of(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return F32
+    if a.dtype == np.uint16:
+        return BF16
+    raise TypeError("activations are float32 or uint16 (bf16 bits), got %s" % a.dtype)
+
+
+def _batch(run_lengths, slots, fresh):
+    rl = np.ascontiguousarray(run_lengths, dtype=np.int32)
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    fr = np.ascontiguousarray(fresh, dtype=np.uint8)
+    return rl, sl, fr
+
+
+def conv1d(dst, x, weight, bias, conv_state, run_lengths, slots, fresh) -> int:
+    """CausalConv1D: dst, x [T, Dc] act; weight [Dc, K] f32; bias [Dc] f32;
+    conv_state [M, K-1, Dc] act (updated in place)."""
+    rl, sl, fr = _batch(run_lengths, slots, fresh)
+    Dc = x.shape[1]
+    K = weight.shape[1]
+    M = conv_state.shape[0]
+    return lib().oracle_conv1d(_p(dst), _p(x), _p(weight), _p(bias), _p(conv_state), len(rl),
+                               x.shape[0], _p(rl), _p(sl), _p(fr), Dc, K, M, _act_of(x))
+
+
+def scan(y, xbc, dt, a_log, dt_bias, d, ssm_state, run_lengths, slots, fresh, ngroups,
+         head_mask=None, decode=False) -> int:
+    """SSMScan: y [T, H*P] act; xbc [T, H*P + 2*G*N] act; dt [T, H] act; a_log, dt_bias,
+    d [H] f32; ssm_state [M, H, P, N] f32 (updated in place)."""
+    rl, sl, fr = _batch(run_lengths, slots, fresh)
+    M, H, P, N = ssm_state.shape
+    hm = None if head_mask is None else np.ascontiguousarray(head_mask, dtype=np.uint8)
+    return lib().oracle_scan(_p(y), _p(xbc), _p(dt), _p(a_log), _p(dt_bias), _p(d), _p(ssm_state),
+                             len(rl), xbc.shape[0], _p(rl), _p(sl), _p(fr), H, P, N, ngroups, M,
+                             _act_of(xbc), _p(hm), 1 if decode else 0)
+
+
+def gated_rmsnorm(dst, x, z, weight, groups, eps) -> int:
+    """GatedRMSNorm: dst, x, z [rows, Di] act; weight [Di] f32."""
+    return lib().oracle_gated_rmsnorm(_p(dst), _p(x), _p(z), _p(weight), int(groups), float(eps),
+                                      x.shape[0], x.shape[1], _act_of(x))
+
+
+def check_batch(num_rows, run_lengths, slots, pool_slots, decode=False) -> int:
+    rl, sl, _ = _batch(run_lengths, slots, np.zeros(len(run_lengths)))
+    return lib().oracle_check_batch(len(rl), num_rows, _p(rl), _p(sl), pool_slots, 1 if decode else 0)
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(int(n))
