@@ -1,0 +1,259 @@
+"""Benchmark of the Mamba2 mixer hot path on one MI355X.
+
+One step = one pass of the whole prefill path (causal conv1d + SiLU, chunked selective
+scan, gated RMSNorm) over the long-prefill batch: 4 fresh sequences x 16384 rows, 48 heads
+x headdim 64, d_state 128, one B/C group, conv kernel 4, norm over 8 groups, bf16
+activations, fp32 states.  ``value`` is prefill tokens/s.  The decode half of the metric is
+timed on the batched-decode workload (256 one-row requests on a 512-slot pool, 64
+successive steps of conv + decode scan + norm) and reported as ``decode_us_per_step``.
+
+Inputs are seeded synthetic tensors resident in HBM before the timed region.  Per-kernel
+durations come from HIP events the library records on the launch stream; the roofline
+object uses the dominant kernel's algorithmic bytes (or flops) per launch over its average
+duration.  The CPU oracle is timed on a bounded sample on the host cores as a reported
+baseline.  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    return ap.parse_args()
+
+
+def kernel_bytes_flops(name, wl, nrows):
+    """Algorithmic bytes (and flops) one launch of `name` must move on this workload."""
+    sh = wl.shape
+    a = 2 if sh.act == "bf16" else 4
+    T, Dc, Di, H, P, N, G = nrows, sh.conv_dim, sh.d_inner, sh.nheads, sh.headdim, sh.d_state, sh.ngroups
+    S = len(wl.run_lengths)
+    resumed = int((wl.fresh == 0).sum())
+    if name == "conv1d_silu":
+        return 2 * T * Dc * a + (S + resumed) * (sh.conv_kernel - 1) * Dc * a, 0
+    if name in ("ssd_scan", "ssd_generic_scan"):
+        q = 64
+        flops = T * H * (N * (q + 1) / (H // G) + P * (q + 1) + 4 * N * P)
+        return T * (Dc + H + Di) * a + (S + resumed) * H * P * N * 4, flops
+    if name in ("gated_rmsnorm", "gated_rmsnorm_wide"):
+        return 3 * T * Di * a + Di * 4, 0
+    if name == "scan_decode":
+        return (T * (Dc + H + Di) * a + (S + resumed) * H * P * N * 4), 6 * T * H * P * N
+    return None, None
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: every box here has one MI355X and this path has no "
+              "multi-GPU part (--gpus %d is not supported)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from mamba2_selective_scan_causalconv1d_amd import ops
+    from mamba2_selective_scan_causalconv1d_amd import workloads as W
+
+    dev = "cuda"
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    t_gen = time.time()
+    wl = W.long_prefill()
+    sh = wl.shape
+    T = wl.num_rows
+    dims = ops.make_dims(sh.nheads, sh.headdim, sh.d_state, sh.ngroups, sh.conv_kernel, sh.chunk_size,
+                         sh.pool_slots, sh.act)
+    d = ops.to_device
+    conv_w, conv_b, a_log, dt_bias, D, norm_w = (d(wl.conv_w), d(wl.conv_b), d(wl.a_log), d(wl.dt_bias),
+                                                 d(wl.D), d(wl.norm_w))
+    xbc, z, dt = d(wl.xbc), d(wl.z), d(wl.dt)
+    conv_pool, ssm_pool = d(wl.conv_pool), d(wl.ssm_pool)
+    batch = ops.RecurrentBatch(wl.run_lengths, wl.slots, wl.fresh, device=dev)
+    xa = torch.empty_like(xbc)
+    y = torch.empty((T, sh.d_inner), dtype=xbc.dtype, device=dev)
+    out = torch.empty_like(y)
+    ws = torch.empty(max(256, ops.scan_prefill_workspace_bytes(batch, dims)), dtype=torch.uint8, device=dev)
+    print("bench: inputs ready in %.1fs (T=%d, workspace %.1f MB)" % (time.time() - t_gen, T, ws.numel() / 1e6),
+          file=sys.stderr, flush=True)
+
+    def step():
+        ops.conv1d(xa, xbc, conv_w, conv_b, conv_pool, batch, dims)
+        ops.scan_prefill(y, xa, dt, a_log, dt_bias, D, ssm_pool, batch, dims, workspace=ws)
+        ops.gated_rmsnorm(out, y, z, norm_w, sh.norm_groups, sh.eps)
+
+    # parity digest of the timed output (all-fresh batch: every step recomputes the same result)
+    step()
+    torch.cuda.synchronize()
+    ref_digest = (float(out.float().sum().item()), float(y.float().abs().sum().item()))
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_per_step = e0.elapsed_time(e1) / args.steps
+    digest = (float(out.float().sum().item()), float(y.float().abs().sum().item()))
+    assert digest == ref_digest, "timed output differs from the parity run: %s vs %s" % (digest, ref_digest)
+
+    # per-kernel durations (HIP events recorded by the library on the launch stream)
+    ops.timing_enable(64 * max(1, args.steps))
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    recs = ops.timing_collect(64 * max(1, args.steps))
+    ops.timing_enable(0)
+    per = {}
+    for name, ms in recs:
+        per.setdefault(name, []).append(ms)
+    kernels = {k: {"avg_us": 1e3 * float(np.mean(v)), "launches_per_step": len(v) / args.steps}
+               for k, v in per.items()}
+    rooflines = {}
+    for k, v in kernels.items():
+        nbytes, flops = kernel_bytes_flops(k, wl, T)
+        if nbytes is None:
+            continue
+        sec = v["avg_us"] * 1e-6
+        r = {"achieved_GBs": nbytes / sec / 1e9, "frac_hbm": nbytes / sec / 1e9 / HBM_PEAK_GBS,
+             "alg_bytes": nbytes}
+        if flops:
+            r["achieved_TFLOPs"] = flops / sec / 1e12
+            r["frac_mfma"] = flops / sec / 1e12 / MFMA_BF16_PEAK_TFLOPS
+            r["alg_flops"] = flops
+        rooflines[k] = r
+    dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
+    dr = rooflines.get(dom, {})
+    roofline = {"kernel": dom, "bound": "hbm", "achieved": dr.get("achieved_GBs"), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": dr.get("frac_hbm"), "traffic": None,
+                "avg_us": kernels[dom]["avg_us"]}
+
+    # ---------------------------------------------------------------- decode
+    dwl = W.decode_batch()
+    dsh = dwl.shape
+    ddims = ops.make_dims(dsh.nheads, dsh.headdim, dsh.d_state, dsh.ngroups, dsh.conv_kernel, dsh.chunk_size,
+                          dsh.pool_slots, dsh.act)
+    dparams = [d(a) for a in (dwl.conv_w, dwl.conv_b, dwl.a_log, dwl.dt_bias, dwl.D, dwl.norm_w)]
+    dsteps = [tuple(d(a) for a in s) for s in dwl.steps]
+    pristine_conv, pristine_ssm = d(dwl.conv_pool), d(dwl.ssm_pool)
+    cpool, spool = pristine_conv.clone(), pristine_ssm.clone()
+    b0 = ops.RecurrentBatch(dwl.run_lengths, dwl.slots, dwl.fresh, device=dev)
+    b1 = ops.RecurrentBatch(dwl.run_lengths, dwl.slots, np.zeros_like(dwl.fresh), device=dev)
+    R = len(dwl.run_lengths)
+    dxa = torch.empty((R, dsh.conv_dim), dtype=torch.bfloat16, device=dev)
+    dy = torch.empty((R, dsh.d_inner), dtype=torch.bfloat16, device=dev)
+    dout = torch.empty_like(dy)
+
+    def decode_run():
+        cw, cb, al, db, DD, nw = dparams
+        for i, (x, zz, dd) in enumerate(dsteps):
+            b = b0 if i == 0 else b1
+            ops.conv1d(dxa, x, cw, cb, cpool, b, ddims)
+            ops.scan_decode(dy, dxa, dd, al, db, DD, spool, b, ddims)
+            ops.gated_rmsnorm(dout, dy, zz, nw, dsh.norm_groups, dsh.eps)
+
+    decode_run()  # warm-up on a scratch copy of the pools
+    torch.cuda.synchronize()
+    dref = float(dout.float().sum().item())
+    times = []
+    for _ in range(max(1, args.decode_reps)):
+        cpool.copy_(pristine_conv)
+        spool.copy_(pristine_ssm)
+        torch.cuda.synchronize()
+        e0.record()
+        decode_run()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+        assert float(dout.float().sum().item()) == dref
+    decode_us = 1e3 * float(np.median(times)) / len(dsteps)
+    cpool.copy_(pristine_conv)
+    spool.copy_(pristine_ssm)
+    ops.timing_enable(4096)
+    decode_run()
+    torch.cuda.synchronize()
+    drecs = ops.timing_collect(4096)
+    ops.timing_enable(0)
+    dper = {}
+    for name, ms in drecs:
+        dper.setdefault(name, []).append(ms)
+    dkern = {k: {"avg_us": 1e3 * float(np.mean(v)), "launches_per_step": len(v) / len(dsteps)}
+             for k, v in dper.items()}
+    dec_bytes, _ = kernel_bytes_flops("scan_decode", dwl, R)
+    # steps 1..63 read every slot (none fresh): algorithmic bytes of a resumed step
+    dec_bytes = R * (dsh.conv_dim + dsh.nheads + dsh.d_inner) * 2 + 2 * R * dsh.nheads * dsh.headdim * dsh.d_state * 4
+    dec_roof = {"kernel": "scan_decode", "achieved_GBs": dec_bytes / (dkern["scan_decode"]["avg_us"] * 1e-6) / 1e9}
+    dec_roof["frac_hbm"] = dec_roof["achieved_GBs"] / HBM_PEAK_GBS
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        L = min(args.cpu_sample_rows, int(wl.run_lengths[0]))
+        sub = W.Workload(wl.name, wl.seed, sh, np.array([L], np.int32), np.array([0], np.int32),
+                         np.array([1], np.uint8), wl.conv_w, wl.conv_b, wl.dt_bias, wl.a_log, wl.D, wl.norm_w,
+                         wl.conv_pool[:1].copy(), wl.ssm_pool[:1].copy(), np.ascontiguousarray(wl.xbc[:L]),
+                         np.ascontiguousarray(wl.z[:L]), np.ascontiguousarray(wl.dt[:L]))
+        t0 = time.perf_counter()
+        oa = np.zeros_like(sub.xbc)
+        cp = sub.conv_pool.copy()
+        assert oracle.conv1d(oa, sub.xbc, sub.conv_w, sub.conv_b, cp, sub.run_lengths, sub.slots, sub.fresh) == 0
+        oy = np.zeros((L, sh.d_inner), dtype=sub.xbc.dtype)
+        sp = sub.ssm_pool.copy()
+        assert oracle.scan(oy, oa, sub.dt, sub.a_log, sub.dt_bias, sub.D, sp, sub.run_lengths, sub.slots,
+                           sub.fresh, sh.ngroups) == 0
+        oo = np.zeros_like(oy)
+        assert oracle.gated_rmsnorm(oo, oy, sub.z, sub.norm_w, sh.norm_groups, sh.eps) == 0
+        dt_cpu = time.perf_counter() - t0
+        cpu = {"value": L / dt_cpu, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+               "sample": "first %d rows of one long-prefill sequence (all 48 heads, conv+scan+norm), %.1fs"
+                         % (L, dt_cpu)}
+
+    res = {
+        "metric": "Mamba2 mixer prefill tokens/s + decode us/step; % of HBM/MFMA roofline",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long_prefill_4x16384", "global_batch": 4, "seq_len": 16384, "nheads": 48,
+                   "headdim": 64, "d_state": 128, "ngroups": 1, "conv_kernel": 4, "norm_groups": 8,
+                   "parallelism": "single_gpu"},
+        "decode_us_per_step": decode_us,
+        "decode_config": {"workload": "decode_256x64", "requests": R, "pool_slots": dsh.pool_slots,
+                          "steps": len(dsteps)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "rooflines": rooflines,
+        "decode_kernels": dkern,
+        "decode_roofline": dec_roof,
+    }
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,201 @@
+/*
+ * mamba2.h - C ABI of the Mamba2 mixer hot path on AMD Instinct MI355X (gfx950).
+ *
+ * The path, as the page "feat(backend): Mamba2 ops, with CPU reference
+ * implementations" (gllm PR #85) defines it in its section "Ops":
+ *
+ *   1. CausalConv1D: a depthwise causal conv over each sequence's run of rows,
+ *      fused with SiLU, preceded by the sequence's last kernel-1 inputs from its
+ *      conv-state slot (zeros when fresh); the slot then holds the last kernel-1
+ *      inputs.                                             -> mamba2_conv1d
+ *   2. SSMScan: dt' = softplus(dt + dt_bias) (no clamp), per token
+ *      h = h * exp(-exp(A_log) * dt') + dt' * B (x) x and y = h . C + D * x, head h
+ *      reading B and C of group h / (heads / groups), the state seeded from and
+ *      written back to the sequence's SSM slot.     -> mamba2_scan_prefill (a
+ *      chunked parallel scan over packed variable-length runs) and
+ *      mamba2_scan_decode (one row per sequence).
+ *   3. GatedRMSNorm: rmsnorm(x * silu(z)) * weight, the RMS taken per group.
+ *                                                      -> mamba2_gated_rmsnorm
+ *
+ * The stateful calls take a mamba2_recurrent_batch: per sequence its run length,
+ * slot and fresh flag (same page, section "Ops": a fresh sequence starts from
+ * zero and never reads its slot; a slot out of range, a slot shared by two
+ * sequences and run lengths that do not cover the rows are rejected).
+ *
+ * Conventions for every call
+ *   - Memory: the caller allocates every buffer; the library keeps no pointer
+ *     past the call and allocates no device memory.  "device" pointers are HIP
+ *     device memory; "host" pointers are read during the call only.
+ *   - Layout: row-major, last index contiguous.  An xBC row is
+ *     [x (H*P, head h at h*P+p) | B (G*N, group g at g*N+n) | C (G*N)],
+ *     Dc = H*P + 2*G*N channels; Di = H*P.
+ *   - Types: activations, conv state and outputs in the activation type
+ *     (MAMBA2_DTYPE_F32 or MAMBA2_DTYPE_BF16; bf16 as its 16 raw bits); SSM
+ *     state, weights, biases, A_log, dt_bias and D are fp32.
+ *   - Mutation: only the output and the named state slots are written; inputs
+ *     are never written; the output must not alias any input; slots not named by
+ *     the batch are left bit-identical.
+ *   - Errors: every check runs on the host before the first launch.  On error
+ *     nothing is enqueued and nothing is written.  No call throws.
+ *   - Streams: calls only enqueue on `stream` (a hipStream_t; NULL is the null
+ *     stream) and return; no host synchronisation, no allocation, no copy.
+ *     Device buffers must stay valid until the stream work completes.
+ */
+#ifndef MAMBA2_H
+#define MAMBA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum mamba2_status {
+  MAMBA2_OK = 0,
+  MAMBA2_INVALID_ARGUMENT = 1,   /* null pointer, bad dims or dtype, bad groups/eps */
+  MAMBA2_SLOT_OUT_OF_RANGE = 2,  /* a slot < 0 or >= pool_slots */
+  MAMBA2_SLOT_SHARED = 3,        /* two sequences of one batch name the same slot */
+  MAMBA2_RUN_LENGTHS = 4,        /* a length <= 0, sum != num_rows, or decode length != 1 */
+  MAMBA2_WORKSPACE_TOO_SMALL = 5,
+  MAMBA2_NOT_IMPLEMENTED = 6,    /* valid dims the kernels do not cover */
+  MAMBA2_HIP_ERROR = 7           /* the runtime reported a launch failure */
+} mamba2_status;
+
+typedef enum mamba2_dtype { MAMBA2_DTYPE_F32 = 0, MAMBA2_DTYPE_BF16 = 1 } mamba2_dtype;
+
+/* Sizes of one mixer layer. */
+typedef struct mamba2_dims {
+  int32_t nheads;      /* H >= 1 */
+  int32_t headdim;     /* P >= 1 */
+  int32_t d_state;     /* N >= 1 */
+  int32_t ngroups;     /* G >= 1, H % G == 0 */
+  int32_t conv_kernel; /* K, 2..4; the conv state holds K-1 rows */
+  int32_t chunk_size;  /* Q >= 1: chunk length of the chunked scan (see mamba2_scan_prefill) */
+  int32_t pool_slots;  /* M >= 0: slots in each state pool */
+  int32_t act_dtype;   /* mamba2_dtype of activations, outputs and conv state */
+} mamba2_dims;
+
+/*
+ * One batch of sequences, packed row after row in cu_seqlens order.
+ * The host arrays are validated; the device arrays are what the kernels read
+ * and must hold the same values (dev_cu_seqlens[s] = sum of run_lengths[0..s),
+ * dev_cu_seqlens[S] = num_rows).  The library does not read device arrays on
+ * the host, so a mismatch between the two copies is the caller's error.
+ */
+typedef struct mamba2_recurrent_batch {
+  int32_t num_seqs;               /* S >= 0 */
+  int32_t num_rows;               /* T = sum of run_lengths */
+  const int32_t* run_lengths;     /* host   [S], each >= 1 */
+  const int32_t* slots;           /* host   [S], distinct, in [0, pool_slots) */
+  const uint8_t* fresh;           /* host   [S], nonzero: start from zero, never read the slot */
+  const int32_t* dev_cu_seqlens;  /* device [S+1] */
+  const int32_t* dev_slots;       /* device [S] */
+  const uint8_t* dev_fresh;       /* device [S] */
+} mamba2_recurrent_batch;
+
+/*
+ * Depthwise causal conv1d fused with SiLU, with per-sequence conv-state slots
+ * (gllm PR #85, "Ops", CausalConv1D):
+ *   dst[r, c] = silu(bias[c] + sum_{k=0}^{K-1} weight[c, k] * win[t + k]),
+ * where row r is row t of its sequence and win is the sequence's history (K-1
+ * rows from conv_state[slot], or zeros when fresh) followed by its rows of x;
+ * weight[c, K-1] multiplies the current row.  Afterwards conv_state[slot] holds
+ * the last K-1 rows of win, copied bit for bit.
+ *   dst        device [T, Dc] act (written)
+ *   x          device [T, Dc] act, the xBC rows before the conv
+ *   weight     device [Dc, K] f32;  bias device [Dc] f32
+ *   conv_state device [M, K-1, Dc] act, row 0 the oldest (slots of rb read/written)
+ * Needs Dc % 8 == 0 (bf16) or Dc % 4 == 0 (f32), else MAMBA2_NOT_IMPLEMENTED.
+ */
+mamba2_status mamba2_conv1d(void* dst, const void* x, const float* weight, const float* bias,
+                            void* conv_state, const mamba2_recurrent_batch* rb,
+                            const mamba2_dims* dims, void* stream);
+
+/*
+ * Selective scan over packed variable-length prefill runs (gllm PR #85, "Ops",
+ * SSMScan), computed as a chunked parallel scan: within a chunk the outputs
+ * come from the quadratic (masked C.B^T) form, across chunks from the carried
+ * state.  In exact arithmetic this equals the per-token recurrence, so the
+ * results do not depend on the chunk length (dims->chunk_size sets the chunk of
+ * the fp32 path; the bf16 MFMA path for P = 64, N = 128 uses 64-row chunks).
+ *   dst       device [T, Di] act (y, written)
+ *   xbc       device [T, Dc] act, the conv output; x, B, C at fixed offsets
+ *   dt        device [T, H] act;  a_log, dt_bias, d: device [H] f32
+ *   ssm_state device [M, H, P, N] f32: seeded from (unless fresh) and written to
+ *             the slot of every sequence
+ *   workspace device, >= mamba2_scan_prefill_workspace_bytes(rb, dims) bytes,
+ *             256-byte aligned; contents on entry are ignored.
+ */
+mamba2_status mamba2_scan_prefill(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                  const float* dt_bias, const float* d, float* ssm_state,
+                                  const mamba2_recurrent_batch* rb, const mamba2_dims* dims,
+                                  void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mamba2_scan_prefill needs for this batch (0 when S == 0). */
+size_t mamba2_scan_prefill_workspace_bytes(const mamba2_recurrent_batch* rb,
+                                           const mamba2_dims* dims);
+
+/*
+ * One-row decode step of the same recurrence (every run length must be 1):
+ * each sequence's fp32 state is read once from its slot (not at all when fresh)
+ * and written back once.  Arguments as mamba2_scan_prefill, no workspace.
+ */
+mamba2_status mamba2_scan_decode(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                 const float* dt_bias, const float* d, float* ssm_state,
+                                 const mamba2_recurrent_batch* rb, const mamba2_dims* dims,
+                                 void* stream);
+
+/*
+ * Gated RMSNorm (gllm PR #85, "Ops", GatedRMSNorm; the gate is applied before
+ * the norm): for each row and each of `groups` column groups of size
+ * d_inner / groups,
+ *   g = x * silu(z),  dst = g / sqrt(mean_group(g^2) + eps) * weight.
+ *   dst, x, z device [rows, d_inner] act;  weight device [d_inner] f32.
+ * Needs (d_inner / groups) % 8 == 0 (bf16) or % 4 == 0 (f32), else
+ * MAMBA2_NOT_IMPLEMENTED; groups must divide d_inner; eps >= 0 and finite.
+ */
+mamba2_status mamba2_gated_rmsnorm(void* dst, const void* x, const void* z, const float* weight,
+                                   int32_t groups, float eps, int32_t rows, int32_t d_inner,
+                                   int32_t act_dtype, void* stream);
+
+/*
+ * Host-only checks shared by every stateful call (no device access):
+ * dims, then run lengths (each >= 1; decode != 0: each == 1; sum == num_rows),
+ * then slot range, then slot sharing.  Returns the first failing status.
+ */
+mamba2_status mamba2_validate(const mamba2_recurrent_batch* rb, const mamba2_dims* dims,
+                              int32_t decode);
+
+/*
+ * Bytes of one slot: fp32 SSM state H*P*N*4, conv state (K-1)*Dc*sizeof(act).
+ * ("feat(mamba2): integrate model loading and recurrent inference", InfiniLM
+ * PR #575, section "Motivation": conv plus FP32 SSM state per request, constant
+ * in the history length.)
+ */
+size_t mamba2_ssm_slot_bytes(const mamba2_dims* dims);
+size_t mamba2_conv_slot_bytes(const mamba2_dims* dims);
+
+const char* mamba2_status_string(mamba2_status status);
+
+/*
+ * Kernel timing.  While enabled, the library records a pair of HIP events on the
+ * launch stream around every kernel it launches (creating the events costs
+ * nothing at launch time: a pool of `capacity` pairs is made by the enable
+ * call).  mamba2_timing_collect waits for the recorded events, writes up to
+ * `max` records, resets the log and returns how many it wrote (< 0 on error).
+ * Not thread-safe; meant for benchmarks.
+ */
+typedef struct mamba2_kernel_time {
+  const char* name; /* static string: the kernel's name */
+  float ms;         /* duration between the two events */
+} mamba2_kernel_time;
+
+mamba2_status mamba2_timing_enable(int32_t capacity); /* capacity 0 disables */
+int32_t mamba2_timing_collect(mamba2_kernel_time* out, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAMBA2_H */

@@ -1,0 +1,182 @@
+// C ABI of the Mamba2 mixer hot path: host-side validation and kernel launches.
+//
+// Every check runs before the first launch; on any error nothing is enqueued and
+// nothing is written.  The library allocates no device memory and never
+// synchronises the host with the stream.
+#include <algorithm>
+#include <vector>
+
+#include "common.h"
+
+using namespace m2;
+
+namespace {
+
+constexpr int64_t kMaxElems = (int64_t)1 << 31;
+
+mamba2_status check_dims(const mamba2_dims* d) {
+  if (!d) return MAMBA2_INVALID_ARGUMENT;
+  if (d->nheads < 1 || d->headdim < 1 || d->d_state < 1 || d->ngroups < 1) return MAMBA2_INVALID_ARGUMENT;
+  if (d->nheads % d->ngroups != 0) return MAMBA2_INVALID_ARGUMENT;
+  if (d->conv_kernel < 1 || d->chunk_size < 1 || d->pool_slots < 0) return MAMBA2_INVALID_ARGUMENT;
+  if (d->act_dtype != MAMBA2_DTYPE_F32 && d->act_dtype != MAMBA2_DTYPE_BF16) return MAMBA2_INVALID_ARGUMENT;
+  const int64_t Di = (int64_t)d->nheads * d->headdim;
+  const int64_t Dc = Di + 2 * (int64_t)d->ngroups * d->d_state;
+  const int64_t hpn = Di * d->d_state;
+  if (Dc >= kMaxElems || hpn >= kMaxElems) return MAMBA2_INVALID_ARGUMENT;
+  return MAMBA2_OK;
+}
+
+// Run lengths, then slot range, then slot sharing (the RecurrentBatch rules).
+mamba2_status check_batch(const mamba2_recurrent_batch* rb, const mamba2_dims* d, bool decode) {
+  if (!rb) return MAMBA2_INVALID_ARGUMENT;
+  const int S = rb->num_seqs;
+  if (S < 0 || rb->num_rows < 0) return MAMBA2_INVALID_ARGUMENT;
+  if (S > 0 && (!rb->run_lengths || !rb->slots || !rb->fresh || !rb->dev_cu_seqlens ||
+                !rb->dev_slots || !rb->dev_fresh))
+    return MAMBA2_INVALID_ARGUMENT;
+  int64_t sum = 0;
+  for (int s = 0; s < S; ++s) {
+    const int32_t L = rb->run_lengths[s];
+    if (L <= 0 || (decode && L != 1)) return MAMBA2_RUN_LENGTHS;
+    sum += L;
+  }
+  if (sum != rb->num_rows) return MAMBA2_RUN_LENGTHS;
+  for (int s = 0; s < S; ++s)
+    if (rb->slots[s] < 0 || rb->slots[s] >= d->pool_slots) return MAMBA2_SLOT_OUT_OF_RANGE;
+  if (S > 1) {
+    std::vector<int32_t> v(rb->slots, rb->slots + S);
+    std::sort(v.begin(), v.end());
+    for (int s = 1; s < S; ++s)
+      if (v[s] == v[s - 1]) return MAMBA2_SLOT_SHARED;
+  }
+  return MAMBA2_OK;
+}
+
+mamba2_status check_all(const mamba2_recurrent_batch* rb, const mamba2_dims* d, bool decode) {
+  mamba2_status st = check_dims(d);
+  if (st != MAMBA2_OK) return st;
+  return check_batch(rb, d, decode);
+}
+
+int act_vec(int32_t act) { return act == MAMBA2_DTYPE_BF16 ? 8 : 4; }
+
+BatchDev batch_dev(const mamba2_recurrent_batch* rb) {
+  return BatchDev{rb->dev_cu_seqlens, rb->dev_slots, rb->dev_fresh, rb->num_seqs, rb->num_rows};
+}
+
+mamba2_status from_hip(hipError_t e) { return e == hipSuccess ? MAMBA2_OK : MAMBA2_HIP_ERROR; }
+
+// Shapes the prefill scan covers (both paths need N % 4 == 0 for 16-byte state access).
+bool scan_supported(const mamba2_dims* d) { return d->d_state % 4 == 0; }
+
+}  // namespace
+
+extern "C" {
+
+mamba2_status mamba2_validate(const mamba2_recurrent_batch* rb, const mamba2_dims* dims,
+                              int32_t decode) {
+  return check_all(rb, dims, decode != 0);
+}
+
+mamba2_status mamba2_conv1d(void* dst, const void* x, const float* weight, const float* bias,
+                            void* conv_state, const mamba2_recurrent_batch* rb,
+                            const mamba2_dims* dims, void* stream) {
+  mamba2_status st = check_dims(dims);
+  if (st != MAMBA2_OK) return st;
+  if (!rb) return MAMBA2_INVALID_ARGUMENT;
+  if (rb->num_rows > 0 && (!dst || !x || !weight || !bias || !conv_state)) return MAMBA2_INVALID_ARGUMENT;
+  st = check_batch(rb, dims, false);
+  if (st != MAMBA2_OK) return st;
+  const int64_t Dc = (int64_t)dims->nheads * dims->headdim + 2 * (int64_t)dims->ngroups * dims->d_state;
+  if (dims->conv_kernel < 2 || dims->conv_kernel > 4 || Dc % act_vec(dims->act_dtype) != 0)
+    return MAMBA2_NOT_IMPLEMENTED;
+  if (rb->num_rows == 0) return MAMBA2_OK;
+  return from_hip(launch_conv1d(dst, x, weight, bias, conv_state, batch_dev(rb), (int32_t)Dc,
+                                dims->conv_kernel, dims->act_dtype, (hipStream_t)stream));
+}
+
+size_t mamba2_scan_prefill_workspace_bytes(const mamba2_recurrent_batch* rb, const mamba2_dims* dims) {
+  if (check_all(rb, dims, false) != MAMBA2_OK || rb->num_rows == 0) return 0;
+  const bool mfma = scan_uses_mfma(dims);
+  return scan_layout(rb, dims, scan_segment_length(rb, dims, mfma)).total;
+}
+
+mamba2_status mamba2_scan_prefill(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                  const float* dt_bias, const float* d, float* ssm_state,
+                                  const mamba2_recurrent_batch* rb, const mamba2_dims* dims,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  mamba2_status st = check_dims(dims);
+  if (st != MAMBA2_OK) return st;
+  if (!rb) return MAMBA2_INVALID_ARGUMENT;
+  if (rb->num_rows > 0 && (!dst || !xbc || !dt || !a_log || !dt_bias || !d || !ssm_state))
+    return MAMBA2_INVALID_ARGUMENT;
+  st = check_batch(rb, dims, false);
+  if (st != MAMBA2_OK) return st;
+  if (!scan_supported(dims)) return MAMBA2_NOT_IMPLEMENTED;
+  if (rb->num_rows == 0) return MAMBA2_OK;
+  const bool mfma = scan_uses_mfma(dims);
+  const ScanLayout lay = scan_layout(rb, dims, scan_segment_length(rb, dims, mfma));
+  if (!workspace || workspace_bytes < lay.total) return MAMBA2_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & 255) != 0) return MAMBA2_INVALID_ARGUMENT;
+  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace};
+  return from_hip(launch_scan_prefill(a, (hipStream_t)stream));
+}
+
+mamba2_status mamba2_scan_decode(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                 const float* dt_bias, const float* d, float* ssm_state,
+                                 const mamba2_recurrent_batch* rb, const mamba2_dims* dims,
+                                 void* stream) {
+  mamba2_status st = check_dims(dims);
+  if (st != MAMBA2_OK) return st;
+  if (!rb) return MAMBA2_INVALID_ARGUMENT;
+  if (rb->num_rows > 0 && (!dst || !xbc || !dt || !a_log || !dt_bias || !d || !ssm_state))
+    return MAMBA2_INVALID_ARGUMENT;
+  st = check_batch(rb, dims, true);
+  if (st != MAMBA2_OK) return st;
+  if (!decode_supported(*dims)) return MAMBA2_NOT_IMPLEMENTED;
+  if (rb->num_rows == 0) return MAMBA2_OK;
+  return from_hip(launch_scan_decode(dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims,
+                                     (hipStream_t)stream));
+}
+
+mamba2_status mamba2_gated_rmsnorm(void* dst, const void* x, const void* z, const float* weight,
+                                   int32_t groups, float eps, int32_t rows, int32_t d_inner,
+                                   int32_t act_dtype, void* stream) {
+  if (rows < 0 || d_inner < 1 || groups < 1 || d_inner % groups != 0) return MAMBA2_INVALID_ARGUMENT;
+  if (act_dtype != MAMBA2_DTYPE_F32 && act_dtype != MAMBA2_DTYPE_BF16) return MAMBA2_INVALID_ARGUMENT;
+  if (!(eps >= 0.f) || eps == __builtin_inff()) return MAMBA2_INVALID_ARGUMENT;
+  if (rows > 0 && (!dst || !x || !z || !weight)) return MAMBA2_INVALID_ARGUMENT;
+  if ((int64_t)rows * d_inner >= ((int64_t)1 << 40)) return MAMBA2_INVALID_ARGUMENT;
+  if ((d_inner / groups) % act_vec(act_dtype) != 0) return MAMBA2_NOT_IMPLEMENTED;
+  if (rows == 0) return MAMBA2_OK;
+  return from_hip(launch_gated_rmsnorm(dst, x, z, weight, groups, eps, rows, d_inner, act_dtype,
+                                       (hipStream_t)stream));
+}
+
+size_t mamba2_ssm_slot_bytes(const mamba2_dims* d) {
+  if (check_dims(d) != MAMBA2_OK) return 0;
+  return (size_t)d->nheads * d->headdim * d->d_state * sizeof(float);
+}
+
+size_t mamba2_conv_slot_bytes(const mamba2_dims* d) {
+  if (check_dims(d) != MAMBA2_OK) return 0;
+  const size_t Dc = (size_t)d->nheads * d->headdim + 2 * (size_t)d->ngroups * d->d_state;
+  return (size_t)(d->conv_kernel - 1) * Dc * (d->act_dtype == MAMBA2_DTYPE_BF16 ? 2 : 4);
+}
+
+const char* mamba2_status_string(mamba2_status s) {
+  switch (s) {
+    case MAMBA2_OK: return "ok";
+    case MAMBA2_INVALID_ARGUMENT: return "invalid argument";
+    case MAMBA2_SLOT_OUT_OF_RANGE: return "slot out of range";
+    case MAMBA2_SLOT_SHARED: return "slot shared by two sequences";
+    case MAMBA2_RUN_LENGTHS: return "run lengths do not cover the rows";
+    case MAMBA2_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case MAMBA2_NOT_IMPLEMENTED: return "not implemented for these dims";
+    case MAMBA2_HIP_ERROR: return "HIP error";
+  }
+  return "unknown status";
+}
+
+}  // extern "C"

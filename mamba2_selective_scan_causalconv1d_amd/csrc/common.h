@@ -1,0 +1,160 @@
+// Internal declarations of the gfx950 kernels and their host launchers.
+// Device helpers for bf16 storage, wave-level reductions and the workspace layout
+// of the chunked scan.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/mamba2.h"
+
+namespace m2 {
+
+// ------------------------------------------------------------------ storage
+
+typedef uint16_t bf16_t;  // raw bf16 bits
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16, round to nearest even, NaN kept quiet.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// two fp32 -> packed bf16x2 (lo in bits 0..15)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// Activation access: T is float (fp32) or bf16_t (bf16 bits).
+template <typename T>
+struct Act;
+
+template <>
+struct Act<float> {
+  static constexpr int kVec = 4;  // elements per 16-byte vector
+  __device__ static __forceinline__ float load(const float* p) { return *p; }
+  __device__ static __forceinline__ void store(float* p, float v) { *p = v; }
+  __device__ static __forceinline__ void unpack(const uint4& v, float* f) {
+    f[0] = __uint_as_float(v.x);
+    f[1] = __uint_as_float(v.y);
+    f[2] = __uint_as_float(v.z);
+    f[3] = __uint_as_float(v.w);
+  }
+  __device__ static __forceinline__ uint4 pack(const float* f) {
+    return make_uint4(__float_as_uint(f[0]), __float_as_uint(f[1]), __float_as_uint(f[2]),
+                      __float_as_uint(f[3]));
+  }
+};
+
+template <>
+struct Act<bf16_t> {
+  static constexpr int kVec = 8;
+  __device__ static __forceinline__ float load(const bf16_t* p) { return bf16_to_f32(*p); }
+  __device__ static __forceinline__ void store(bf16_t* p, float v) { *p = (bf16_t)f32_to_bf16(v); }
+  __device__ static __forceinline__ void unpack(const uint4& v, float* f) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = __uint_as_float(w[i] << 16);
+      f[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  __device__ static __forceinline__ uint4 pack(const float* f) {
+    return make_uint4(pack_bf16x2(f[0], f[1]), pack_bf16x2(f[2], f[3]), pack_bf16x2(f[4], f[5]),
+                      pack_bf16x2(f[6], f[7]));
+  }
+};
+
+// ------------------------------------------------------------------ math
+
+// softplus without a clamp; above 20 the identity is exact to fp32 precision.
+__device__ __forceinline__ float softplus_f32(float v) { return v > 20.f ? v : log1pf(__expf(v)); }
+
+__device__ __forceinline__ float silu_f32(float v) { return v / (1.f + __expf(-v)); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// ------------------------------------------------------- chunked scan workspace
+//
+// Sequences are cut into segments of at most seg_len rows (aligned to each
+// sequence's first row).  Layout (each section 256-byte aligned):
+//   seq_info  int2  [S]        (first segment index, number of segments)
+//   seg_info  int4  [nseg]     (sequence, first row, rows, index within sequence)
+//   seg_decay f32   [nseg][H]  exp(sum of log-decays over the segment)
+//   seg_state f32   [nseg][H][P][N]  local end state, then the state entering
+//                                    the segment
+struct ScanLayout {
+  int64_t nseg;
+  int32_t seg_len;
+  size_t off_seq_info, off_seg_info, off_seg_decay, off_seg_state, total;
+};
+
+ScanLayout scan_layout(const mamba2_recurrent_batch* rb, const mamba2_dims* d, int32_t seg_len);
+int32_t scan_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims* d, bool mfma);
+bool scan_uses_mfma(const mamba2_dims* d);
+
+// ------------------------------------------------------------------ launchers
+// Each returns hipSuccess or the launch error.  Shapes are validated by the caller.
+
+struct BatchDev {
+  const int32_t* cu_seqlens;  // [S+1]
+  const int32_t* slots;       // [S]
+  const uint8_t* fresh;       // [S]
+  int32_t num_seqs;
+  int32_t num_rows;
+};
+
+hipError_t launch_conv1d(void* dst, const void* x, const float* w, const float* b, void* conv_state,
+                         const BatchDev& bd, int32_t Dc, int32_t K, int32_t act, hipStream_t st);
+
+hipError_t launch_gated_rmsnorm(void* dst, const void* x, const void* z, const float* w,
+                                int32_t groups, float eps, int32_t rows, int32_t Di, int32_t act,
+                                hipStream_t st);
+
+hipError_t launch_scan_decode(void* dst, const void* xbc, const void* dt, const float* a_log,
+                              const float* dt_bias, const float* D, float* ssm_state,
+                              const BatchDev& bd, const mamba2_dims& dims, hipStream_t st);
+
+struct ScanArgs {
+  void* y;
+  const void* xbc;
+  const void* dt;
+  const float* a_log;
+  const float* dt_bias;
+  const float* D;
+  float* ssm_state;
+  BatchDev bd;
+  mamba2_dims dims;
+  ScanLayout lay;
+  char* ws;
+};
+
+hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st);
+hipError_t launch_scan_pass(const ScanArgs& a, hipStream_t st);
+bool decode_supported(const mamba2_dims& dm);
+
+// ------------------------------------------------------------------ timing
+// When enabled, kernel launches are bracketed by event records.
+void timing_before(hipStream_t st, const char* name);
+void timing_after(hipStream_t st);
+
+}  // namespace m2
+
+// Launch a kernel with optional timing and return the launch status.
+#define M2_LAUNCH(name, kernel, grid, block, shmem, stream, ...)                 \
+  do {                                                                          \
+    ::m2::timing_before((stream), (name));                                      \
+    hipLaunchKernelGGL((kernel), (grid), (block), (shmem), (stream), __VA_ARGS__); \
+    ::m2::timing_after((stream));                                               \
+    hipError_t _e = hipGetLastError();                                          \
+    if (_e != hipSuccess) return _e;                                            \
+  } while (0)

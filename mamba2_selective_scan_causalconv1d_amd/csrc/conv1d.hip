@@ -1,0 +1,183 @@
+// Depthwise causal conv1d + SiLU with per-sequence conv-state slots, for gfx950.
+//
+// Operation ("feat(backend): Mamba2 ops, with CPU reference implementations",
+// section "Ops", CausalConv1D): out[t, c] = silu(b[c] + sum_k w[c, k] * win[t + k]),
+// win = (K-1 history rows from the slot, or zeros when fresh) ++ the sequence's rows;
+// afterwards the slot holds the last K-1 rows of win, bit for bit.
+//
+// Mapping: one thread owns one 16-byte channel vector (8 bf16 / 4 fp32 channels)
+// of a tile of R consecutive packed rows and slides a K-tap window down them in
+// registers; a wavefront covers 64 consecutive vectors of a row, so every row
+// access is a contiguous 1 KiB.
+//
+// Slot ownership: the first K-1 rows of a sequence (its "head", the rows that read
+// history) are processed by the tile that holds the sequence's first row, even
+// when they run past that tile's end; the next tile skips them.  That thread reads
+// the slot (unless fresh) into registers and then writes the new state, so every
+// slot element is read and written by one thread, in program order, and one
+// launch serves any mix of run lengths (decode included).
+#include "common.h"
+
+namespace m2 {
+namespace {
+
+__device__ __forceinline__ int seq_of_row(const int32_t* __restrict__ cu, int S, int row) {
+  // largest s in [0, S) with cu[s] <= row (cu is strictly increasing, cu[S] > row)
+  int lo = 0, hi = S - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (cu[mid] <= row)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  return lo;
+}
+
+template <typename T, int K>
+__global__ __launch_bounds__(256) void conv1d_silu_kernel(
+    T* __restrict__ dst, const T* __restrict__ x, const float* __restrict__ w,
+    const float* __restrict__ b, T* __restrict__ conv_state, const int32_t* __restrict__ cu,
+    const int32_t* __restrict__ slots, const uint8_t* __restrict__ fresh, int S, int T_rows,
+    int Dc, int R, int64_t nthreads) {
+  constexpr int V = Act<T>::kVec;
+  constexpr int H1 = K - 1;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= nthreads) return;
+  const int NV = Dc / V;
+  const int v = (int)(gid % NV);
+  const int tile = (int)(gid / NV);
+  const int a = tile * R;
+  const int bnd = min(T_rows, a + R);
+  const size_t col = (size_t)v * V;
+
+  float wr[V][K], br[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    br[i] = b[col + i];
+#pragma unroll
+    for (int k = 0; k < K; ++k) wr[i][k] = w[(col + i) * K + k];
+  }
+
+  int s = seq_of_row(cu, S, a);
+  int t = a;
+  {
+    const int st0 = cu[s], en = cu[s + 1];
+    if (st0 < a) t = max(a, min(st0 + H1, en));  // head rows belong to an earlier tile
+  }
+
+  float win[H1][V];
+  for (;;) {
+    while (t >= cu[s + 1]) {
+      if (++s >= S) return;
+    }
+    const int st0 = cu[s], en = cu[s + 1];
+    if (st0 >= bnd) return;
+    const bool own_head = st0 >= a;
+    const int run_end = own_head ? min(en, max(bnd, st0 + H1)) : min(en, bnd);
+    if (t >= run_end) return;
+
+    if (t == st0) {
+      // Sequence start (own_head): read the history, then write the new state.
+      const size_t sbase = (size_t)slots[s] * H1 * Dc + col;
+      uint4 raw[H1];
+#pragma unroll
+      for (int r = 0; r < H1; ++r) raw[r] = make_uint4(0, 0, 0, 0);
+      if (!fresh[s]) {  // a fresh sequence never reads its slot
+#pragma unroll
+        for (int r = 0; r < H1; ++r)
+          raw[r] = *reinterpret_cast<const uint4*>(conv_state + sbase + (size_t)r * Dc);
+      }
+#pragma unroll
+      for (int r = 0; r < H1; ++r) Act<T>::unpack(raw[r], win[r]);
+      const int L = en - st0;
+      uint4 nst[H1];
+#pragma unroll
+      for (int r = 0; r < H1; ++r) {
+        const int idx = L + r;  // position in win = history ++ rows
+        nst[r] = idx < H1 ? raw[idx]
+                          : *reinterpret_cast<const uint4*>(x + (size_t)(st0 + idx - H1) * Dc + col);
+      }
+#pragma unroll
+      for (int r = 0; r < H1; ++r)
+        *reinterpret_cast<uint4*>(conv_state + sbase + (size_t)r * Dc) = nst[r];
+    } else {
+      // Mid-sequence entry: t >= st0 + H1, the window comes from the rows before t.
+#pragma unroll
+      for (int r = 0; r < H1; ++r)
+        Act<T>::unpack(*reinterpret_cast<const uint4*>(x + (size_t)(t - H1 + r) * Dc + col), win[r]);
+    }
+
+    while (t < run_end) {
+      const int n = min(4, run_end - t);
+      uint4 xv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j < n) xv[j] = *reinterpret_cast<const uint4*>(x + (size_t)(t + j) * Dc + col);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (j < n) {
+          float xf[V], out[V];
+          Act<T>::unpack(xv[j], xf);
+#pragma unroll
+          for (int i = 0; i < V; ++i) {
+            float pre = br[i];
+#pragma unroll
+            for (int k = 0; k < H1; ++k) pre = fmaf(wr[i][k], win[k][i], pre);
+            pre = fmaf(wr[i][H1], xf[i], pre);
+            out[i] = silu_f32(pre);
+          }
+          *reinterpret_cast<uint4*>(dst + (size_t)(t + j) * Dc + col) = Act<T>::pack(out);
+#pragma unroll
+          for (int k = 0; k + 1 < H1; ++k)
+#pragma unroll
+            for (int i = 0; i < V; ++i) win[k][i] = win[k + 1][i];
+#pragma unroll
+          for (int i = 0; i < V; ++i) win[H1 - 1][i] = xf[i];
+        }
+      }
+      t += n;
+    }
+    if (t >= bnd) return;
+  }
+}
+
+template <typename T, int K>
+hipError_t launch_t(void* dst, const void* x, const float* w, const float* b, void* cs,
+                    const BatchDev& bd, int32_t Dc, hipStream_t st) {
+  constexpr int V = Act<T>::kVec;
+  const int NV = Dc / V;
+  const int64_t work = (int64_t)bd.num_rows * NV;
+  // rows per thread: enough threads to fill the chip (~512K), at most 32 rows each
+  int R = (int)((work + 524287) / 524288);
+  R = R < 1 ? 1 : (R > 32 ? 32 : R);
+  const int64_t tiles = (bd.num_rows + R - 1) / R;
+  const int64_t nthreads = tiles * NV;
+  const dim3 grid((unsigned)((nthreads + 255) / 256));
+  M2_LAUNCH("conv1d_silu", (conv1d_silu_kernel<T, K>), grid, dim3(256), 0, st, (T*)dst,
+            (const T*)x, w, b, (T*)cs, bd.cu_seqlens, bd.slots, bd.fresh, bd.num_seqs, bd.num_rows,
+            Dc, R, nthreads);
+  return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_conv1d(void* dst, const void* x, const float* w, const float* b, void* cs,
+                         const BatchDev& bd, int32_t Dc, int32_t K, int32_t act, hipStream_t st) {
+  if (act == MAMBA2_DTYPE_BF16) {
+    switch (K) {
+      case 2: return launch_t<bf16_t, 2>(dst, x, w, b, cs, bd, Dc, st);
+      case 3: return launch_t<bf16_t, 3>(dst, x, w, b, cs, bd, Dc, st);
+      case 4: return launch_t<bf16_t, 4>(dst, x, w, b, cs, bd, Dc, st);
+    }
+  } else {
+    switch (K) {
+      case 2: return launch_t<float, 2>(dst, x, w, b, cs, bd, Dc, st);
+      case 3: return launch_t<float, 3>(dst, x, w, b, cs, bd, Dc, st);
+      case 4: return launch_t<float, 4>(dst, x, w, b, cs, bd, Dc, st);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace m2

@@ -1,0 +1,159 @@
+// One-row decode step of the selective scan for gfx950.
+//
+// Operation ("feat(backend): Mamba2 ops, with CPU reference implementations", section
+// "Ops", SSMScan, with one row per sequence): dt' = softplus(dt + dt_bias),
+//   h[p, n] <- h[p, n] * exp(-exp(A_log) * dt') + (dt' * x[p]) * B[n],
+//   y[p] = sum_n h[p, n] * C[n] + D * x[p],
+// head h reading B and C of group h / (H / G); a fresh sequence starts from zero and
+// never reads its slot.
+//
+// Mapping: one workgroup per (sequence, head).  The head's fp32 state [P][N] is
+// streamed once in and once out with 16-byte accesses; consecutive threads take
+// consecutive float4s, so each wave instruction touches 1 KiB of contiguous state.
+// A thread keeps the same four state columns for every row it visits, so its B and
+// C values are loaded once; the row sums of h * C are reduced over the N/4 lanes
+// that share a row.  This is an HBM-streaming kernel (~0.75 flop per byte).
+#include "common.h"
+
+namespace m2 {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ void load4(const T* p, float* f);
+
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float* f) {
+  const float4 v = *reinterpret_cast<const float4*>(p);
+  f[0] = v.x;
+  f[1] = v.y;
+  f[2] = v.z;
+  f[3] = v.w;
+}
+
+template <>
+__device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float* f) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  f[0] = bf16_to_f32(v.x & 0xffffu);
+  f[1] = bf16_to_f32(v.x >> 16);
+  f[2] = bf16_to_f32(v.y & 0xffffu);
+  f[3] = bf16_to_f32(v.y >> 16);
+}
+
+// KP float4s per thread; Q4 = N / 4 lanes share a state row (Q4 divides 64).
+template <typename T, int KP>
+__global__ __launch_bounds__(256) void scan_decode_kernel(
+    T* __restrict__ y, const T* __restrict__ xbc, const T* __restrict__ dt,
+    const float* __restrict__ a_log, const float* __restrict__ dt_bias,
+    const float* __restrict__ Dp, float* __restrict__ pool, const int32_t* __restrict__ slots,
+    const uint8_t* __restrict__ fresh, int H, int P, int N, int G) {
+  const int h = blockIdx.x;
+  const int r = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int Q4 = N >> 2;
+  const int Di = H * P;
+  const size_t Dc = (size_t)Di + 2 * (size_t)G * N;
+  const int g = h / (H / G);
+  const T* row = xbc + (size_t)r * Dc;
+
+  const float v = Act<T>::load(dt + (size_t)r * H + h) + dt_bias[h];
+  const float dtp = softplus_f32(v);
+  const float dA = __expf(-__expf(a_log[h]) * dtp);
+  const int n0 = 4 * (tid % Q4);
+  float Bv[4], Cv[4];
+  load4<T>(row + Di + (size_t)g * N + n0, Bv);
+  load4<T>(row + Di + (size_t)G * N + (size_t)g * N + n0, Cv);
+
+  float4* st = reinterpret_cast<float4*>(pool + ((size_t)slots[r] * H + h) * (size_t)P * N);
+  float4 hv[KP];
+  if (fresh[r]) {
+#pragma unroll
+    for (int k = 0; k < KP; ++k) hv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+  } else {
+#pragma unroll
+    for (int k = 0; k < KP; ++k) hv[k] = st[k * nthr + tid];
+  }
+  float part[KP], xs[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int p = (k * nthr + tid) / Q4;
+    xs[k] = Act<T>::load(row + (size_t)h * P + p);
+    const float c = dtp * xs[k];
+    float4 s = hv[k];
+    s.x = fmaf(c, Bv[0], s.x * dA);
+    s.y = fmaf(c, Bv[1], s.y * dA);
+    s.z = fmaf(c, Bv[2], s.z * dA);
+    s.w = fmaf(c, Bv[3], s.w * dA);
+    hv[k] = s;
+    part[k] = fmaf(s.x, Cv[0], fmaf(s.y, Cv[1], fmaf(s.z, Cv[2], s.w * Cv[3])));
+  }
+#pragma unroll
+  for (int k = 0; k < KP; ++k) st[k * nthr + tid] = hv[k];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    float s = part[k];
+    for (int o = Q4 >> 1; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
+    part[k] = s;
+  }
+  if ((tid % Q4) == 0) {
+    const float d = Dp[h];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      const int p = (k * nthr + tid) / Q4;
+      Act<T>::store(y + (size_t)r * Di + (size_t)h * P + p, fmaf(d, xs[k], part[k]));
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_t(void* y, const void* xbc, const void* dt, const float* a_log,
+                    const float* dt_bias, const float* D, float* pool, const BatchDev& bd,
+                    const mamba2_dims& dm, hipStream_t st) {
+  const int Q4 = dm.d_state / 4;
+  const int64_t f4 = (int64_t)dm.headdim * Q4;  // float4s per head state
+  const int nthr = (int)(f4 < 256 ? f4 : 256);
+  const int KP = (int)(f4 / nthr);
+  const dim3 grid((unsigned)dm.nheads, (unsigned)bd.num_seqs);
+#define M2_DEC(kp)                                                                           \
+  case kp:                                                                                   \
+    M2_LAUNCH("scan_decode", (scan_decode_kernel<T, kp>), grid, dim3(nthr), 0, st, (T*)y,   \
+              (const T*)xbc, (const T*)dt, a_log, dt_bias, D, pool, bd.slots, bd.fresh,       \
+              dm.nheads, dm.headdim, dm.d_state, dm.ngroups);                                \
+    return hipSuccess;
+  switch (KP) {
+    M2_DEC(1)
+    M2_DEC(2)
+    M2_DEC(4)
+    M2_DEC(8)
+    M2_DEC(16)
+  }
+#undef M2_DEC
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+// Shapes the decode kernel covers: N % 4 == 0 with N/4 a power of two <= 64, and
+// P*N/4 either < 256 and a multiple of 64, or a multiple of 256 with at most 16
+// float4s per thread.
+bool decode_supported(const mamba2_dims& dm) {
+  const int N = dm.d_state;
+  if (N % 4 != 0) return false;
+  const int Q4 = N / 4;
+  if (Q4 > 64 || (Q4 & (Q4 - 1)) != 0) return false;
+  const int64_t f4 = (int64_t)dm.headdim * Q4;
+  if (f4 < 256) return f4 % 64 == 0;
+  if (f4 % 256 != 0) return false;
+  const int64_t kp = f4 / 256;
+  return kp == 1 || kp == 2 || kp == 4 || kp == 8 || kp == 16;
+}
+
+hipError_t launch_scan_decode(void* y, const void* xbc, const void* dt, const float* a_log,
+                              const float* dt_bias, const float* D, float* pool,
+                              const BatchDev& bd, const mamba2_dims& dm, hipStream_t st) {
+  if (dm.act_dtype == MAMBA2_DTYPE_BF16)
+    return launch_t<bf16_t>(y, xbc, dt, a_log, dt_bias, D, pool, bd, dm, st);
+  return launch_t<float>(y, xbc, dt, a_log, dt_bias, D, pool, bd, dm, st);
+}
+
+}  // namespace m2

@@ -1,0 +1,166 @@
+// Chunked selective scan for prefill: segment tables and the inter-segment state pass.
+//
+// The chunked form of the recurrence ("feat(backend): Mamba2 ops, with CPU reference
+// implementations", section "Ops", SSMScan; "Granite Mamba2 Inference Optimization":
+// long prefill as a chunked parallel scan).  Each sequence is cut into segments of
+// seg_len rows aligned to its first row, so no segment spans two sequences and the
+// state never crosses a sequence boundary.  With a_t = -exp(A_log) * dt'_t and
+// S_in(k) the state entering segment k of a sequence:
+//   S_in(0)   = 0 when fresh, else the slot,
+//   S_in(k+1) = exp(sum_{t in k} a_t) * S_in(k) + S_loc(k),
+//   S_loc(k)  = sum_{j in k} exp(sum_{t in k, t > j} a_t) * dt'_j * x_j (x) B_j.
+// Three launches: segment states S_loc for every segment but a sequence's last
+// (scan kernels), this pass (turns them into S_in, serially over a sequence's
+// segments), and the output kernels that walk each segment from S_in, write y and,
+// for a sequence's last segment, the final state into the slot.
+#include "common.h"
+
+namespace m2 {
+
+namespace {
+
+constexpr int kSetupThreads = 1024;
+
+__global__ __launch_bounds__(kSetupThreads) void scan_setup_kernel(const int32_t* __restrict__ cu,
+                                                                   int S, int seg_len,
+                                                                   int2* __restrict__ seq_info,
+                                                                   int4* __restrict__ seg_info) {
+  __shared__ int buf[kSetupThreads];
+  __shared__ int carry;
+  const int tid = threadIdx.x;
+  if (tid == 0) carry = 0;
+  __syncthreads();
+  for (int base = 0; base < S; base += kSetupThreads) {
+    const int s = base + tid;
+    int len = 0, n = 0;
+    if (s < S) {
+      len = cu[s + 1] - cu[s];
+      n = (len + seg_len - 1) / seg_len;
+    }
+    buf[tid] = n;
+    __syncthreads();
+    for (int o = 1; o < kSetupThreads; o <<= 1) {
+      const int add = tid >= o ? buf[tid - o] : 0;
+      __syncthreads();
+      buf[tid] += add;
+      __syncthreads();
+    }
+    const int first = carry + buf[tid] - n;
+    if (s < S) {
+      seq_info[s] = make_int2(first, n);
+      for (int k = 0; k < n; ++k)
+        seg_info[first + k] = make_int4(s, cu[s] + k * seg_len, min(seg_len, len - k * seg_len), k);
+    }
+    __syncthreads();
+    if (tid == kSetupThreads - 1) carry += buf[tid];
+    __syncthreads();
+  }
+}
+
+// One thread per float4 of a head's state, walking one sequence's segments in order.
+__global__ __launch_bounds__(256) void scan_pass_kernel(const int2* __restrict__ seq_info,
+                                                        const float* __restrict__ seg_decay,
+                                                        float4* __restrict__ seg_state,
+                                                        const float4* __restrict__ pool,
+                                                        const int32_t* __restrict__ slots,
+                                                        const uint8_t* __restrict__ fresh, int H,
+                                                        int f4) {
+  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y;
+  const int s = blockIdx.z;
+  if (f >= f4) return;
+  const int2 si = seq_info[s];
+  float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (!fresh[s]) S = pool[((size_t)slots[s] * H + h) * f4 + f];
+  for (int k = 0; k < si.y; ++k) {
+    const int64_t seg = si.x + k;
+    float4* p = seg_state + ((size_t)seg * H + h) * f4 + f;
+    if (k + 1 < si.y) {
+      const float4 loc = *p;  // S_loc(k), written by the segment-state kernel
+      *p = S;                 // S_in(k)
+      const float d = seg_decay[seg * H + h];
+      S.x = fmaf(d, S.x, loc.x);
+      S.y = fmaf(d, S.y, loc.y);
+      S.z = fmaf(d, S.z, loc.z);
+      S.w = fmaf(d, S.w, loc.w);
+    } else {
+      *p = S;
+    }
+  }
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bool scan_uses_mfma(const mamba2_dims* d) {
+  (void)d;
+  return false;
+}
+
+int32_t scan_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims* d, bool mfma) {
+  if (!mfma) {
+    const int q = d->chunk_size < 64 ? d->chunk_size : 64;
+    return q < 1 ? 1 : q;
+  }
+  // MFMA path: 64-row chunks; a segment is a run of chunks walked by one workgroup
+  // (two heads each).  Aim at ~768 workgroups (three per CU), 64..4096 rows each.
+  const int64_t hblocks = (d->nheads + 1) / 2;
+  const int64_t work = (int64_t)rb->num_rows * hblocks;
+  int64_t L = (work + 767) / 768;
+  L = (L + 63) / 64 * 64;
+  if (L < 64) L = 64;
+  if (L > 4096) L = 4096;
+  return (int32_t)L;
+}
+
+ScanLayout scan_layout(const mamba2_recurrent_batch* rb, const mamba2_dims* d, int32_t seg_len) {
+  ScanLayout L{};
+  L.seg_len = seg_len;
+  int64_t nseg = 0;
+  for (int s = 0; s < rb->num_seqs; ++s) nseg += (rb->run_lengths[s] + seg_len - 1) / seg_len;
+  L.nseg = nseg;
+  const size_t S = (size_t)rb->num_seqs;
+  const size_t H = (size_t)d->nheads;
+  const size_t PN = (size_t)d->headdim * d->d_state;
+  size_t off = 0;
+  L.off_seq_info = off;
+  off = align256(off + S * sizeof(int2));
+  L.off_seg_info = off;
+  off = align256(off + (size_t)nseg * sizeof(int4));
+  L.off_seg_decay = off;
+  off = align256(off + (size_t)nseg * H * sizeof(float));
+  L.off_seg_state = off;
+  off = align256(off + (size_t)nseg * H * PN * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+hipError_t launch_scan_setup(const ScanArgs& a, hipStream_t st) {
+  M2_LAUNCH("scan_setup", scan_setup_kernel, dim3(1), dim3(kSetupThreads), 0, st, a.bd.cu_seqlens,
+            a.bd.num_seqs, a.lay.seg_len, (int2*)(a.ws + a.lay.off_seq_info),
+            (int4*)(a.ws + a.lay.off_seg_info));
+  return hipSuccess;
+}
+
+hipError_t launch_scan_pass(const ScanArgs& a, hipStream_t st) {
+  const int f4 = a.dims.headdim * a.dims.d_state / 4;
+  const dim3 grid((unsigned)((f4 + 255) / 256), (unsigned)a.dims.nheads, (unsigned)a.bd.num_seqs);
+  M2_LAUNCH("scan_pass", scan_pass_kernel, grid, dim3(256), 0, st,
+            (const int2*)(a.ws + a.lay.off_seq_info), (const float*)(a.ws + a.lay.off_seg_decay),
+            (float4*)(a.ws + a.lay.off_seg_state), (const float4*)a.ssm_state, a.bd.slots,
+            a.bd.fresh, a.dims.nheads, f4);
+  return hipSuccess;
+}
+
+hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t st);
+hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t st);
+
+hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
+  hipError_t e = launch_scan_setup(a, st);
+  if (e != hipSuccess) return e;
+  if (scan_uses_mfma(&a.dims)) return launch_scan_mfma(a, st);
+  return launch_scan_generic(a, st);
+}
+
+}  // namespace m2

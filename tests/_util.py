@@ -36,9 +36,10 @@ def assert_close(got, ref, bar, what=""):
 
 
 def oracle_conv(wl: W.Workload, xbc=None, conv_pool=None, run_lengths=None, slots=None,
-                fresh=None):
+                fresh=None, inplace=False):
     xbc = wl.xbc if xbc is None else xbc
-    pool = (wl.conv_pool if conv_pool is None else conv_pool).copy()
+    pool = wl.conv_pool if conv_pool is None else conv_pool
+    pool = pool if inplace else pool.copy()
     out = np.zeros_like(xbc)
     st = oracle.conv1d(out, xbc, wl.conv_w, wl.conv_b, pool,
                        wl.run_lengths if run_lengths is None else run_lengths,
@@ -48,9 +49,10 @@ def oracle_conv(wl: W.Workload, xbc=None, conv_pool=None, run_lengths=None, slot
 
 
 def oracle_scan(wl: W.Workload, xa, dt=None, ssm_pool=None, run_lengths=None, slots=None,
-                fresh=None, head_mask=None, decode=False):
+                fresh=None, head_mask=None, decode=False, inplace=False):
     sh = wl.shape
-    pool = (wl.ssm_pool if ssm_pool is None else ssm_pool).copy()
+    pool = wl.ssm_pool if ssm_pool is None else ssm_pool
+    pool = pool if inplace else pool.copy()
     y = np.zeros((xa.shape[0], sh.d_inner), dtype=xa.dtype)
     st = oracle.scan(y, xa, wl.dt if dt is None else dt, wl.a_log, wl.dt_bias, wl.D, pool,
                      wl.run_lengths if run_lengths is None else run_lengths,

@@ -1,0 +1,153 @@
+"""The C-ABI library on the CPU: it loads, exports every function the header declares,
+and rejects malformed calls on the host before any launch (no GPU needed)."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mamba2.h")
+
+
+@pytest.fixture(scope="module")
+def ops():
+    from mamba2_selective_scan_causalconv1d_amd import _lib, build
+
+    if not os.path.exists(_lib.LIB_PATH):
+        build.build()
+    from mamba2_selective_scan_causalconv1d_amd import ops as o
+
+    return o
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(mamba2_\w+)\s*\(", src, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_declared_function(ops):
+    names = _declared_functions()
+    assert len(names) >= 11, names
+    lib = ctypes.CDLL(ops._lib.LIB_PATH)
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    declared_py = {n for n, _, _ in ops._lib.SIGNATURES}
+    assert declared_py == set(names)
+
+
+def _dims(ops, **kw):
+    base = dict(nheads=4, headdim=8, d_state=8, ngroups=2, conv_kernel=4, chunk_size=16, pool_slots=6,
+                act="bf16")
+    base.update(kw)
+    return ops.make_dims(**base)
+
+
+CASES = [
+    ("ok", [3, 4], [0, 1], 7, False),
+    ("slot_high", [3, 4], [0, 6], 7, False),
+    ("slot_negative", [3, 4], [-1, 1], 7, False),
+    ("slot_shared", [3, 4], [2, 2], 7, False),
+    ("rows_not_covered", [3, 3], [0, 1], 7, False),
+    ("rows_overrun", [3, 5], [0, 1], 7, False),
+    ("zero_length", [0, 7], [0, 1], 7, False),
+    ("negative_length", [-1, 8], [0, 1], 7, False),
+    ("decode_ok", [1, 1], [0, 1], 2, True),
+    ("decode_long_run", [1, 2], [0, 1], 3, True),
+    ("empty", [], [], 0, False),
+    ("empty_with_rows", [], [], 3, False),
+]
+
+
+@pytest.mark.parametrize("name,lens,slots,T,decode", CASES)
+def test_validation_agrees_with_oracle_rules(ops, name, lens, slots, T, decode):
+    """The library's host checks and the oracle's (written separately from the same page
+    rules) give the same status for every case."""
+    b = ops.RecurrentBatch(lens, slots, [0] * len(lens), device=None)
+    b.c.num_rows = T
+    got = ops.validate(b, _dims(ops), decode)
+    want = oracle.check_batch(T, lens, slots, 6, decode)
+    assert got == want, (name, got, want)
+
+
+def test_entry_points_reject_before_launch(ops):
+    """Malformed batches and unsupported dims return their status from every entry point
+    on a machine with no GPU (nothing is launched, nothing is written).  The calls pass host
+    pointers, so the test is kept off machines with a GPU: the same rejections are checked
+    through the GPU path, with device buffers, by the gpu-marked tests."""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("host-pointer rejection checks run on CPU-only machines")
+    from mamba2_selective_scan_causalconv1d_amd import _lib
+
+    d = _dims(ops)
+    host = np.zeros(4096, dtype=np.float32)
+    p = host.ctypes.data
+    for lens, slots, code in (([3, 4], [2, 2], _lib.SLOT_SHARED), ([3, 4], [0, 9], _lib.SLOT_OUT_OF_RANGE),
+                              ([3, 3], [0, 1], _lib.RUN_LENGTHS)):
+        b = ops.RecurrentBatch(lens, slots, [0] * len(lens), device=None)
+        b.c.num_rows = 7
+        L = ops.LIB
+        assert L.mamba2_conv1d(p, p, p, p, p, b.ref(), ctypes.byref(d), None) == code
+        assert L.mamba2_scan_prefill(p, p, p, p, p, p, p, b.ref(), ctypes.byref(d), p, 1 << 20, None) == code
+        assert L.mamba2_scan_decode(p, p, p, p, p, p, p, b.ref(), ctypes.byref(d), None) in (
+            code, _lib.RUN_LENGTHS)
+    assert not host.any()
+    b = ops.RecurrentBatch([3, 4], [0, 1], [0, 0], device=None)
+    L = ops.LIB
+    # null pointers
+    assert L.mamba2_conv1d(None, p, p, p, p, b.ref(), ctypes.byref(d), None) == _lib.INVALID_ARGUMENT
+    # bad dims
+    bad = _dims(ops, nheads=3)  # not a multiple of ngroups
+    assert L.mamba2_validate(b.ref(), ctypes.byref(bad), 0) == _lib.INVALID_ARGUMENT
+    bad = _dims(ops, act=5)
+    assert L.mamba2_validate(b.ref(), ctypes.byref(bad), 0) == _lib.INVALID_ARGUMENT
+    # unsupported conv kernel width / channel count
+    k5 = _dims(ops, conv_kernel=5)
+    assert L.mamba2_conv1d(p, p, p, p, p, b.ref(), ctypes.byref(k5), None) == _lib.NOT_IMPLEMENTED
+    odd = _dims(ops, headdim=3, d_state=4, nheads=2, ngroups=1)  # Dc = 6 + 8 = 14
+    assert L.mamba2_conv1d(p, p, p, p, p, b.ref(), ctypes.byref(odd), None) == _lib.NOT_IMPLEMENTED
+    # workspace too small
+    assert L.mamba2_scan_prefill(p, p, p, p, p, p, p, b.ref(), ctypes.byref(d), p, 16, None) == \
+        _lib.WORKSPACE_TOO_SMALL
+    # decode needs run lengths of 1
+    assert L.mamba2_scan_decode(p, p, p, p, p, p, p, b.ref(), ctypes.byref(d), None) == _lib.RUN_LENGTHS
+    # norm argument checks
+    assert L.mamba2_gated_rmsnorm(p, p, p, p, 3, 1e-5, 4, 64, 1, None) == _lib.INVALID_ARGUMENT
+    assert L.mamba2_gated_rmsnorm(p, p, p, p, 2, -1.0, 4, 64, 1, None) == _lib.INVALID_ARGUMENT
+    assert L.mamba2_gated_rmsnorm(p, p, p, p, 16, 1e-5, 4, 64, 1, None) == _lib.NOT_IMPLEMENTED
+    assert L.mamba2_gated_rmsnorm(p, p, p, p, 1, 1e-5, 0, 64, 1, None) == _lib.OK
+    assert not host.any()
+
+
+def test_state_size_closed_form(ops):
+    """InfiniLM PR #575, 'Motivation': conv + fp32 SSM state of mamba2-130m (TP1, BF16) is about
+    18.25 MiB per request -- the slot layout [K-1, Dc] act + [H, P, N] fp32 gives that figure."""
+    g = json.load(open(os.path.join(ROOT, "tests", "golden", "state_size_130m.json")))
+    d = ops.make_dims(g["nheads"], g["headdim"], g["d_state"], g["ngroups"], g["conv_kernel"], 256, 1,
+                      "bf16")
+    per_layer = ops.ssm_slot_bytes(d) + ops.conv_slot_bytes(d)
+    assert per_layer == g["bytes_per_layer"] == 797184
+    assert round(per_layer * g["layers"] / 2 ** 20, 2) == g["mib_per_request_printed"]
+    # the readings the figure rules out: K rows of conv state, or an fp32 conv state
+    dk = ops.make_dims(g["nheads"], g["headdim"], g["d_state"], g["ngroups"], g["conv_kernel"] + 1, 256, 1,
+                       "bf16")
+    assert round((ops.ssm_slot_bytes(dk) + ops.conv_slot_bytes(dk)) * 24 / 2 ** 20, 2) != 18.25
+    df = ops.make_dims(g["nheads"], g["headdim"], g["d_state"], g["ngroups"], g["conv_kernel"], 256, 1, "f32")
+    assert round((ops.ssm_slot_bytes(df) + ops.conv_slot_bytes(df)) * 24 / 2 ** 20, 2) != 18.25
+
+
+def test_workspace_size(ops):
+    d = _dims(ops)
+    b = ops.RecurrentBatch([30, 5], [0, 1], [1, 0], device=None)
+    n = ops.scan_prefill_workspace_bytes(b, d)
+    assert n > 0 and n % 256 == 0
+    bad = ops.RecurrentBatch([30, 5], [0, 0], [1, 0], device=None)
+    assert ops.scan_prefill_workspace_bytes(bad, d) == 0

@@ -1,0 +1,334 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle, on the seeded workloads.
+
+Bars: bf16 outputs |err| <= 2e-2 (1 + |ref|); fp32 outputs and SSM states |err| <= 1e-3 (1 + |ref|);
+conv states, written-slot sets, untouched slots and error behaviour bit-exact.
+Per-op checks feed both sides the same inputs (the oracle's upstream outputs); the chained
+checks run each side's own pipeline end to end.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from mamba2_selective_scan_causalconv1d_amd import workloads as W
+from _util import BF16_BAR, F32_BAR, assert_close, bar_for, oracle_conv, oracle_norm, oracle_scan
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    assert torch.cuda.is_available(), "the gpu tests need an MI355X"
+    import _gpu
+
+    return _gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def _check_pools(wl, named, ssm_got, ssm_ref, conv_got=None, conv_ref=None):
+    """Named slots: SSM within the fp32 bar, conv bit-exact; every other slot untouched."""
+    M = wl.shape.pool_slots
+    named = set(int(s) for s in named)
+    for s in range(M):
+        if s in named:
+            assert_close(ssm_got[s], ssm_ref[s], F32_BAR, "ssm slot %d" % s)
+            if conv_got is not None:
+                assert np.array_equal(conv_got[s], conv_ref[s]), "conv slot %d" % s
+        else:
+            assert ssm_got[s].tobytes() == wl.ssm_pool[s].tobytes(), "untouched ssm slot %d" % s
+            if conv_got is not None:
+                assert conv_got[s].tobytes() == wl.conv_pool[s].tobytes(), "untouched conv slot %d" % s
+
+
+def _prefill_parity(gpu, wl):
+    """Each op of the GPU chain against the oracle run on the same inputs: the conv on the
+    workload's rows, the scan on the GPU's conv output, the norm on the GPU's y.  (Comparing
+    the two chains end to end would compare each side's own rounding of the intermediates,
+    which the scan amplifies: one-ulp bf16 changes in its inputs move y by several bars.)"""
+    sh = wl.shape
+    bar = bar_for(sh.act)
+    b = gpu.batch_of(wl)
+    p = gpu.Params(wl)
+    say("[%s] T=%d S=%d H=%d P=%d N=%d act=%s" % (wl.name, wl.num_rows, len(wl.run_lengths), sh.nheads,
+                                                sh.headdim, sh.d_state, sh.act))
+    xa_o, cp_o = oracle_conv(wl)
+    xa_g, cp_g = gpu.gpu_conv(wl, wl.xbc, wl.conv_pool, b, p)
+    f = assert_close(gpu.f32(xa_g), gpu.f32(xa_o), bar, "conv out")
+    say("  conv out: %.3g of bar" % f)
+    y_o, sp_o = oracle_scan(wl, xa_g)
+    y_g, sp_g = gpu.gpu_scan(wl, xa_g, wl.dt, wl.ssm_pool, b, p)
+    f = assert_close(gpu.f32(y_g), gpu.f32(y_o), bar, "scan y")
+    say("  scan y: %.3g of bar" % f)
+    _check_pools(wl, wl.slots, sp_g, sp_o, cp_g, cp_o)
+    out_o = oracle_norm(wl, y_g)
+    out_g = gpu.gpu_norm(wl, y_g, wl.z)
+    f = assert_close(gpu.f32(out_g), gpu.f32(out_o), bar, "norm out")
+    say("  norm out: %.3g of bar" % f)
+
+
+def test_tiny_fp32(gpu):
+    _prefill_parity(gpu, W.tiny_fp32())
+
+
+def test_130m_prefill(gpu):
+    _prefill_parity(gpu, W.layer_130m_prefill())
+
+
+def test_varlen_prefill(gpu):
+    _prefill_parity(gpu, W.varlen_prefill())
+
+
+def test_varlen_slow_decay(gpu):
+    """Slow decay keeps resumed states and the state carried across chunks visible."""
+    _prefill_parity(gpu, W.varlen_slow_decay())
+
+
+def test_long_prefill_sampled(gpu):
+    """4 x 16384 rows, 48 heads, norm over 8 groups: conv and norm compared in full, the scan
+    on four heads (all rows and final states) -- heads are independent, so the oracle computes
+    the sampled heads exactly as a full run would."""
+    wl = W.long_prefill()
+    sh = wl.shape
+    b = gpu.batch_of(wl)
+    p = gpu.Params(wl)
+    say("[%s] conv" % wl.name)
+    xa_o, cp_o = oracle_conv(wl)
+    xa_g, cp_g = gpu.gpu_conv(wl, wl.xbc, wl.conv_pool, b, p)
+    say("  conv out: %.3g of bar" % assert_close(gpu.f32(xa_g), gpu.f32(xa_o), BF16_BAR, "conv out"))
+    assert np.array_equal(cp_g, cp_o)
+    del xa_o
+    heads = [0, 17, 30, 47]
+    mask = np.zeros(sh.nheads, dtype=np.uint8)
+    mask[heads] = 1
+    say("  scan (oracle on heads %s)" % heads)
+    y_o, sp_o = oracle_scan(wl, xa_g, head_mask=mask)
+    y_g, sp_g = gpu.gpu_scan(wl, xa_g, wl.dt, wl.ssm_pool, b, p)
+    P = sh.headdim
+    for h in heads:
+        cols = slice(h * P, (h + 1) * P)
+        f = assert_close(gpu.f32(y_g[:, cols]), gpu.f32(y_o[:, cols]), BF16_BAR, "y head %d" % h)
+        for s in wl.slots:
+            assert_close(sp_g[s, h], sp_o[s, h], F32_BAR, "state slot %d head %d" % (s, h))
+    say("  scan y (sampled heads) ok, last %.3g of bar" % f)
+    say("  norm")
+    out_o = oracle_norm(wl, y_g)  # the norm on the GPU's own y (full rows needed)
+    out_g = gpu.gpu_norm(wl, y_g, wl.z)
+    say("  norm out: %.3g of bar" % assert_close(gpu.f32(out_g), gpu.f32(out_o), BF16_BAR, "norm out"))
+
+
+def test_decode_64_steps(gpu):
+    """256 one-row requests on 512 slots, 10% fresh over dirty slots, 64 successive steps.
+    Each step: conv on the step's rows (both sides), the decode scan on the GPU's conv output,
+    the norm on the GPU's y; each side carries its own conv and SSM pools across steps."""
+    wl = W.decode_batch()
+    sh = wl.shape
+    p = gpu.Params(wl)
+    fresh0 = wl.fresh
+    cp_o, sp_o = wl.conv_pool.copy(), wl.ssm_pool.copy()
+    cp_g, sp_g = gpu.ops.to_device(wl.conv_pool), gpu.ops.to_device(wl.ssm_pool)
+    dims = gpu.dims_of(sh)
+    worst = [0.0, 0.0, 0.0]
+    for step, (xbc, z, dt) in enumerate(wl.steps):
+        fresh = fresh0 if step == 0 else np.zeros_like(fresh0)
+        b = gpu.batch_of(wl, fresh=fresh)
+        x = gpu.ops.to_device(xbc)
+        xa = torch.empty_like(x)
+        gpu.ops.conv1d(xa, x, p.conv_w, p.conv_b, cp_g, b, dims)
+        y = torch.empty((x.shape[0], sh.d_inner), dtype=x.dtype, device="cuda")
+        gpu.ops.scan_decode(y, xa, gpu.ops.to_device(dt), p.a_log, p.dt_bias, p.D, sp_g, b, dims)
+        out = torch.empty_like(y)
+        gpu.ops.gated_rmsnorm(out, y, gpu.ops.to_device(z), p.norm_w, sh.norm_groups, sh.eps)
+        torch.cuda.synchronize()
+        xa_h, y_h, out_h = gpu.ops.to_host(xa), gpu.ops.to_host(y), gpu.ops.to_host(out)
+        xa_o, cp_o = oracle_conv(wl, xbc=xbc, conv_pool=cp_o, fresh=fresh, inplace=True)
+        y_o, sp_o = oracle_scan(wl, xa_h, dt=dt, ssm_pool=sp_o, fresh=fresh, decode=True, inplace=True)
+        out_o = oracle_norm(wl, y_h, z=z)
+        fs = (assert_close(gpu.f32(xa_h), gpu.f32(xa_o), BF16_BAR, "conv step %d" % step),
+              assert_close(gpu.f32(y_h), gpu.f32(y_o), BF16_BAR, "y step %d" % step),
+              assert_close(gpu.f32(out_h), gpu.f32(out_o), BF16_BAR, "out step %d" % step))
+        worst = [max(a, c) for a, c in zip(worst, fs)]
+        if step % 16 == 0:
+            say("  step %d: conv %.3g, y %.3g, out %.3g of bar" % ((step,) + fs))
+    say("  decode worst: conv %.3g, y %.3g, out %.3g of bar" % tuple(worst))
+    _check_pools(wl, wl.slots, gpu.ops.to_host(sp_g), sp_o, gpu.ops.to_host(cp_g), cp_o)
+
+
+# ------------------------------------------------------------ invariants and edge cases
+
+SMALL = W.Shape(nheads=4, headdim=8, d_state=8, ngroups=2, conv_kernel=4, chunk_size=16, norm_groups=2,
+                pool_slots=6, act="bf16")
+MFMA_SHAPE = W.Shape(nheads=4, headdim=64, d_state=128, ngroups=2, conv_kernel=4, chunk_size=256,
+                     norm_groups=1, pool_slots=6, act="bf16")
+SHAPES = {"small": SMALL, "p64n128": MFMA_SHAPE}
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_ragged_batch_with_short_runs(gpu, shape):
+    """Runs of 1, 2 (shorter than the conv history), ragged multi-chunk runs, fresh and resumed."""
+    sh = SHAPES[shape]
+    lens = [1, 2, 3, 77, 300, 5, 129]
+    wl = W.random_prefill(50, W.Shape(**{**sh.__dict__, "pool_slots": 9}), lens,
+                          fresh=[1, 0, 0, 1, 0, 1, 0])
+    _prefill_parity(gpu, wl)
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_split_vs_whole(gpu, shape):
+    """Conv outputs and states bit-exact between one call and a split {1, 2, L-3, ...};
+    the scan within the bars."""
+    sh = SHAPES[shape]
+    L = 200
+    wl = W.random_prefill(51, sh, [L], fresh=[1], slots=[2])
+    p = gpu.Params(wl)
+    whole_b = gpu.batch_of(wl)
+    xa_w, cp_w = gpu.gpu_conv(wl, wl.xbc, wl.conv_pool, whole_b, p)
+    y_w, sp_w = gpu.gpu_scan(wl, xa_w, wl.dt, wl.ssm_pool, whole_b, p)
+    for split in ([1, 2, L - 3], [64, 1, 63, L - 128]):
+        cp, sp = wl.conv_pool.copy(), wl.ssm_pool.copy()
+        xs, ys = [], []
+        r = 0
+        for i, n in enumerate(split):
+            b = gpu.batch_of(wl, run_lengths=[n], fresh=[1 if i == 0 else 0])
+            xa, cp = gpu.gpu_conv(wl, np.ascontiguousarray(wl.xbc[r:r + n]), cp, b, p)
+            y, sp = gpu.gpu_scan(wl, xa, np.ascontiguousarray(wl.dt[r:r + n]), sp, b, p)
+            xs.append(xa)
+            ys.append(y)
+            r += n
+        assert np.array_equal(np.concatenate(xs), xa_w)
+        assert np.array_equal(cp, cp_w)
+        assert_close(gpu.f32(np.concatenate(ys)), gpu.f32(y_w), BF16_BAR, "split y")
+        assert_close(sp[2], sp_w[2], F32_BAR, "split state")
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_fresh_ignores_dirty_slot(gpu, shape):
+    """NaN in the slots of fresh sequences changes nothing (bit for bit)."""
+    sh = SHAPES[shape]
+    wl = W.random_prefill(52, sh, [70, 9], fresh=[1, 1], slots=[0, 5])
+    p = gpu.Params(wl)
+    b = gpu.batch_of(wl)
+    res = []
+    for fill in (np.nan, 0.0):
+        cp, sp = wl.conv_pool.copy(), wl.ssm_pool.copy()
+        cp[[0, 5]] = W.to_act(np.full(cp[[0, 5]].shape, fill, np.float32), sh.act)
+        sp[[0, 5]] = fill
+        xa, cp2 = gpu.gpu_conv(wl, wl.xbc, cp, b, p)
+        y, sp2 = gpu.gpu_scan(wl, xa, wl.dt, sp, b, p)
+        res.append((xa, cp2, y, sp2))
+    for a, c in zip(*res):
+        assert np.array_equal(a, c)
+    assert np.isfinite(gpu.f32(res[0][2])).all()
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_swapped_slots_match_solo(gpu, shape):
+    sh = SHAPES[shape]
+    la, lb = 90, 133
+    wl = W.random_prefill(53, sh, [la, lb], fresh=[1, 0], slots=[1, 3])
+    p = gpu.Params(wl)
+    xa, _ = oracle_conv(wl)
+    ya, pa = gpu.gpu_scan(wl, np.ascontiguousarray(xa[:la]), np.ascontiguousarray(wl.dt[:la]), wl.ssm_pool,
+                          gpu.batch_of(wl, run_lengths=[la], slots=[1], fresh=[1]), p)
+    yb, pb = gpu.gpu_scan(wl, np.ascontiguousarray(xa[la:]), np.ascontiguousarray(wl.dt[la:]), wl.ssm_pool,
+                          gpu.batch_of(wl, run_lengths=[lb], slots=[3], fresh=[0]), p)
+    sigma = wl.ssm_pool[3].copy()
+    for sa, sb in ((1, 3), (3, 1)):
+        pool = wl.ssm_pool.copy()
+        pool[sb] = sigma
+        pool[sa] = -5.0
+        y, pp = gpu.gpu_scan(wl, xa, wl.dt, pool, gpu.batch_of(wl, slots=[sa, sb], fresh=[1, 0]), p)
+        assert_close(gpu.f32(y[:la]), gpu.f32(ya), BF16_BAR, "a")
+        assert_close(gpu.f32(y[la:]), gpu.f32(yb), BF16_BAR, "b")
+        assert_close(pp[sa], pa[1], F32_BAR, "state a")
+        assert_close(pp[sb], pb[3], F32_BAR, "state b")
+
+
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_head_to_group(gpu, shape):
+    """Zeroing group 1's B and C: heads of group 1 give D*x with a zero state, group 0's heads
+    are unchanged."""
+    sh = SHAPES[shape]
+    wl = W.random_prefill(54, sh, [150], fresh=[1], slots=[2])
+    p = gpu.Params(wl)
+    b = gpu.batch_of(wl)
+    xa, _ = oracle_conv(wl)
+    y0, _ = gpu.gpu_scan(wl, xa, wl.dt, wl.ssm_pool, b, p)
+    xz = xa.copy()
+    Di, GN, N, P = sh.d_inner, sh.ngroups * sh.d_state, sh.d_state, sh.headdim
+    xz[:, Di + N:Di + 2 * N] = 0
+    xz[:, Di + GN + N:Di + GN + 2 * N] = 0
+    y1, s1 = gpu.gpu_scan(wl, xz, wl.dt, wl.ssm_pool, b, p)
+    half = sh.nheads // 2
+    assert_close(gpu.f32(y1[:, :half * P]), gpu.f32(y0[:, :half * P]), BF16_BAR, "group 0 heads")
+    for h in range(half, sh.nheads):
+        x = gpu.f32(xa[:, h * P:(h + 1) * P]).astype(np.float64)
+        assert_close(gpu.f32(y1[:, h * P:(h + 1) * P]), np.float64(wl.D[h]) * x, BF16_BAR, "D*x head %d" % h)
+        assert not s1[2, h].any()
+
+
+def test_malformed_batches_through_gpu_abi(gpu):
+    """Each rejected call leaves outputs and pools byte-identical (device buffers)."""
+    from mamba2_selective_scan_causalconv1d_amd import _lib, ops
+
+    wl = W.random_prefill(55, SMALL, [3, 4], fresh=[0, 0], slots=[0, 1])
+    p = gpu.Params(wl)
+    dims = gpu.dims_of(SMALL)
+    x = ops.to_device(wl.xbc)
+    dt = ops.to_device(wl.dt)
+    out = torch.full_like(x, 7.0)
+    y = torch.full((7, SMALL.d_inner), 5.0, dtype=x.dtype, device="cuda")
+    cp, sp = ops.to_device(wl.conv_pool), ops.to_device(wl.ssm_pool)
+    cases = [([3, 4], [0, 6], _lib.SLOT_OUT_OF_RANGE), ([3, 4], [2, 2], _lib.SLOT_SHARED),
+             ([3, 3], [0, 1], _lib.RUN_LENGTHS), ([0, 7], [0, 1], _lib.RUN_LENGTHS)]
+    for lens, slots, code in cases:
+        b = ops.RecurrentBatch(lens, slots, [0, 0])
+        b.c.num_rows = 7
+        with pytest.raises(ops.Mamba2Error) as e:
+            ops.conv1d(out, x, p.conv_w, p.conv_b, cp, b, dims)
+        assert e.value.status == code
+        with pytest.raises(ops.Mamba2Error) as e:
+            ops.scan_prefill(y, x, dt, p.a_log, p.dt_bias, p.D, sp, b, dims)
+        assert e.value.status == code
+    with pytest.raises(ops.Mamba2Error) as e:
+        ops.scan_decode(y, x, dt, p.a_log, p.dt_bias, p.D, sp, ops.RecurrentBatch([3, 4], [0, 1], [0, 0]), dims)
+    assert e.value.status == _lib.RUN_LENGTHS
+    torch.cuda.synchronize()
+    assert (out == 7).all() and (y == 5).all()
+    assert np.array_equal(ops.to_host(cp), wl.conv_pool) and np.array_equal(ops.to_host(sp), wl.ssm_pool)
+
+
+def test_empty_batch_is_a_noop(gpu):
+    from mamba2_selective_scan_causalconv1d_amd import ops
+
+    wl = W.random_prefill(56, SMALL, [5], fresh=[0], slots=[0])
+    p = gpu.Params(wl)
+    dims = gpu.dims_of(SMALL)
+    b = ops.RecurrentBatch([], [], [])
+    cp, sp = ops.to_device(wl.conv_pool), ops.to_device(wl.ssm_pool)
+    e = torch.empty((0, SMALL.conv_dim), dtype=torch.bfloat16, device="cuda")
+    ops.conv1d(e, e, p.conv_w, p.conv_b, cp, b, dims)
+    ops.scan_prefill(torch.empty((0, SMALL.d_inner), dtype=torch.bfloat16, device="cuda"), e,
+                     torch.empty((0, 4), dtype=torch.bfloat16, device="cuda"), p.a_log, p.dt_bias, p.D, sp, b, dims)
+    torch.cuda.synchronize()
+    assert np.array_equal(ops.to_host(cp), wl.conv_pool) and np.array_equal(ops.to_host(sp), wl.ssm_pool)
+
+
+@pytest.mark.parametrize("groups,act", [(1, "bf16"), (8, "bf16"), (2, "f32"), (48, "bf16")])
+def test_norm_group_widths(gpu, groups, act):
+    """Norm groups of 3072, 384, 1536 (fp32) and 64 columns, weight ~ N(1, 0.1)."""
+    rng = np.random.default_rng(57)
+    Di = 3072
+    y = W.to_act(rng.standard_normal((33, Di), dtype=np.float32), act)
+    z = W.to_act(rng.standard_normal((33, Di), dtype=np.float32), act)
+    w = rng.normal(1, 0.1, Di).astype(np.float32)
+    sh = W.Shape(48, 64, 128, 1, 4, 256, groups, 1, act)
+    wl = W.Workload("norm", 57, sh, np.array([33], np.int32), np.array([0], np.int32), np.array([1], np.uint8),
+                    None, None, None, None, None, w, None, None, z=z)
+    out_o = oracle_norm(wl, y, z=z, weight=w, groups=groups)
+    out_g = gpu.gpu_norm(wl, y, z, weight=w, groups=groups)
+    assert_close(gpu.f32(out_g), gpu.f32(out_o), bar_for(act), "norm")
