@@ -93,10 +93,9 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 }  // namespace
 
-bool scan_uses_mfma(const mamba2_dims* d) {
-  (void)d;
-  return false;
-}
+bool scan_mfma_supported(const mamba2_dims* d);
+
+bool scan_uses_mfma(const mamba2_dims* d) { return scan_mfma_supported(d); }
 
 int32_t scan_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims* d, bool mfma) {
   if (!mfma) {
