@@ -34,7 +34,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-rows", type=int, default=4096)
+    ap.add_argument("--no-decode", action="store_true", help="prefill only (for counter runs)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="also run a plain device copy of this many MB (calibrates traffic counters)")
+    ap.add_argument("--cpu-sample-rows", type=int, default=16384)
     return ap.parse_args()
 
 
@@ -51,7 +54,7 @@ def kernel_bytes_flops(name, wl, nrows):
         q = 64
         flops = T * H * (N * (q + 1) / (H // G) + P * (q + 1) + 4 * N * P)
         return T * (Dc + H + Di) * a + (S + resumed) * H * P * N * 4, flops
-    if name in ("gated_rmsnorm", "gated_rmsnorm_wide"):
+    if name in ("gated_rmsnorm", "gated_rmsnorm_unit", "gated_rmsnorm_wide"):
         return 3 * T * Di * a + Di * 4, 0
     if name == "scan_decode":
         return (T * (Dc + H + Di) * a + (S + resumed) * H * P * N * 4), 6 * T * H * P * N
@@ -144,7 +147,57 @@ def main():
                 "unit": "GB/s", "frac": dr.get("frac_hbm"), "traffic": None,
                 "avg_us": kernels[dom]["avg_us"]}
 
+    if args.copy_calibration_mb:
+        # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE give the counters' scale
+        src = torch.empty(args.copy_calibration_mb * (1 << 20) // 2, dtype=torch.bfloat16, device=dev)
+        src.fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---------------------------------------------------------------- decode
+    decode_us, dkern, dec_roof, R, dsh, dsteps = None, None, None, None, None, []
+    if not args.no_decode:
+        decode_us, dkern, dec_roof, R, dsh, dsteps = run_decode(args, torch, ops, W, dev, e0, e1)
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(args, W, wl, sh)
+
+    res = {
+        "metric": "Mamba2 mixer prefill tokens/s + decode us/step; % of HBM/MFMA roofline",
+        "value": T / (ms_per_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "long_prefill_4x16384", "global_batch": 4, "seq_len": 16384, "nheads": 48,
+                   "headdim": 64, "d_state": 128, "ngroups": 1, "conv_kernel": 4, "norm_groups": 8,
+                   "parallelism": "single_gpu"},
+        "decode_us_per_step": decode_us,
+        "decode_config": None if args.no_decode else
+        {"workload": "decode_256x64", "requests": R, "pool_slots": dsh.pool_slots, "steps": len(dsteps)},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "rooflines": rooflines,
+        "decode_kernels": dkern,
+        "decode_roofline": dec_roof,
+    }
+    print(json.dumps(res))
+
+
+def run_decode(args, torch, ops, W, dev, e0, e1):
+    d = ops.to_device
     dwl = W.decode_batch()
     dsh = dwl.shape
     ddims = ops.make_dims(dsh.nheads, dsh.headdim, dsh.d_state, dsh.ngroups, dsh.conv_kernel, dsh.chunk_size,
@@ -201,58 +254,37 @@ def main():
     dec_roof = {"kernel": "scan_decode", "achieved_GBs": dec_bytes / (dkern["scan_decode"]["avg_us"] * 1e-6) / 1e9}
     dec_roof["frac_hbm"] = dec_roof["achieved_GBs"] / HBM_PEAK_GBS
 
-    # ---------------------------------------------------------------- CPU oracle baseline
-    cpu = None
-    if not args.no_cpu_baseline:
-        import oracle
+    return decode_us, dkern, dec_roof, R, dsh, dsteps
 
-        L = min(args.cpu_sample_rows, int(wl.run_lengths[0]))
-        sub = W.Workload(wl.name, wl.seed, sh, np.array([L], np.int32), np.array([0], np.int32),
-                         np.array([1], np.uint8), wl.conv_w, wl.conv_b, wl.dt_bias, wl.a_log, wl.D, wl.norm_w,
-                         wl.conv_pool[:1].copy(), wl.ssm_pool[:1].copy(), np.ascontiguousarray(wl.xbc[:L]),
-                         np.ascontiguousarray(wl.z[:L]), np.ascontiguousarray(wl.dt[:L]))
-        t0 = time.perf_counter()
-        oa = np.zeros_like(sub.xbc)
-        cp = sub.conv_pool.copy()
-        assert oracle.conv1d(oa, sub.xbc, sub.conv_w, sub.conv_b, cp, sub.run_lengths, sub.slots, sub.fresh) == 0
-        oy = np.zeros((L, sh.d_inner), dtype=sub.xbc.dtype)
-        sp = sub.ssm_pool.copy()
-        assert oracle.scan(oy, oa, sub.dt, sub.a_log, sub.dt_bias, sub.D, sp, sub.run_lengths, sub.slots,
-                           sub.fresh, sh.ngroups) == 0
-        oo = np.zeros_like(oy)
-        assert oracle.gated_rmsnorm(oo, oy, sub.z, sub.norm_w, sh.norm_groups, sh.eps) == 0
-        dt_cpu = time.perf_counter() - t0
-        cpu = {"value": L / dt_cpu, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-               "sample": "first %d rows of one long-prefill sequence (all 48 heads, conv+scan+norm), %.1fs"
-                         % (L, dt_cpu)}
 
-    res = {
-        "metric": "Mamba2 mixer prefill tokens/s + decode us/step; % of HBM/MFMA roofline",
-        "value": T / (ms_per_step * 1e-3),
-        "unit": "tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "long_prefill_4x16384", "global_batch": 4, "seq_len": 16384, "nheads": 48,
-                   "headdim": 64, "d_state": 128, "ngroups": 1, "conv_kernel": 4, "norm_groups": 8,
-                   "parallelism": "single_gpu"},
-        "decode_us_per_step": decode_us,
-        "decode_config": {"workload": "decode_256x64", "requests": R, "pool_slots": dsh.pool_slots,
-                          "steps": len(dsteps)},
-        "roofline": roofline,
-        "cpu_baseline": cpu,
-        "kernels": kernels,
-        "rooflines": rooflines,
-        "decode_kernels": dkern,
-        "decode_roofline": dec_roof,
-    }
-    print(json.dumps(res))
+def cpu_baseline(args, W, wl, sh):
+    """The oracle (as it stands) on the first cpu_sample_rows rows of every sequence of the
+    long-prefill batch (the whole batch by default): conv, scan and gated norm."""
+    import oracle
+
+    L = min(args.cpu_sample_rows, int(wl.run_lengths.min()))
+    S = len(wl.run_lengths)
+    cu = np.concatenate([[0], np.cumsum(wl.run_lengths)])
+    rows = np.concatenate([np.arange(cu[s], cu[s] + L) for s in range(S)])
+    sub = W.Workload(wl.name, wl.seed, sh, np.full(S, L, np.int32), wl.slots.copy(), wl.fresh.copy(), wl.conv_w,
+                     wl.conv_b, wl.dt_bias, wl.a_log, wl.D, wl.norm_w, wl.conv_pool.copy(), wl.ssm_pool.copy(),
+                     np.ascontiguousarray(wl.xbc[rows]), np.ascontiguousarray(wl.z[rows]),
+                     np.ascontiguousarray(wl.dt[rows]))
+    t0 = time.perf_counter()
+    oa = np.zeros_like(sub.xbc)
+    cp = sub.conv_pool.copy()
+    assert oracle.conv1d(oa, sub.xbc, sub.conv_w, sub.conv_b, cp, sub.run_lengths, sub.slots, sub.fresh) == 0
+    oy = np.zeros((S * L, sh.d_inner), dtype=sub.xbc.dtype)
+    sp = sub.ssm_pool.copy()
+    assert oracle.scan(oy, oa, sub.dt, sub.a_log, sub.dt_bias, sub.D, sp, sub.run_lengths, sub.slots,
+                       sub.fresh, sh.ngroups) == 0
+    oo = np.zeros_like(oy)
+    assert oracle.gated_rmsnorm(oo, oy, sub.z, sub.norm_w, sh.norm_groups, sh.eps) == 0
+    dt_cpu = time.perf_counter() - t0
+    cpu = {"value": S * L / dt_cpu, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+           "sample": "%d sequences x first %d rows of the long-prefill batch (48 heads, conv+scan+norm), "
+                     "%.1f s wall" % (S, L, dt_cpu)}
+    return cpu
 
 
 if __name__ == "__main__":

@@ -75,7 +75,9 @@ struct Act<bf16_t> {
 // softplus without a clamp; above 20 the identity is exact to fp32 precision.
 __device__ __forceinline__ float softplus_f32(float v) { return v > 20.f ? v : log1pf(__expf(v)); }
 
-__device__ __forceinline__ float silu_f32(float v) { return v / (1.f + __expf(-v)); }
+// silu(v) = v / (1 + e^-v); the reciprocal is the hardware approximation (~1 ulp), far
+// below the bf16 / fp32 output rounding of every op that uses it.
+__device__ __forceinline__ float silu_f32(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

@@ -109,33 +109,42 @@ __global__ __launch_bounds__(256) void conv1d_silu_kernel(
     }
 
     while (t < run_end) {
+      // four rows at a time: the window holds the K-1 previous rows, then the four new ones
       const int n = min(4, run_end - t);
+      float xf[H1 + 4][V];
+#pragma unroll
+      for (int r = 0; r < H1; ++r)
+#pragma unroll
+        for (int i = 0; i < V; ++i) xf[r][i] = win[r][i];
       uint4 xv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        if (j < n) xv[j] = *reinterpret_cast<const uint4*>(x + (size_t)(t + j) * Dc + col);
+        xv[j] = j < n ? *reinterpret_cast<const uint4*>(x + (size_t)(t + j) * Dc + col) : make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) Act<T>::unpack(xv[j], xf[H1 + j]);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (j < n) {
-          float xf[V], out[V];
-          Act<T>::unpack(xv[j], xf);
+          float out[V];
 #pragma unroll
           for (int i = 0; i < V; ++i) {
             float pre = br[i];
 #pragma unroll
-            for (int k = 0; k < H1; ++k) pre = fmaf(wr[i][k], win[k][i], pre);
-            pre = fmaf(wr[i][H1], xf[i], pre);
+            for (int k = 0; k < K; ++k) pre = fmaf(wr[i][k], xf[j + k][i], pre);
             out[i] = silu_f32(pre);
           }
           *reinterpret_cast<uint4*>(dst + (size_t)(t + j) * Dc + col) = Act<T>::pack(out);
-#pragma unroll
-          for (int k = 0; k + 1 < H1; ++k)
-#pragma unroll
-            for (int i = 0; i < V; ++i) win[k][i] = win[k + 1][i];
-#pragma unroll
-          for (int i = 0; i < V; ++i) win[H1 - 1][i] = xf[i];
         }
       }
+      // the window for the next rows: the last K-1 of the K-1 + n rows
+#pragma unroll
+      for (int r = 0; r < H1; ++r)
+#pragma unroll
+        for (int i = 0; i < V; ++i) {
+          float v = xf[r + 4][i];
+          if (n < 4) v = n == 3 ? xf[r + 3][i] : (n == 2 ? xf[r + 2][i] : xf[r + 1][i]);
+          win[r][i] = v;
+        }
       t += n;
     }
     if (t >= bnd) return;

@@ -4,9 +4,12 @@
 // "Ops", GatedRMSNorm (the gate before the norm, the RMS per group of d_inner/groups
 // columns).
 //
-// Mapping: one wavefront per (row, group).  Each lane holds up to kMaxVec 16-byte
-// vectors of x and z in registers (the group is read once and written once: a
-// streaming HBM-bound kernel), the sum of squares is a wave reduction.
+// Mapping (row kernel): one wavefront per row, the row held in registers (read once,
+// written once: a streaming HBM-bound kernel).  Each group owns a contiguous run of
+// L = 64 / groups lanes, and its 16-byte vectors are dealt to those lanes round robin,
+// so every load instruction touches whole 128-byte lines and the group's sum of squares
+// is an xor-shuffle over L lanes.  Shapes that do not fit (groups not dividing 64, rows
+// not a multiple of 64 vectors) use the unit kernel: one wavefront per (row, group).
 #include "common.h"
 
 namespace m2 {
@@ -104,14 +107,88 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_wide_kernel(T* __restrict__
   }
 }
 
+template <typename T, int NVPL>
+__global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ dst, const T* __restrict__ x,
+                                                                const T* __restrict__ z,
+                                                                const float* __restrict__ w, int lanes_per_group,
+                                                                int log2_lpg, float eps, float inv_gs, int rows,
+                                                                int Di) {
+  constexpr int V = Act<T>::kVec;
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  if (row >= rows) return;
+  const int q = lane >> log2_lpg;                 // this lane's group
+  const int jl = lane & (lanes_per_group - 1);    // its place in the group's lanes
+  const int gv = NVPL * lanes_per_group;          // vectors per group
+  const size_t base = (size_t)row * Di;
+  float g[NVPL][V];
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < NVPL; ++k) {
+    const int vi = q * gv + jl + lanes_per_group * k;
+    float xf[V], zf[V];
+    Act<T>::unpack(*reinterpret_cast<const uint4*>(x + base + (size_t)vi * V), xf);
+    Act<T>::unpack(*reinterpret_cast<const uint4*>(z + base + (size_t)vi * V), zf);
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      g[k][i] = xf[i] * silu_f32(zf[i]);
+      ss = fmaf(g[k][i], g[k][i], ss);
+    }
+  }
+  for (int o = lanes_per_group >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  const float inv = rsqrtf(ss * inv_gs + eps);
+#pragma unroll
+  for (int k = 0; k < NVPL; ++k) {
+    const int vi = q * gv + jl + lanes_per_group * k;
+    const float4* wp = reinterpret_cast<const float4*>(w + (size_t)vi * V);
+    float wf[V];
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+      const float4 t4 = wp[i];
+      wf[4 * i] = t4.x;
+      wf[4 * i + 1] = t4.y;
+      wf[4 * i + 2] = t4.z;
+      wf[4 * i + 3] = t4.w;
+    }
+    float out[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) out[i] = g[k][i] * inv * wf[i];
+    *reinterpret_cast<uint4*>(dst + base + (size_t)vi * V) = Act<T>::pack(out);
+  }
+}
+
+template <typename T, int NVPL>
+hipError_t launch_row(void* dst, const void* x, const void* z, const float* w, int32_t groups, float eps,
+                      int32_t rows, int32_t Di, hipStream_t st) {
+  const int lpg = 64 / groups;
+  int log2_lpg = 0;
+  while ((1 << log2_lpg) < lpg) ++log2_lpg;
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  M2_LAUNCH("gated_rmsnorm", (gated_rmsnorm_row_kernel<T, NVPL>), grid, dim3(256), 0, st, (T*)dst, (const T*)x,
+            (const T*)z, w, lpg, log2_lpg, eps, 1.f / (float)(Di / groups), rows, Di);
+  return hipSuccess;
+}
+
 template <typename T>
 hipError_t launch_t(void* dst, const void* x, const void* z, const float* w, int32_t groups,
                     float eps, int32_t rows, int32_t Di, hipStream_t st) {
   constexpr int V = Act<T>::kVec;
+  const int nv_row = Di / V;
+  if (64 % groups == 0 && nv_row % 64 == 0) {
+    switch (nv_row / 64) {
+      case 1: return launch_row<T, 1>(dst, x, z, w, groups, eps, rows, Di, st);
+      case 2: return launch_row<T, 2>(dst, x, z, w, groups, eps, rows, Di, st);
+      case 3: return launch_row<T, 3>(dst, x, z, w, groups, eps, rows, Di, st);
+      case 4: return launch_row<T, 4>(dst, x, z, w, groups, eps, rows, Di, st);
+      case 6: return launch_row<T, 6>(dst, x, z, w, groups, eps, rows, Di, st);
+      case 8: return launch_row<T, 8>(dst, x, z, w, groups, eps, rows, Di, st);
+      default: break;
+    }
+  }
   const int64_t units = (int64_t)rows * groups;
   const dim3 grid((unsigned)((units + 3) / 4));
   if ((Di / groups) / V <= 64 * kMaxVec) {
-    M2_LAUNCH("gated_rmsnorm", gated_rmsnorm_kernel<T>, grid, dim3(256), 0, st, (T*)dst,
+    M2_LAUNCH("gated_rmsnorm_unit", gated_rmsnorm_kernel<T>, grid, dim3(256), 0, st, (T*)dst,
               (const T*)x, (const T*)z, w, groups, eps, rows, Di);
   } else {
     M2_LAUNCH("gated_rmsnorm_wide", gated_rmsnorm_wide_kernel<T>, grid, dim3(256), 0, st, (T*)dst,

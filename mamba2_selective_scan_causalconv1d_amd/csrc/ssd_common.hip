@@ -102,11 +102,10 @@ int32_t scan_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims*
     const int q = d->chunk_size < 64 ? d->chunk_size : 64;
     return q < 1 ? 1 : q;
   }
-  // MFMA path: 64-row chunks; a segment is a run of chunks walked by one workgroup
-  // (two heads each).  Aim at ~768 workgroups (three per CU), 64..4096 rows each.
-  const int64_t hblocks = (d->nheads + 1) / 2;
-  const int64_t work = (int64_t)rb->num_rows * hblocks;
-  int64_t L = (work + 767) / 768;
+  // MFMA path: 64-row chunks; a segment is a run of chunks walked by one workgroup per
+  // head.  Aim at ~1536 workgroups (three rounds of two per CU), 64..4096 rows each.
+  const int64_t work = (int64_t)rb->num_rows * d->nheads;
+  int64_t L = (work + 1535) / 1536;
   L = (L + 63) / 64 * 64;
   if (L < 64) L = 64;
   if (L > 4096) L = 4096;
