@@ -94,6 +94,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 }  // namespace
 
 bool scan_mfma_supported(const mamba2_dims* d);
+int32_t scan_mfma_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims* d);
 
 bool scan_uses_mfma(const mamba2_dims* d) { return scan_mfma_supported(d); }
 
@@ -102,14 +103,7 @@ int32_t scan_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims*
     const int q = d->chunk_size < 64 ? d->chunk_size : 64;
     return q < 1 ? 1 : q;
   }
-  // MFMA path: 64-row chunks; a segment is a run of chunks walked by one workgroup per
-  // head.  Aim at ~1536 workgroups (three rounds of two per CU), 64..4096 rows each.
-  const int64_t work = (int64_t)rb->num_rows * d->nheads;
-  int64_t L = (work + 1535) / 1536;
-  L = (L + 63) / 64 * 64;
-  if (L < 64) L = 64;
-  if (L > 4096) L = 4096;
-  return (int32_t)L;
+  return scan_mfma_segment_length(rb, d);
 }
 
 ScanLayout scan_layout(const mamba2_recurrent_batch* rb, const mamba2_dims* d, int32_t seg_len) {

@@ -2,33 +2,38 @@
 //
 // The recurrence ("feat(backend): Mamba2 ops, with CPU reference implementations",
 // section "Ops", SSMScan) summed in closed form over chunks of 64 rows ("Granite Mamba2
-// Inference Optimization": long prefill as a chunked parallel scan).  Per chunk, with
-// a_t = -exp(A_log) dt'_t and cs_i = sum_{t<=i} a_t inside the chunk, for every head:
-//   y_i   = sum_{j<=i} (C_i . B_j) exp(cs_i - cs_j) dt'_j x_j + exp(cs_i) C_i . S + D x_i
-//   S'    = exp(cs_63) S + sum_j exp(cs_63 - cs_j) dt'_j x_j (x) B_j
-// with S the state entering the chunk.  The contractions run on v_mfma_f32_16x16x32_bf16
-// (fp32 accumulate):
-//   G^T = B C^T        (64 x 64, K = N = 128)
-//   Y^T = S C^T (scaled by exp(cs_i)) + X^T M^T   with M = G o decay mask o dt' taken
-//                      straight from the G^T accumulators (their lane layout is the MFMA
-//                      B-operand layout, the K index permuted consistently on both
-//                      operands)
-//   S^T = exp(cs_63) S^T + B^T (w o X),  w_j = exp(cs_63 - cs_j) dt'_j.
-// x, B and C are exact in bf16.  M, S and w o X are fp32 values split into bf16 hi + lo
-// halves (two MFMAs each): y sums terms that cancel, so one bf16 rounding of M or of a
-// large, slowly decaying S moves outputs past the bf16 output bar, and the fp32 state
-// needs ~16 bits per step.
+// Inference Optimization": long prefill as a chunked parallel scan).  Per chunk and head,
+// with a_t = -exp(A_log) dt'_t, cs_i = sum_{t<=i} a_t inside the chunk, G = C B^T and S
+// the state entering the chunk:
+//   y_i  = exp(cs_i) C_i . S + sum_{j<=i} G_ij exp(cs_i - cs_j) dt'_j x_j + D x_i
+//   S'   = exp(cs_63) S + sum_j exp(cs_63 - cs_j) dt'_j x_j (x) B_j
 //
-// Two kernels walk a segment (a run of chunks of one sequence) per workgroup of 4 waves:
-//   ssd_state: the segment's local end state (from zero), two heads per workgroup;
-//   ssd_scan:  y for one head from the state entering the segment (which the pass kernel
-//              supplies), and the final state for a sequence's last segment.
-// Wave w owns output rows 16w..16w+15 of a chunk and state rows n in [32w, 32w+32); the
-// state stays in MFMA accumulator registers across the segment.  The global loads of chunk
-// q+1 (B rows, x, C rows, dt) are issued into registers while chunk q computes.  LDS tiles
-// are XOR-swizzled in 16-byte units so that 16 lanes reading 16 rows of one column block
-// hit distinct banks; chunk rows are read and written through buffer resources (a
-// wave-uniform base and 32-bit lane offsets).
+// Two rewritings keep the element-wise work small:
+//  * State frame.  The state is carried as S = lam * Sh.  The chunk decay then folds into
+//    per-row weights (y's row scale exp(cs_i) lam, the update weights
+//    exp(cs_63 - cs_j) dt'_j / lam'), and Sh is only rescaled when lam' = lam exp(cs_63)
+//    drops below 2^-20 (then Sh <- lam' Sh, lam' <- 1).
+//  * Factored intra-chunk weights.  While the chunk's log-decay span -cs_63 is at most 40,
+//    exp(cs_i - cs_j) = exp(cs_i) exp(-cs_j): y_i = exp(cs_i) lam [C_i . Sh + sum_j G_ij
+//    f_j x_j] with f_j = exp(-cs_j) dt'_j / lam, so the masked matrix M = G o f needs one
+//    multiply per element.  Wider spans use exp(cs_i - cs_j) per element.
+//
+// Contractions run on v_mfma_f32_16x16x32_bf16 (fp32 accumulate).  x, B and C are exact in
+// bf16; M, Sh and w o x are fp32 values split into bf16 hi + lo halves (two MFMAs each): y
+// sums terms that cancel and the fp32 state needs ~16 bits per step.
+//
+// Mapping.  A workgroup walks one segment (a run of chunks of one sequence) for HB heads of
+// one group with 2 HB waves; wave (head hh, half ph) owns state rows p in [32 ph, 32 ph + 32)
+// of its head (all n) and the matching 32 columns of y.  The state lives in MFMA accumulators
+// as S^T tiles (n x p) whose lane layout is the A-operand layout of S C^T, so the state never
+// goes through LDS.  G^T = B C^T is computed once per chunk for all HB heads (one 16 x 16 tile
+// per wave, plus the last two tiles per head), scaled per head into M^T and shared through
+// LDS in operand order.  Chunk rows of B, C and x are copied global -> LDS by buffer loads
+// that write LDS directly (B and C double-buffered), XOR-swizzled in 16-byte units; the
+// transposed operands (x^T, B^T) come from the gfx950 transposing LDS read.  Every
+// contraction over chunk rows (j) and state columns (n) uses the same permuted k order
+// within a 32-wide k block: slot s of lane group g is index 16 (s / 4) + 4 g + s % 4, the
+// row order of two stacked 16 x 16 accumulator tiles.
 #include "common.h"
 
 namespace m2 {
@@ -39,89 +44,129 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+#define M2_LDS __attribute__((address_space(3)))
 
 constexpr int kP = 64;   // head dim
 constexpr int kN = 128;  // state dim
 constexpr int kQ = 64;   // chunk rows
+constexpr float kSpanMax = 40.f;       // largest log-decay span with factored weights
+constexpr float kFrameMin = 0x1p-20f;  // smallest state-frame scale before a rescale
+constexpr int kTiles = 10;             // lower-triangular 16 x 16 tiles of a 64 x 64 chunk
 
-// Swizzled element offsets (16-byte units of 8 bf16 XOR-permuted per row).
-__device__ __forceinline__ int off_pj(int p, int j) {  // [64][64] tiles indexed [p][j]
-  return p * kQ + ((((j >> 3) ^ (p >> 1)) & 7) << 3) + (j & 7);
-}
-__device__ __forceinline__ int off_pn(int p, int n) {  // [64][128] S tiles [p][n]
-  return p * kN + ((((n >> 3) ^ p) & 15) << 3) + (n & 7);
-}
-__device__ __forceinline__ int off_jn(int j, int n) {  // [64][128] B rows [j][n]
-  return j * kN + ((((n >> 3) ^ j) & 15) << 3) + (n & 7);
-}
-
+// Per-chunk decay quantities of one head (written by one wave, read by all).
 struct Decay {
-  float cs[kQ];   // cs_i
-  float dtp[kQ];  // dt'_j
-  float W[kQ];    // exp(cs_63 - cs_j) dt'_j, from suffix sums
-  float dch;      // exp(cs_63)
-  float lsum;     // sum of a over the segment so far
-  float pad[2];
+  float e[kQ];     // exp(cs_i) lam
+  float f[kQ];     // factored: exp(-cs_j) dt'_j / lam; exact: dt'_j
+  float cs[kQ];    // cs_i
+  float w[kQ];     // exp(cs_63 - cs_j) dt'_j / lam'
+  float scale;     // state rescale before this chunk's update (1: none)
+  int exact;       // 1: per-element exp(cs_i - cs_j)
+  float lam_next;  // lam'
+  float pad;
 };
 
-struct SmemScan {
-  bf16_t B[kQ * kN];    // B rows [j][n]
-  bf16_t XT[kP * kQ];   // X^T [p][j]
-  bf16_t WXh[kP * kQ];  // (w o X)^T hi [p][j]
-  bf16_t WXl[kP * kQ];  // (w o X)^T lo
-  bf16_t Sh[kP * kN];   // S hi [p][n]
-  bf16_t Sl[kP * kN];   // S lo
-  Decay d;
+struct SegPtrs {
+  const int2* seq_info;
+  const int4* seg_info;
+  float* seg_decay;
+  float* seg_state;
 };
 
-struct SmemState {
-  bf16_t B[kQ * kN];
-  bf16_t WXh[2][kP * kQ];
-  bf16_t WXl[2][kP * kQ];
-  Decay d[2];
-};
+// ------------------------------------------------------------------ small helpers
 
-__device__ __forceinline__ f32x4 mfma(const bf16x8& a, const bf16x8& b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                  c, 0, 0, 0);
 }
-
 __device__ __forceinline__ uint32_t pk(float lo, float hi) {
   bf16x2 v = {(__bf16)lo, (__bf16)hi};
   return __builtin_bit_cast(uint32_t, v);
 }
-
 __device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-__device__ __forceinline__ float bf_round(float v) { return (float)(__bf16)v; }
-
-__device__ __forceinline__ bf16x8 as_bf8(const u32x4& v) { return __builtin_bit_cast(bf16x8, v); }
-
-// Buffer resources over the rows of one chunk: a wave-uniform base and a byte range, so
-// every access is a 32-bit lane offset, and offsets at or past the range (the rows after
-// the segment's last row) read as zero and drop writes.
-typedef __amdgpu_buffer_rsrc_t Rsrc;
-__device__ __forceinline__ Rsrc rows_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
-}
-__device__ __forceinline__ u32x4 bld16(Rsrc r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
-__device__ __forceinline__ u32x2 bld8(Rsrc r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
-}
-__device__ __forceinline__ void bst8(Rsrc r, uint32_t off, u32x2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
-}
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniformf(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
+// Split 4 fp32 values into packed bf16 hi (x, y) and lo (z, w) halves.
+__device__ __forceinline__ u32x4 split4(float v0, float v1, float v2, float v3) {
+  const uint32_t h01 = pk(v0, v1), h23 = pk(v2, v3);
+  return u32x4{h01, h23, pk(v0 - lo_f(h01), v1 - hi_f(h01)), pk(v2 - lo_f(h23), v3 - hi_f(h23))};
+}
+
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+// Buffer resource over `bytes` bytes from `base`: lane offsets (voffset) at or past the end
+// read as zero and drop writes.  The uniform soffset adds to the address, not to the range.
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  const int n = bytes <= 0 ? 0 : (int)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+__device__ __forceinline__ void bst8(Rsrc r, uint32_t voff, uint32_t soff, u32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
+}
+// 16 bytes per lane from the buffer into LDS at lds + 16 * lane (lds wave-uniform).
+__device__ __forceinline__ void dma16(Rsrc r, const bf16_t* lds, uint32_t voff, uint32_t soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (M2_LDS void*)lds, 16, voff, soff, 0, 0);
+}
+
+// XOR swizzle of 16-byte units within a tile row: four consecutive rows (transposing
+// reads) and eight consecutive rows (row reads) land on distinct bank groups.  It depends
+// on row % 8 only, and every access below keeps the XOR inside per-lane bits so that the
+// loop indices stay additive (immediate offsets on a few per-lane bases).
+__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
 
 template <typename T>
-__device__ __forceinline__ u32x4 ld16(const T* p) { return *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ u32x4 lds16(const T* p) { return *reinterpret_cast<const u32x4*>(p); }
 template <typename T>
-__device__ __forceinline__ u32x2 ld8(const T* p) { return *reinterpret_cast<const u32x2*>(p); }
-template <typename T>
-__device__ __forceinline__ void st8(T* p, u32x2 v) { *reinterpret_cast<u32x2*>(p) = v; }
-template <typename T>
-__device__ __forceinline__ void st16(T* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+__device__ __forceinline__ u32x2 lds8(const T* p) { return *reinterpret_cast<const u32x2*>(p); }
+
+// Transposing read: within each 16-lane group, lane c receives column c of the four rows
+// whose 8-byte pieces the group's lanes address (lane l: row (l % 16) / 4, columns 4 (l % 4)).
+__device__ __forceinline__ u32x2 tr8(const bf16_t* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((M2_LDS i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+
+// Per-lane element offsets into the swizzled tiles (B and C: [64][128], x: [64][64]).
+// Lane (c, g) = (lane % 16, lane / 16); q = (lane % 16) / 4, b = (lane % 4) / 2.
+struct Lofs {
+  int gt[2];     // B / C row 16 jb + c, elements 32 kk + 8 g..: + 16 jb*128 + 64 (kk/2), [kk%2]
+  int cf[2][2];  // C row 16 ib + c, elements 32 kk + 16 h + 4 g..: + 16 ib*128 + 64 (kk/2), [kk%2][h]
+  int bt[4];     // B^T transposing read for column block nb: + row0*128 + 64 (nb/4), [nb%4]
+  int xt[2];     // x^T transposing read for p block 32 ph + 16 t: + row0*64, [t]
+  int xd[2];     // x row 16 ib + c, elements 32 ph + 16 t + 4 g..: + 16 ib*64, [t]
+};
+__device__ __forceinline__ Lofs lane_offsets(int lane, int ph) {
+  const int g = lane >> 4, c = lane & 15, q = (lane & 15) >> 2, b = (lane & 3) >> 1, e = 4 * (lane & 1);
+  const int sc = swz(c), sq = swz(4 * g + q);
+  Lofs o;
+#pragma unroll
+  for (int a = 0; a < 2; ++a) {
+    o.gt[a] = c * kN + (((4 * a + g) ^ sc) << 3);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) o.cf[a][h] = c * kN + (((4 * a + 2 * h + (g >> 1)) ^ sc) << 3) + 4 * (g & 1);
+  }
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) o.bt[nb] = (4 * g + q) * kN + (((2 * nb + b) ^ sq) << 3) + e;
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    o.xt[t] = (4 * g + q) * kP + (((4 * ph + 2 * t + b) ^ sq) << 3) + e;
+    o.xd[t] = c * kP + (((4 * ph + 2 * t + (g >> 1)) ^ sc) << 3) + 4 * (g & 1);
+  }
+  return o;
+}
+
+// Operand whose lane (c, g) holds T[j][col c] for the 8 k slots j of block m (T row-major,
+// k = row index); `base` is the tile plus the lane's transposing-read offset.
+template <int W>
+__device__ __forceinline__ u32x4 tr_frag(const bf16_t* base, int m) {
+  const u32x2 a = tr8(base + 32 * m * W);
+  const u32x2 b = tr8(base + (32 * m + 16) * W);
+  return u32x4{a.x, a.y, b.x, b.y};
+}
 
 __device__ __forceinline__ float wave_scan_incl(float v, int lane) {
 #pragma unroll
@@ -132,395 +177,484 @@ __device__ __forceinline__ float wave_scan_incl(float v, int lane) {
   return v;
 }
 
-__device__ __forceinline__ float wave_rscan_incl(float v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_down(v, o, 64);
-    if (lane + o < 64) v += t;
-  }
-  return v;
+__device__ __forceinline__ constexpr int tile_index(int jb, int ib) { return ib * (ib + 1) / 2 + jb; }
+
+// Workgroup b runs on XCD b % 8; give each XCD a contiguous range of work items so the
+// head groups of one segment share that XCD's L2.
+__device__ __forceinline__ int work_item(int b, int n) {
+  const int x = b & 7;
+  return x * (n >> 3) + min(x, n & 7) + (b >> 3);
 }
 
-struct SegPtrs {
-  const int2* seq_info;
-  const int4* seg_info;
-  float* seg_decay;
-  float* seg_state;
-};
+// ------------------------------------------------------------------ per-chunk pieces
 
-// ------------------------------------------------------------ per-chunk loads (registers)
-
-// B rows of a chunk: thread t holds 16-byte units u = t + 256k (row u / 16, columns 8 (u % 16)).
-struct PfB {
-  u32x4 v[4];
-};
-__device__ __forceinline__ void load_b(PfB& p, Rsrc rows, uint32_t ld, uint32_t col) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const uint32_t u = threadIdx.x + 256u * k;
-    p.v[k] = bld16(rows, 2u * ((u >> 4) * ld + col + (u & 15u) * 8u));
-  }
-}
-__device__ __forceinline__ void store_b(bf16_t* sB, const PfB& p) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int u = (int)threadIdx.x + 256 * k;
-    st16(sB + off_jn(u >> 4, (u & 15) * 8), p.v[k]);
-  }
-}
-
-// x of one head: thread t holds rows 4jq..4jq+3 (jq = t / 16), columns 4pq..4pq+3 (pq = t % 16).
-struct PfX {
-  u32x2 v[4];
-};
-__device__ __forceinline__ void load_x(PfX& p, Rsrc rows, uint32_t ld, uint32_t col) {
-  const uint32_t jq = threadIdx.x >> 4, pq = threadIdx.x & 15;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) p.v[i] = bld8(rows, 2u * ((4u * jq + i) * ld + col + 4u * pq));
-}
-
-// X^T (optional) and (w o X)^T hi/lo from the registers: a 4 x 4 transpose per thread.
-template <bool kWithX>
-__device__ __forceinline__ void store_x(bf16_t* XT, bf16_t* WXh, bf16_t* WXl, const PfX& px, const float* W) {
-  const int jq = threadIdx.x >> 4, pq = threadIdx.x & 15;
-  const f32x4 w = *reinterpret_cast<const f32x4*>(&W[4 * jq]);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const int p = 4 * pq + e;
-    float xf[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t dd = px.v[i][e >> 1];
-      xf[i] = (e & 1) ? hi_f(dd) : lo_f(dd);
-    }
-    if constexpr (kWithX) st8(&XT[off_pj(p, 4 * jq)], u32x2{pk(xf[0], xf[1]), pk(xf[2], xf[3])});
-    float hi[4], lo[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float wx = w[i] * xf[i];
-      hi[i] = bf_round(wx);
-      lo[i] = wx - hi[i];
-    }
-    st8(&WXh[off_pj(p, 4 * jq)], u32x2{pk(hi[0], hi[1]), pk(hi[2], hi[3])});
-    st8(&WXl[off_pj(p, 4 * jq)], u32x2{pk(lo[0], lo[1]), pk(lo[2], lo[3])});
-  }
-}
-
-// dt' and the decay sums of one head for the chunk (one wave: lane = row; v = dt, raw).
-__device__ __forceinline__ void chunk_decay(Decay& d, float v, float A, float bias, int nr, int lane) {
+// Decay quantities of one head for a chunk (one wave; lane = chunk row, v = raw dt).
+// lam is the frame scale entering the chunk; it and lsum (sum of chunk log-decays) advance.
+__device__ __forceinline__ void chunk_decay(Decay& d, float v, float A, float bias, int nr, int lane,
+                                            float& lam, float& lsum) {
   const float dtp = lane < nr ? softplus_f32(v + bias) : 0.f;
-  const float a = -A * dtp;
-  const float cs = wave_scan_incl(a, lane);
-  const float rs = wave_rscan_incl(a, lane);  // sum_{t >= lane} a_t
-  float suf = __shfl_down(rs, 1, 64);         // sum_{t > lane} a_t
-  if (lane == 63) suf = 0.f;
+  const float cs = wave_scan_incl(-A * dtp, lane);
+  const float cend = uniformf(__shfl(cs, 63, 64));
+  const bool exact = -cend > kSpanMax;
+  const float tent = lam * __expf(cend);
+  const bool reset = tent < kFrameMin;
+  const float lam_next = reset ? 1.f : tent;
+  d.e[lane] = __expf(cs) * lam;
+  d.f[lane] = exact ? dtp : __expf(-cs) * dtp * (1.f / lam);
   d.cs[lane] = cs;
-  d.dtp[lane] = dtp;
-  d.W[lane] = __expf(suf) * dtp;
-  if (lane == 63) {
-    d.dch = __expf(cs);
-    d.lsum += cs;
+  d.w[lane] = __expf(cend - cs) * dtp * (1.f / lam_next);
+  if (lane == 0) {
+    d.scale = reset ? tent : 1.f;
+    d.exact = exact ? 1 : 0;
+    d.lam_next = lam_next;
   }
+  lam = lam_next;
+  lsum += cend;
 }
 
-// B^T operands of wave w: rows n = 32w + 16nb + c, k = j = 32m + 8g + s (from the LDS B rows).
-__device__ __forceinline__ void load_bt_ops(const bf16_t* sB, u32x4 (&bt)[2][2], int w, int lane) {
-  const int g = lane >> 4, c = lane & 15;
+// Per-lane byte offsets of the global -> LDS copies (see load_chunk).
+struct DmaOfs {
+  uint32_t bc[2];  // B / C block rows, [k % 2]
+  uint32_t x;      // x block rows
+};
+__device__ __forceinline__ DmaOfs dma_offsets(int lane, uint32_t ld) {
+  DmaOfs o;
+  const int r = lane >> 4;
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int n = 32 * w + 16 * nb + c;
+  for (int a = 0; a < 2; ++a) {
+    const int u = (lane & 15) ^ ((2 * r) | a);  // swz(4 k + r) = 2 r | (k % 2)
+    o.bc[a] = 2u * ((uint32_t)r * ld + 8u * (uint32_t)u);
+  }
+  const int rx = lane >> 3;
+  o.x = 2u * ((uint32_t)rx * ld + 8u * (uint32_t)((lane & 7) ^ swz(rx)));
+  return o;
+}
+
+// Copy chunk rows [r0, r0 + nr) of B (and C) [64][128] and the x of HB heads [64][64] into
+// LDS.  Each instruction fills 1 KB of a tile (4 rows of B or C, 8 rows of x), each lane
+// fetching the global 16-byte unit that the swizzle places at its LDS slot; rows past nr
+// read as zero.  The 16 + 16 + 8 HB instructions are dealt round robin to the 2 HB waves.
+template <int HB, bool kWithC>
+__device__ __forceinline__ void load_chunk(const bf16_t* rows, int nr, uint32_t ld, uint32_t colB, uint32_t colC,
+                                           uint32_t colX, bf16_t* sB, bf16_t* sC, bf16_t (*sX)[kQ * kP],
+                                           const DmaOfs& o, int w) {
+  constexpr int nW = 2 * HB;
+  constexpr int nBC = kWithC ? 32 : 16;
+  constexpr int nAll = nBC + 8 * HB;
+  static_assert(nAll % nW == 0 && 16 % nW == 0, "instruction split");
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      uint32_t e[8];
-#pragma unroll
-      for (int k = 0; k < 8; ++k) e[k] = sB[off_jn(32 * m + 8 * g + k, n)];
-      bt[nb][m] = u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+  for (int i = 0; i < nAll / nW; ++i) {
+    const int t = w + nW * i;  // wave-uniform; t < 16, < nBC per i at compile time
+    if (nW * i < nBC) {
+      const int k = t & 15;
+      const Rsrc r = make_rsrc(rows + (size_t)(4 * k) * ld, ((int64_t)nr - 4 * k) * ld * 2);
+      const bool isB = nW * i < 16;
+      dma16(r, (isB ? sB : sC) + 512 * k, o.bc[k & 1], 2u * (isB ? colB : colC));
+    } else {
+      const int hh = (t - nBC) >> 3, k = (t - nBC) & 7;
+      const Rsrc r = make_rsrc(rows + (size_t)(8 * k) * ld, ((int64_t)nr - 8 * k) * ld * 2);
+      dma16(r, sX[hh] + 512 * k, o.x, 2u * (colX + (uint32_t)(hh * kP)));
     }
   }
 }
 
-// S^T (8 tiles of wave w) <- dch S^T + B^T (w o X), the operand in hi and lo halves.
-__device__ __forceinline__ void state_update(const bf16_t* sB, const bf16_t* WXh, const bf16_t* WXl,
-                                             f32x4 (&S)[8], float d, int w, int lane) {
-  const int g = lane >> 4, c = lane & 15;
-  u32x4 bt[2][2];
-  load_bt_ops(sB, bt, w, lane);
+// w o x operands (hi, lo) of k block m from the x^T operand of the same block.
+__device__ __forceinline__ void wx_frag(const u32x4& xt, const Decay& d, int m, int lane, u32x4& hi, u32x4& lo) {
+  const int g = lane >> 4;
+  const f32x4 w0 = *reinterpret_cast<const f32x4*>(&d.w[32 * m + 4 * g]);
+  const f32x4 w1 = *reinterpret_cast<const f32x4*>(&d.w[32 * m + 16 + 4 * g]);
+  const u32x4 a = split4(w0[0] * lo_f(xt[0]), w0[1] * hi_f(xt[0]), w0[2] * lo_f(xt[1]), w0[3] * hi_f(xt[1]));
+  const u32x4 b = split4(w1[0] * lo_f(xt[2]), w1[1] * hi_f(xt[2]), w1[2] * lo_f(xt[3]), w1[3] * hi_f(xt[3]));
+  hi = u32x4{a[0], a[1], b[0], b[1]};
+  lo = u32x4{a[2], a[3], b[2], b[3]};
+}
+
+// S^T(nb, pb) += B^T (w o x) for the wave's two p blocks; xt[t][m] are the x^T operands.
+__device__ __forceinline__ void state_update(f32x4 (&S)[2][8], const u32x4 (&xt)[2][2], const bf16_t* sB,
+                                             const Lofs& lo, const Decay& d, int lane) {
+  u32x4 wh[2][2], wl[2][2];
 #pragma unroll
-  for (int t = 0; t < 8; ++t) S[t] *= d;
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-  for (int pb = 0; pb < 4; ++pb) {
-    const int p = 16 * pb + c;
+    for (int m = 0; m < 2; ++m) wx_frag(xt[t][m], d, m, lane, wh[t][m], wl[t][m]);
+  const float scale = uniformf(d.scale);
+  if (scale != 1.f) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) S[t][nb] *= scale;
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const int off = off_pj(p, 32 * m + 8 * g);
-      const bf16x8 bh = as_bf8(ld16(&WXh[off]));
-      const bf16x8 bl = as_bf8(ld16(&WXl[off]));
+      const u32x4 bt = tr_frag<kN>(sB + lo.bt[nb & 3] + 64 * (nb >> 2), m);
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const bf16x8 a = as_bf8(bt[nb][m]);
-        S[4 * nb + pb] = mfma(a, bh, S[4 * nb + pb]);
-        S[4 * nb + pb] = mfma(a, bl, S[4 * nb + pb]);
+      for (int t = 0; t < 2; ++t) {
+        S[t][nb] = mfma(bt, wh[t][m], S[t][nb]);
+        S[t][nb] = mfma(bt, wl[t][m], S[t][nb]);
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// State tile t of wave w holds S[p][n..n+3], p = 16 (t % 4) + c, n = 32w + 16 (t / 4) + 4g.
-__device__ __forceinline__ size_t state_elem(int t, int w, int lane) {
+// State tile (nb, t) of wave half ph: S[p][n..n+3], p = 32 ph + 16 t + c, n = 16 nb + 4 g.
+__device__ __forceinline__ size_t state_elem(int ph, int t, int nb, int lane) {
   const int g = lane >> 4, c = lane & 15;
-  return (size_t)(16 * (t & 3) + c) * kN + 32 * w + 16 * (t >> 2) + 4 * g;
+  return (size_t)(32 * ph + 16 * t + c) * kN + 16 * nb + 4 * g;
 }
 
 // ---------------------------------------------------------------- segment states
 
-__global__ __launch_bounds__(256, 2) void ssd_mfma_state_kernel(const bf16_t* __restrict__ xbc,
+template <int HB>
+__global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __restrict__ xbc,
                                                                 const bf16_t* __restrict__ dt,
                                                                 const float* __restrict__ a_log,
-                                                                const float* __restrict__ dt_bias,
-                                                                SegPtrs sp, int H, int G) {
-  __shared__ SmemState sm;
-  const int nhb = H >> 1;
-  const int seg = blockIdx.x / nhb;
-  const int h0 = (blockIdx.x % nhb) * 2;
+                                                                const float* __restrict__ dt_bias, SegPtrs sp,
+                                                                int H, int G, int nitems) {
+  __shared__ __attribute__((aligned(16))) bf16_t sB0[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sB1[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sX0[HB][kQ * kP];
+  __shared__ __attribute__((aligned(16))) bf16_t sX1[HB][kQ * kP];
+  __shared__ __attribute__((aligned(16))) Decay sD[2][HB];
+
+  const int nhg = H / HB;
+  const int item = work_item(blockIdx.x, nitems);
+  const int seg = item / nhg, h0 = (item % nhg) * HB;
   const int4 si0 = sp.seg_info[seg];
   const int4 si = make_int4(uniform(si0.x), uniform(si0.y), uniform(si0.z), uniform(si0.w));
-  const int nseg_seq = uniform(sp.seq_info[si.x].y);
-  if (si.w == nseg_seq - 1) return;  // a sequence's last segment needs no local state
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  if (si.w == uniform(sp.seq_info[si.x].y) - 1) return;  // a sequence's last segment needs no local state
+
+  const int w = uniform((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int hh = w >> 1, ph = w & 1, h = h0 + hh;
   const int Di = H * kP;
   const uint32_t ld = (uint32_t)(Di + 2 * G * kN);
-  const size_t boff = (size_t)Di + (size_t)(h0 / (H / G)) * kN;
-  const float A = w < 2 ? __expf(a_log[h0 + w]) : 0.f;
-  const float bias = w < 2 ? dt_bias[h0 + w] : 0.f;
-  if (tid < 2) sm.d[tid].lsum = 0.f;
+  const int grp = h0 / (H / G);
+  const uint32_t colB = (uint32_t)(Di + grp * kN), colX = (uint32_t)(h0 * kP);
+  const float A = __expf(a_log[h]), bias = dt_bias[h];
+  const int nchunks = (si.z + kQ - 1) / kQ;
+  const Lofs lo = lane_offsets(lane, ph);
+  const DmaOfs dof = dma_offsets(lane, ld);
+
+  auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
+  auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
+  auto dt_of = [&](int q) {
+    const int r0 = si.y + q * kQ;
+    return lane < nr_of(q) ? bf16_to_f32(dt[(size_t)(r0 + lane) * H + h]) : 0.f;
+  };
 
   f32x4 S[2][8];
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh)
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) S[hh][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int nb = 0; nb < 8; ++nb) S[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  PfB pb;
-  PfX px[2];
-  float pdt = 0.f;
-  auto issue = [&](int q) {
-    const int r0 = si.y + q * kQ;
-    const int nr = min(kQ, si.z - q * kQ);
-    const Rsrc rows = rows_rsrc(xbc + (size_t)r0 * ld, (uint32_t)nr * ld * 2u);
-    load_b(pb, rows, ld, (uint32_t)boff);
-    load_x(px[0], rows, ld, (uint32_t)(h0 * kP));
-    load_x(px[1], rows, ld, (uint32_t)((h0 + 1) * kP));
-    if (w < 2 && lane < nr) pdt = bf16_to_f32(dt[(size_t)(r0 + lane) * H + h0 + w]);
+  float lam = 1.f, lsum = 0.f, dtn = 0.f;
+  load_chunk<HB, false>(rows_of(0), nr_of(0), ld, colB, 0, colX, sB0, nullptr, sX0, dof, w);
+  if (ph == 0) chunk_decay(sD[0][hh], dt_of(0), A, bias, nr_of(0), lane, lam, lsum);
+  if (ph == 0 && nchunks > 1) dtn = dt_of(1);
+
+  auto step = [&](int q, bf16_t* sBc, bf16_t (*sXc)[kQ * kP], bf16_t* sBn, bf16_t (*sXn)[kQ * kP], Decay* dc,
+                  Decay* dn) {
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // chunk q rows and decay visible; chunk q-1 done with the other stage
+    float dtn2 = 0.f;
+    if (q + 1 < nchunks) {
+      load_chunk<HB, false>(rows_of(q + 1), nr_of(q + 1), ld, colB, 0, colX, sBn, nullptr, sXn, dof, w);
+      if (ph == 0 && q + 2 < nchunks) dtn2 = dt_of(q + 2);
+    }
+    u32x4 xt[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sXc[hh] + lo.xt[t], m);
+    state_update(S, xt, sBc, lo, dc[hh], lane);
+    if (ph == 0 && q + 1 < nchunks) chunk_decay(dn[hh], dtn, A, bias, nr_of(q + 1), lane, lam, lsum);
+    dtn = dtn2;
   };
 
-  const int nchunks = (si.z + kQ - 1) / kQ;
-  issue(0);
-  for (int q = 0; q < nchunks; ++q) {
-    const int nr = min(kQ, si.z - q * kQ);
-    __syncthreads();  // the previous chunk is done with LDS
-    store_b(sm.B, pb);
-    if (w < 2) chunk_decay(sm.d[w], pdt, A, bias, nr, lane);
-    __syncthreads();
-    store_x<false>(nullptr, sm.WXh[0], sm.WXl[0], px[0], sm.d[0].W);
-    store_x<false>(nullptr, sm.WXh[1], sm.WXl[1], px[1], sm.d[1].W);
-    if (q + 1 < nchunks) issue(q + 1);
-    __syncthreads();
-    state_update(sm.B, sm.WXh[0], sm.WXl[0], S[0], sm.d[0].dch, w, lane);
-    state_update(sm.B, sm.WXh[1], sm.WXl[1], S[1], sm.d[1].dch, w, lane);
+  for (int q = 0; q < nchunks; q += 2) {
+    step(q, sB0, sX0, sB1, sX1, sD[0], sD[1]);
+    if (q + 1 < nchunks) step(q + 1, sB1, sX1, sB0, sX0, sD[1], sD[0]);
   }
+
+  const float lam_end = uniformf(sD[(nchunks - 1) & 1][hh].lam_next);
+  float* out = sp.seg_state + ((size_t)seg * H + h) * (size_t)(kP * kN);
 #pragma unroll
-  for (int hh = 0; hh < 2; ++hh) {
-    float* out = sp.seg_state + ((size_t)seg * H + h0 + hh) * (size_t)(kP * kN);
+  for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(out + state_elem(t, w, lane)) = S[hh][t];
-  }
-  if (tid < 2) sp.seg_decay[(size_t)seg * H + h0 + tid] = __expf(sm.d[tid].lsum);
+    for (int nb = 0; nb < 8; ++nb)
+      *reinterpret_cast<f32x4*>(out + state_elem(ph, t, nb, lane)) = S[t][nb] * lam_end;
+  if (ph == 0 && lane == 0) sp.seg_decay[(size_t)seg * H + h] = __expf(lsum);
 }
 
 // ---------------------------------------------------------------- outputs
 
-__global__ __launch_bounds__(256, 2) void ssd_mfma_scan_kernel(
+template <int HB>
+__global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
     bf16_t* __restrict__ y, const bf16_t* __restrict__ xbc, const bf16_t* __restrict__ dt,
     const float* __restrict__ a_log, const float* __restrict__ dt_bias, const float* __restrict__ Dp,
-    float* __restrict__ pool, const int32_t* __restrict__ slots, SegPtrs sp, int H, int G) {
-  __shared__ SmemScan sm;
-  const int seg = blockIdx.x / H;
-  const int h = blockIdx.x % H;
+    float* __restrict__ pool, const int32_t* __restrict__ slots, SegPtrs sp, int H, int G, int nitems) {
+  __shared__ __attribute__((aligned(16))) bf16_t sB0[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sB1[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sC0[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sC1[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sX[HB][kQ * kP];
+  __shared__ __attribute__((aligned(16))) u32x4 sM[HB][kTiles][64];
+  __shared__ __attribute__((aligned(16))) Decay sD[2][HB];
+
+  const int nhg = H / HB;
+  const int item = work_item(blockIdx.x, nitems);
+  const int seg = item / nhg, h0 = (item % nhg) * HB;
   const int4 si0 = sp.seg_info[seg];
   const int4 si = make_int4(uniform(si0.x), uniform(si0.y), uniform(si0.z), uniform(si0.w));
   const bool last = si.w == uniform(sp.seq_info[si.x].y) - 1;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+
+  const int w = uniform((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
+  const int hh = w >> 1, ph = w & 1, h = h0 + hh;
   const int Di = H * kP;
   const uint32_t ld = (uint32_t)(Di + 2 * G * kN);
-  const int grp = h / (H / G);
-  const size_t boff = (size_t)Di + (size_t)grp * kN;
-  const size_t coff = (size_t)Di + (size_t)G * kN + (size_t)grp * kN;
-  const int irow = 16 * w + c;  // this lane's output row in the chunk
+  const int grp = h0 / (H / G);
+  const uint32_t colB = (uint32_t)(Di + grp * kN), colC = (uint32_t)(Di + (G + grp) * kN);
+  const uint32_t colX = (uint32_t)(h0 * kP);
   const float A = __expf(a_log[h]), bias = dt_bias[h], dh = Dp[h];
-  if (tid == 0) sm.d.lsum = 0.f;
+  const int nchunks = (si.z + kQ - 1) / kQ;
+  const Lofs lo = lane_offsets(lane, ph);
+  const DmaOfs dof = dma_offsets(lane, ld);
+  const uint32_t yvoff = 2u * ((uint32_t)c * (uint32_t)Di + 4u * (uint32_t)g);
 
-  // the state entering the segment (written by the pass kernel)
-  f32x4 S[8];
+  auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
+  auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
+  auto dt_of = [&](int q) {
+    const int r0 = si.y + q * kQ;
+    return lane < nr_of(q) ? bf16_to_f32(dt[(size_t)(r0 + lane) * H + h]) : 0.f;
+  };
+
+  // the state entering the segment (written by the pass kernel), frame scale 1
+  f32x4 S[2][8];
   {
     const float* in = sp.seg_state + ((size_t)seg * H + h) * (size_t)(kP * kN);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) S[t] = *reinterpret_cast<const f32x4*>(in + state_elem(t, w, lane));
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) S[t][nb] = *reinterpret_cast<const f32x4*>(in + state_elem(ph, t, nb, lane));
   }
 
-  PfB pb;
-  PfX px;
-  u32x4 pc[4];
-  float pdt = 0.f;
-  auto issue = [&](int q) {
-    const int r0 = si.y + q * kQ;
-    const int nr = min(kQ, si.z - q * kQ);
-    const Rsrc rows = rows_rsrc(xbc + (size_t)r0 * ld, (uint32_t)nr * ld * 2u);
-    load_b(pb, rows, ld, (uint32_t)boff);
-    load_x(px, rows, ld, (uint32_t)(h * kP));
-    // C rows of this wave's row block: B-operand of G^T and of S C^T (k = n, col = i)
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
-      pc[kk] = bld16(rows, 2u * ((uint32_t)irow * ld + (uint32_t)coff + (uint32_t)(32 * kk + 8 * g)));
-    if (w == 0 && lane < nr) pdt = bf16_to_f32(dt[(size_t)(r0 + lane) * H + h]);
-  };
+  float lam = 1.f, lsum = 0.f, dtn = 0.f;
+  load_chunk<HB, true>(rows_of(0), nr_of(0), ld, colB, colC, colX, sB0, sC0, sX, dof, w);
+  if (ph == 0) chunk_decay(sD[0][hh], dt_of(0), A, bias, nr_of(0), lane, lam, lsum);
+  if (ph == 0 && nchunks > 1) dtn = dt_of(1);
 
-  const int nchunks = (si.z + kQ - 1) / kQ;
-  issue(0);
-  for (int q = 0; q < nchunks; ++q) {
+  auto step = [&](int q, bf16_t* sBc, bf16_t* sCc, bf16_t* sBn, bf16_t* sCn, Decay* dc, Decay* dn) {
     const int r0 = si.y + q * kQ;
-    const int nr = min(kQ, si.z - q * kQ);
-    __syncthreads();  // (1) the previous chunk is done with LDS
-    store_b(sm.B, pb);
-    if (w == 0) chunk_decay(sm.d, pdt, A, bias, nr, lane);
-    u32x4 cr[4];
+    const int nr = nr_of(q);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();  // (1) chunk q rows and decay visible; chunk q-1 done with x and M
+
+    // ---- phase 1: x operands; G^T tiles and M^T for the workgroup's heads ----
+    u32x4 xt[2][2];
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) cr[kk] = pc[kk];
-    __syncthreads();  // (2) B rows and decay sums visible
-    store_x<true>(sm.XT, sm.WXh, sm.WXl, px, sm.d.W);
-    // S [p][n] in bf16 hi + lo halves
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      const int p = 16 * (t & 3) + c;
-      const int n = 32 * w + 16 * (t >> 2) + 4 * g;
-      float lo[4];
+      for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sX[hh] + lo.xt[t], m);
+    u32x2 xd[2][4];  // x[i = 16 ib + c][p = 32 ph + 16 t + 4 g ..+3] for D x
 #pragma unroll
-      for (int r = 0; r < 4; ++r) lo[r] = S[t][r] - bf_round(S[t][r]);
-      st8(&sm.Sh[off_pn(p, n)], u32x2{pk(S[t][0], S[t][1]), pk(S[t][2], S[t][3])});
-      st8(&sm.Sl[off_pn(p, n)], u32x2{pk(lo[0], lo[1]), pk(lo[2], lo[3])});
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) xd[t][ib] = lds8(sX[hh] + lo.xd[t] + 16 * ib * kP);
+
+    auto gt_tile = [&](int jb, int ib) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        acc = mfma(lds16(sBc + lo.gt[kk & 1] + 16 * jb * kN + 64 * (kk >> 1)),
+                   lds16(sCc + lo.gt[kk & 1] + 16 * ib * kN + 64 * (kk >> 1)), acc);
+      return acc;
+    };
+    auto m_tile = [&](const f32x4& gt, int t, int jb, int ib, int head) {
+      const Decay& d = dc[head];
+      const f32x4 fj = *reinterpret_cast<const f32x4*>(&d.f[16 * jb + 4 * g]);
+      float v[4];
+      if (uniform(d.exact)) {
+        const float csi = d.cs[16 * ib + c];
+        const f32x4 csj = *reinterpret_cast<const f32x4*>(&d.cs[16 * jb + 4 * g]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = gt[r] * (__expf(csi - csj[r]) * fj[r]);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = gt[r] * fj[r];
+      }
+      if (jb == ib) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = (4 * g + r > c) ? 0.f : v[r];
+      }
+      sM[head][t][lane] = split4(v[0], v[1], v[2], v[3]);
+    };
+    // tiles 0..7 for every head, one per wave (two per wave with four waves)
+#pragma unroll
+    for (int i = 0; i < 8 / (2 * HB); ++i) {
+      const int t = w + 2 * HB * i;
+      const int ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+      const int jb = t - ib * (ib + 1) / 2;
+      const f32x4 gt = gt_tile(jb, ib);
+#pragma unroll
+      for (int head = 0; head < HB; ++head) m_tile(gt, t, jb, ib, head);
     }
-    // G^T tiles (j block jb, i block w), jb <= w
-    f32x4 Gt[4];
+    // tiles 8 = (2, 3) and 9 = (3, 3) for the wave's own head
+    if (ph == 0) m_tile(gt_tile(2, 3), 8, 2, 3, hh);
+    else m_tile(gt_tile(3, 3), 9, 3, 3, hh);
+    __syncthreads();  // (2) M^T visible; x of chunk q no longer read
+
+    float dtn2 = 0.f;
+    if (q + 1 < nchunks) {
+      load_chunk<HB, true>(rows_of(q + 1), nr_of(q + 1), ld, colB, colC, colX, sBn, sCn, sX, dof, w);
+      if (ph == 0 && q + 2 < nchunks) dtn2 = dt_of(q + 2);
+    }
+
+    // ---- phase 2: Y^T(pb, ib) = S C^T + x^T M^T (row scales), + D x ----
+    const Decay& d = dc[hh];
+    f32x4 Y[2][4];
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-      Gt[jb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (jb <= w) {
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          Gt[jb] = mfma(as_bf8(ld16(&sm.B[off_jn(16 * jb + c, 32 * kk + 8 * g)])), as_bf8(cr[kk]), Gt[jb]);
+      for (int ib = 0; ib < 4; ++ib) Y[t][ib] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      u32x4 sh[2], sl[2];
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const f32x4 a = S[t][2 * kk], b = S[t][2 * kk + 1];
+        const u32x4 s0 = split4(a[0], a[1], a[2], a[3]), s1 = split4(b[0], b[1], b[2], b[3]);
+        sh[t] = u32x4{s0[0], s0[1], s1[0], s1[1]};
+        sl[t] = u32x4{s0[2], s0[3], s1[2], s1[3]};
+      }
+#pragma unroll
+      for (int ib = 0; ib < 4; ++ib) {
+        const bf16_t* cb = sCc + 16 * ib * kN + 64 * (kk >> 1);
+        const u32x2 c0 = lds8(cb + lo.cf[kk & 1][0]);
+        const u32x2 c1 = lds8(cb + lo.cf[kk & 1][1]);
+        const u32x4 cf = u32x4{c0.x, c0.y, c1.x, c1.y};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          Y[t][ib] = mfma(sh[t], cf, Y[t][ib]);
+          Y[t][ib] = mfma(sl[t], cf, Y[t][ib]);
+        }
       }
     }
-    if (q + 1 < nchunks) issue(q + 1);
-    __syncthreads();  // (3) X^T, (w o X)^T and S tiles visible
-
-    // ---- Y^T tiles (p block pb, i block w): exp(cs_i) S C^T + X^T M^T + D x ----
-    const float csi = sm.d.cs[irow];
-    const float ei = __expf(csi);
-    f32x4 yacc[4];
+    const bool exact = uniform(d.exact) != 0;
+    float ei[4];
 #pragma unroll
-    for (int pb4 = 0; pb4 < 4; ++pb4) {
-      yacc[pb4] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int p = 16 * pb4 + c;
+    for (int ib = 0; ib < 4; ++ib) ei[ib] = d.e[16 * ib + c];
+    if (exact) {
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const int off = off_pn(p, 32 * kk + 8 * g);
-        yacc[pb4] = mfma(as_bf8(ld16(&sm.Sh[off])), as_bf8(cr[kk]), yacc[pb4]);
-        yacc[pb4] = mfma(as_bf8(ld16(&sm.Sl[off])), as_bf8(cr[kk]), yacc[pb4]);
-      }
-      yacc[pb4] *= ei;
-      __builtin_amdgcn_sched_barrier(0);
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int ib = 0; ib < 4; ++ib) Y[t][ib] *= ei[ib];
     }
-    // M^T operands, hi and lo: slots 0..3 from G^T tile 2m, slots 4..7 from tile 2m + 1
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      if (m <= (w >> 1)) {
-        float mv[8];
+    for (int ib = 0; ib < 4; ++ib) {
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-          const int jb = 2 * m + half;
-          const int j0 = 16 * jb + 4 * g;
-          const f32x4 csj = *reinterpret_cast<const f32x4*>(&sm.d.cs[j0]);
-          const f32x4 dtj = *reinterpret_cast<const f32x4*>(&sm.d.dtp[j0]);
+      for (int m = 0; m < 2; ++m) {
+        if (m <= (ib >> 1)) {
+          const u32x4 t0 = sM[hh][tile_index(2 * m, ib)][lane];
+          const u32x4 t1 = (2 * m + 1 <= ib) ? sM[hh][tile_index(2 * m + 1, ib)][lane] : u32x4{0u, 0u, 0u, 0u};
+          const u32x4 mh = u32x4{t0[0], t0[1], t1[0], t1[1]};
+          const u32x4 ml = u32x4{t0[2], t0[3], t1[2], t1[3]};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            float v = 0.f;
-            if (jb <= w && j0 + r <= irow) v = Gt[jb][r] * __expf(csi - csj[r]) * dtj[r];
-            mv[4 * half + r] = v;
+          for (int t = 0; t < 2; ++t) {
+            Y[t][ib] = mfma(xt[t][m], mh, Y[t][ib]);
+            Y[t][ib] = mfma(xt[t][m], ml, Y[t][ib]);
           }
         }
-        u32x4 mh, ml;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          mh[k] = pk(mv[2 * k], mv[2 * k + 1]);
-          ml[k] = pk(mv[2 * k] - bf_round(mv[2 * k]), mv[2 * k + 1] - bf_round(mv[2 * k + 1]));
-        }
-#pragma unroll
-        for (int pb4 = 0; pb4 < 4; ++pb4) {
-          const int p = 16 * pb4 + c;
-          const u32x2 x0 = ld8(&sm.XT[off_pj(p, 32 * m + 4 * g)]);
-          const u32x2 x1 = ld8(&sm.XT[off_pj(p, 32 * m + 16 + 4 * g)]);
-          const bf16x8 xo = as_bf8(u32x4{x0.x, x0.y, x1.x, x1.y});
-          yacc[pb4] = mfma(xo, as_bf8(mh), yacc[pb4]);
-          yacc[pb4] = mfma(xo, as_bf8(ml), yacc[pb4]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
       }
     }
-    // + D x and store: lane holds y[i = irow][p = 16pb + 4g + r]; x from X^T
-    {
-      const Rsrc yrows = rows_rsrc(y + (size_t)r0 * Di, (uint32_t)nr * (uint32_t)Di * 2u);
 #pragma unroll
-      for (int pb4 = 0; pb4 < 4; ++pb4) {
-        const int p0 = 16 * pb4 + 4 * g;
-        float o[4];
+    for (int ib = 0; ib < 4; ++ib) {
+      // rows 16 ib.. of the chunk; rows at or past nr are dropped by the range
+      const Rsrc yr = make_rsrc(y + (size_t)(r0 + 16 * ib) * Di, ((int64_t)nr - 16 * ib) * Di * 2);
+      const float sc = exact ? 1.f : ei[ib];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) o[r] = fmaf(dh, bf16_to_f32(sm.XT[off_pj(p0 + r, irow)]), yacc[pb4][r]);
-        bst8(yrows, 2u * ((uint32_t)irow * (uint32_t)Di + (uint32_t)(h * kP + p0)),
-             u32x2{pk(o[0], o[1]), pk(o[2], o[3])});
+      for (int t = 0; t < 2; ++t) {
+        const u32x2 xv = xd[t][ib];
+        const float o0 = fmaf(dh, lo_f(xv.x), Y[t][ib][0] * sc);
+        const float o1 = fmaf(dh, hi_f(xv.x), Y[t][ib][1] * sc);
+        const float o2 = fmaf(dh, lo_f(xv.y), Y[t][ib][2] * sc);
+        const float o3 = fmaf(dh, hi_f(xv.y), Y[t][ib][3] * sc);
+        bst8(yr, yvoff, 2u * (uint32_t)(h * kP + 32 * ph + 16 * t), u32x2{pk(o0, o1), pk(o2, o3)});
       }
     }
+
     // ---- state update ----
-    state_update(sm.B, sm.WXh, sm.WXl, S, sm.d.dch, w, lane);
+    state_update(S, xt, sBc, lo, d, lane);
+    if (ph == 0 && q + 1 < nchunks) chunk_decay(dn[hh], dtn, A, bias, nr_of(q + 1), lane, lam, lsum);
+    dtn = dtn2;
+  };
+
+  for (int q = 0; q < nchunks; q += 2) {
+    step(q, sB0, sC0, sB1, sC1, sD[0], sD[1]);
+    if (q + 1 < nchunks) step(q + 1, sB1, sC1, sB0, sC0, sD[1], sD[0]);
   }
   if (last) {
+    const float lam_end = uniformf(sD[(nchunks - 1) & 1][hh].lam_next);
     float* out = pool + ((size_t)slots[si.x] * H + h) * (size_t)(kP * kN);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) *reinterpret_cast<f32x4*>(out + state_elem(t, w, lane)) = S[t];
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        *reinterpret_cast<f32x4*>(out + state_elem(ph, t, nb, lane)) = S[t][nb] * lam_end;
   }
 }
 
+int heads_per_block(const mamba2_dims& d) { return (d.nheads / d.ngroups) % 4 == 0 ? 4 : 2; }
+
 }  // namespace
 
-// Shapes the MFMA path covers: bf16, P = 64, N = 128, heads in pairs within one group (the
-// state kernel takes two heads per workgroup), and 64-row offsets within 32 bits.
+// Shapes the MFMA path covers: bf16, P = 64, N = 128, an even number of heads per group
+// (a workgroup takes 2 or 4 heads of one group), and chunk-row offsets within 32 bits.
 bool scan_mfma_supported(const mamba2_dims* d) {
   const int64_t Dc = (int64_t)d->nheads * d->headdim + 2 * (int64_t)d->ngroups * d->d_state;
-  return d->act_dtype == MAMBA2_DTYPE_BF16 && d->headdim == kP && d->d_state == kN && d->nheads % 2 == 0 &&
-         (d->nheads / d->ngroups) % 2 == 0 && Dc * kQ < ((int64_t)1 << 31);
+  return d->act_dtype == MAMBA2_DTYPE_BF16 && d->headdim == kP && d->d_state == kN &&
+         (d->nheads / d->ngroups) % 2 == 0 && Dc * kQ * 2 < ((int64_t)1 << 31);
+}
+
+// Segment length for the MFMA path: aim at three workgroups per CU (one resident at a
+// time on each of 256 CUs), 64..4096 rows per segment.
+int32_t scan_mfma_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims* d) {
+  const int64_t groups = d->nheads / heads_per_block(*d);
+  const int64_t target = 3 * 256;
+  int64_t L = ((int64_t)rb->num_rows * groups + target - 1) / target;
+  L = (L + kQ - 1) / kQ * kQ;
+  if (L < kQ) L = kQ;
+  if (L > 4096) L = 4096;
+  return (int32_t)L;
 }
 
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t st) {
   const SegPtrs sp{(const int2*)(a.ws + a.lay.off_seq_info), (const int4*)(a.ws + a.lay.off_seg_info),
                    (float*)(a.ws + a.lay.off_seg_decay), (float*)(a.ws + a.lay.off_seg_state)};
   const mamba2_dims& d = a.dims;
-  M2_LAUNCH("ssd_state", ssd_mfma_state_kernel, dim3((unsigned)(a.lay.nseg * (d.nheads / 2))), dim3(256), 0,
-            st, (const bf16_t*)a.xbc, (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, d.ngroups);
+  const int HB = heads_per_block(d);
+  const int nitems = (int)(a.lay.nseg * (d.nheads / HB));
+  if (nitems == 0) return hipSuccess;
+  if (HB == 4) {
+    M2_LAUNCH("ssd_state", ssd_state_kernel<4>, dim3((unsigned)nitems), dim3(512), 0, st, (const bf16_t*)a.xbc,
+              (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, d.ngroups, nitems);
+  } else {
+    M2_LAUNCH("ssd_state", ssd_state_kernel<2>, dim3((unsigned)nitems), dim3(256), 0, st, (const bf16_t*)a.xbc,
+              (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, d.ngroups, nitems);
+  }
   hipError_t e = launch_scan_pass(a, st);
   if (e != hipSuccess) return e;
-  M2_LAUNCH("ssd_scan", ssd_mfma_scan_kernel, dim3((unsigned)(a.lay.nseg * d.nheads)), dim3(256), 0, st,
-            (bf16_t*)a.y, (const bf16_t*)a.xbc, (const bf16_t*)a.dt, a.a_log, a.dt_bias, a.D, a.ssm_state,
-            a.bd.slots, sp, d.nheads, d.ngroups);
+  if (HB == 4) {
+    M2_LAUNCH("ssd_scan", ssd_scan_kernel<4>, dim3((unsigned)nitems), dim3(512), 0, st, (bf16_t*)a.y,
+              (const bf16_t*)a.xbc, (const bf16_t*)a.dt, a.a_log, a.dt_bias, a.D, a.ssm_state, a.bd.slots, sp,
+              d.nheads, d.ngroups, nitems);
+  } else {
+    M2_LAUNCH("ssd_scan", ssd_scan_kernel<2>, dim3((unsigned)nitems), dim3(256), 0, st, (bf16_t*)a.y,
+              (const bf16_t*)a.xbc, (const bf16_t*)a.dt, a.a_log, a.dt_bias, a.D, a.ssm_state, a.bd.slots, sp,
+              d.nheads, d.ngroups, nitems);
+  }
   return hipSuccess;
 }
 
