@@ -53,17 +53,20 @@ constexpr int kN = 128;  // state dim
 constexpr int kQ = 64;   // chunk rows
 constexpr float kSpanMax = 40.f;       // largest log-decay span with factored weights
 constexpr float kFrameMin = 0x1p-20f;  // smallest state-frame scale before a rescale
+constexpr float kDropSpan = 60.f;      // a chunk decaying by more than e^-60 drops the carried state
 constexpr int kTiles = 10;             // lower-triangular 16 x 16 tiles of a 64 x 64 chunk
 
-// Per-chunk decay quantities of one head (written by one wave, read by all).
+// Per-chunk decay quantities of one head (written by the head's two waves, read by all).
 struct Decay {
-  float e[kQ];     // exp(cs_i) lam
-  float f[kQ];     // factored: exp(-cs_j) dt'_j / lam; exact: dt'_j
-  float cs[kQ];    // cs_i
-  float w[kQ];     // exp(cs_63 - cs_j) dt'_j / lam'
-  float scale;     // state rescale before this chunk's update (1: none)
-  int exact;       // 1: per-element exp(cs_i - cs_j)
-  float lam_next;  // lam'
+  float e[kQ];      // exp(cs_i) lam
+  float f[kQ];      // factored: exp(-cs_j) dt'_j / lam; exact: dt'_j
+  float cs[kQ];     // cs_i
+  float w[kQ];      // exp(cs_63 - cs_j) dt'_j / lam'
+  float ef[kQ];     // exact: exp(cs_b - cs_j) dt'_j, b the last row of j's 16-row block
+  float er[3][kQ];  // exact: exp(cs_i - cs_b), b = 16 jb + 15, for rows i past block jb
+  float scale;      // state factor before this chunk's update: 1 keep, 0 drop, else rescale
+  int exact;        // 1: intra-chunk weights without the exp(cs_i) exp(-cs_j) factoring
+  float lam_next;   // lam'
   float pad;
 };
 
@@ -87,6 +90,12 @@ __device__ __forceinline__ uint32_t pk(float lo, float hi) {
 __device__ __forceinline__ float lo_f(uint32_t u) { return __uint_as_float(u << 16); }
 __device__ __forceinline__ float hi_f(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
 __device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+// The same value, hidden from the optimiser: addresses derived from it are recomputed where
+// used instead of being kept live across the chunk loop.
+__device__ __forceinline__ int opaque(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
 __device__ __forceinline__ float uniformf(float v) {
   return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
 }
@@ -168,13 +177,25 @@ __device__ __forceinline__ u32x4 tr_frag(const bf16_t* base, int m) {
   return u32x4{a.x, a.y, b.x, b.y};
 }
 
-__device__ __forceinline__ float wave_scan_incl(float v, int lane) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const float t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
+// x + (x from another lane by the DPP control `ctrl`, 0 where there is none), on the rows
+// in row_mask.  All 64 lanes must be active.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xf, false));
+}
+// Inclusive prefix sum over the 64 lanes: shifts within 16-lane rows, then the row totals
+// broadcast forward (lane 15 to row 1 and 3, lane 31 to rows 2 and 3).
+__device__ __forceinline__ float wave_scan_incl(float v) {
+  v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xa>(v);  // row_bcast:15
+  v = dpp_add<0x143, 0xc>(v);  // row_bcast:31
   return v;
+}
+__device__ __forceinline__ float lane_value(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
 __device__ __forceinline__ constexpr int tile_index(int jb, int ib) { return ib * (ib + 1) / 2 + jb; }
@@ -188,73 +209,87 @@ __device__ __forceinline__ int work_item(int b, int n) {
 
 // ------------------------------------------------------------------ per-chunk pieces
 
-// Decay quantities of one head for a chunk (one wave; lane = chunk row, v = raw dt).
-// lam is the frame scale entering the chunk; it and lsum (sum of chunk log-decays) advance.
-__device__ __forceinline__ void chunk_decay(Decay& d, float v, float A, float bias, int nr, int lane,
+// Decay quantities of one head for a chunk (lane = chunk row, v = raw dt).  Both waves of
+// the head compute dt' and the prefix sums; half 0 writes the row scales and intra-chunk
+// weights, half 1 the update weights and the scalars.  lam is the frame scale entering the
+// chunk; it and lsum (sum of chunk log-decays) advance in both waves.
+__device__ __forceinline__ void chunk_decay(Decay& d, float v, float A, float bias, int nr, int lane, int ph,
                                             float& lam, float& lsum) {
   const float dtp = lane < nr ? softplus_f32(v + bias) : 0.f;
-  const float cs = wave_scan_incl(-A * dtp, lane);
-  const float cend = uniformf(__shfl(cs, 63, 64));
+  const float cs = wave_scan_incl(-A * dtp);
+  const float cend = lane_value(cs, 63);
   const bool exact = -cend > kSpanMax;
   const float tent = lam * __expf(cend);
   const bool reset = tent < kFrameMin;
   const float lam_next = reset ? 1.f : tent;
-  d.e[lane] = __expf(cs) * lam;
-  d.f[lane] = exact ? dtp : __expf(-cs) * dtp * (1.f / lam);
-  d.cs[lane] = cs;
-  d.w[lane] = __expf(cend - cs) * dtp * (1.f / lam_next);
-  if (lane == 0) {
-    d.scale = reset ? tent : 1.f;
-    d.exact = exact ? 1 : 0;
-    d.lam_next = lam_next;
+  if (ph == 0) {
+    d.e[lane] = __expf(cs) * lam;
+    d.f[lane] = exact ? dtp : __expf(-cs) * dtp * __builtin_amdgcn_rcpf(lam);
+    d.cs[lane] = cs;
+    if (exact) {
+#pragma unroll
+      for (int jb = 0; jb < 3; ++jb) d.er[jb][lane] = __expf(cs - lane_value(cs, 16 * jb + 15));
+    }
+  } else {
+    d.w[lane] = __expf(cend - cs) * dtp * __builtin_amdgcn_rcpf(lam_next);
+    if (exact) {
+      const int r = lane >> 4;
+      const float b0 = lane_value(cs, 15), b1 = lane_value(cs, 31), b2 = lane_value(cs, 47);
+      const float cb = r == 0 ? b0 : r == 1 ? b1 : r == 2 ? b2 : cend;
+      d.ef[lane] = __expf(cb - cs) * dtp;
+    }
+    if (lane == 0) {
+      d.scale = -cend > kDropSpan ? 0.f : (reset ? tent : 1.f);
+      d.exact = exact ? 1 : 0;
+      d.lam_next = lam_next;
+    }
   }
   lam = lam_next;
   lsum += cend;
 }
 
-// Per-lane byte offsets of the global -> LDS copies (see load_chunk).
+// A wave's B / C instructions all have block index k of the wave's parity (see load_bc).
 struct DmaOfs {
-  uint32_t bc[2];  // B / C block rows, [k % 2]
-  uint32_t x;      // x block rows
+  uint32_t bc;  // B / C block rows
+  uint32_t x;   // x block rows
 };
-__device__ __forceinline__ DmaOfs dma_offsets(int lane, uint32_t ld) {
+__device__ __forceinline__ DmaOfs dma_offsets(int lane, int w, uint32_t ld) {
   DmaOfs o;
   const int r = lane >> 4;
-#pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    const int u = (lane & 15) ^ ((2 * r) | a);  // swz(4 k + r) = 2 r | (k % 2)
-    o.bc[a] = 2u * ((uint32_t)r * ld + 8u * (uint32_t)u);
-  }
+  // swz(4 k + r) = 2 r | (k % 2)
+  o.bc = 2u * ((uint32_t)r * ld + 8u * (uint32_t)((lane & 15) ^ (2 * r + (w & 1))));
   const int rx = lane >> 3;
   o.x = 2u * ((uint32_t)rx * ld + 8u * (uint32_t)((lane & 7) ^ swz(rx)));
   return o;
 }
 
-// Copy chunk rows [r0, r0 + nr) of B (and C) [64][128] and the x of HB heads [64][64] into
-// LDS.  Each instruction fills 1 KB of a tile (4 rows of B or C, 8 rows of x), each lane
-// fetching the global 16-byte unit that the swizzle places at its LDS slot; rows past nr
-// read as zero.  The 16 + 16 + 8 HB instructions are dealt round robin to the 2 HB waves.
-template <int HB, bool kWithC>
-__device__ __forceinline__ void load_chunk(const bf16_t* rows, int nr, uint32_t ld, uint32_t colB, uint32_t colC,
-                                           uint32_t colX, bf16_t* sB, bf16_t* sC, bf16_t (*sX)[kQ * kP],
-                                           const DmaOfs& o, int w) {
+// Global -> LDS copies of chunk rows [r0, r0 + nr): each instruction fills 1 KB of a tile
+// (4 rows of a [64][128] B or C tile, 8 rows of a [64][64] x tile), each lane fetching the
+// global 16-byte unit that the swizzle places at its LDS slot; rows past nr read as zero.
+// Instructions are dealt round robin to the 2 HB waves.
+template <int HB, int NT>
+__device__ __forceinline__ void load_bc(const bf16_t* rows, int nr, uint32_t ld, const uint32_t (&col)[NT],
+                                        bf16_t* const (&dst)[NT], const DmaOfs& o, int w) {
   constexpr int nW = 2 * HB;
-  constexpr int nBC = kWithC ? 32 : 16;
-  constexpr int nAll = nBC + 8 * HB;
-  static_assert(nAll % nW == 0 && 16 % nW == 0, "instruction split");
+  static_assert(16 % nW == 0, "instruction split");
 #pragma unroll
-  for (int i = 0; i < nAll / nW; ++i) {
-    const int t = w + nW * i;  // wave-uniform; t < 16, < nBC per i at compile time
-    if (nW * i < nBC) {
-      const int k = t & 15;
-      const Rsrc r = make_rsrc(rows + (size_t)(4 * k) * ld, ((int64_t)nr - 4 * k) * ld * 2);
-      const bool isB = nW * i < 16;
-      dma16(r, (isB ? sB : sC) + 512 * k, o.bc[k & 1], 2u * (isB ? colB : colC));
-    } else {
-      const int hh = (t - nBC) >> 3, k = (t - nBC) & 7;
-      const Rsrc r = make_rsrc(rows + (size_t)(8 * k) * ld, ((int64_t)nr - 8 * k) * ld * 2);
-      dma16(r, sX[hh] + 512 * k, o.x, 2u * (colX + (uint32_t)(hh * kP)));
-    }
+  for (int i = 0; i < 16 * NT / nW; ++i) {
+    const int tile = nW * i / 16;  // compile time
+    const int k = (w + nW * i) & 15;
+    const Rsrc r = make_rsrc(rows + (size_t)(4 * k) * ld, ((int64_t)nr - 4 * k) * ld * 2);
+    dma16(r, dst[tile] + 512 * k, o.bc, 2u * col[tile]);  // k % 2 == w % 2
+  }
+}
+template <int HB>
+__device__ __forceinline__ void load_x(const bf16_t* rows, int nr, uint32_t ld, uint32_t colX,
+                                       bf16_t (*sX)[kQ * kP], const DmaOfs& o, int w) {
+  constexpr int nW = 2 * HB;
+#pragma unroll
+  for (int i = 0; i < 8 * HB / nW; ++i) {
+    const int t = w + nW * i;
+    const int hh = t >> 3, k = t & 7;
+    const Rsrc r = make_rsrc(rows + (size_t)(8 * k) * ld, ((int64_t)nr - 8 * k) * ld * 2);
+    dma16(r, sX[hh] + 512 * k, o.x, 2u * (colX + (uint32_t)(hh * kP)));
   }
 }
 
@@ -269,7 +304,25 @@ __device__ __forceinline__ void wx_frag(const u32x4& xt, const Decay& d, int m, 
   lo = u32x4{a[2], a[3], b[2], b[3]};
 }
 
-// S^T(nb, pb) += B^T (w o x) for the wave's two p blocks; xt[t][m] are the x^T operands.
+// S^T(nb, pb) (+)= B^T (w o x) for the wave's two p blocks; kFresh starts from zero.
+template <bool kFresh>
+__device__ __forceinline__ void su_mfma(f32x4 (&S)[2][8], const u32x4 (&wh)[2][2], const u32x4 (&wl)[2][2],
+                                        const bf16_t* sB, const Lofs& lo) {
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const u32x4 bt = tr_frag<kN>(sB + lo.bt[nb & 3] + 64 * (nb >> 2), m);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        S[t][nb] = mfma(bt, wh[t][m], (kFresh && m == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][nb]);
+        S[t][nb] = mfma(bt, wl[t][m], S[t][nb]);
+      }
+    }
+  }
+}
+
+// State update for the chunk: S <- scale S + B^T (w o x); xt[t][m] are the x^T operands.
 __device__ __forceinline__ void state_update(f32x4 (&S)[2][8], const u32x4 (&xt)[2][2], const bf16_t* sB,
                                              const Lofs& lo, const Decay& d, int lane) {
   u32x4 wh[2][2], wl[2][2];
@@ -278,23 +331,16 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[2][8], const u32x4 (&xt)
 #pragma unroll
     for (int m = 0; m < 2; ++m) wx_frag(xt[t][m], d, m, lane, wh[t][m], wl[t][m]);
   const float scale = uniformf(d.scale);
-  if (scale != 1.f) {
+  if (scale == 0.f) {
+    su_mfma<true>(S, wh, wl, sB, lo);
+  } else {
+    if (scale != 1.f) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) S[t][nb] *= scale;
-  }
-#pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const u32x4 bt = tr_frag<kN>(sB + lo.bt[nb & 3] + 64 * (nb >> 2), m);
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        S[t][nb] = mfma(bt, wh[t][m], S[t][nb]);
-        S[t][nb] = mfma(bt, wl[t][m], S[t][nb]);
-      }
+        for (int nb = 0; nb < 8; ++nb) S[t][nb] *= scale;
     }
+    su_mfma<false>(S, wh, wl, sB, lo);
   }
 }
 
@@ -330,11 +376,14 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __
   const int Di = H * kP;
   const uint32_t ld = (uint32_t)(Di + 2 * G * kN);
   const int grp = h0 / (H / G);
-  const uint32_t colB = (uint32_t)(Di + grp * kN), colX = (uint32_t)(h0 * kP);
+  const uint32_t colB[1] = {(uint32_t)(Di + grp * kN)};
+  const uint32_t colX = (uint32_t)(h0 * kP);
   const float A = __expf(a_log[h]), bias = dt_bias[h];
   const int nchunks = (si.z + kQ - 1) / kQ;
   const Lofs lo = lane_offsets(lane, ph);
-  const DmaOfs dof = dma_offsets(lane, ld);
+  const DmaOfs dof = dma_offsets(lane, w, ld);
+  bf16_t* const dB0[1] = {sB0};
+  bf16_t* const dB1[1] = {sB1};
 
   auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
   auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
@@ -350,18 +399,20 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __
     for (int nb = 0; nb < 8; ++nb) S[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   float lam = 1.f, lsum = 0.f, dtn = 0.f;
-  load_chunk<HB, false>(rows_of(0), nr_of(0), ld, colB, 0, colX, sB0, nullptr, sX0, dof, w);
-  if (ph == 0) chunk_decay(sD[0][hh], dt_of(0), A, bias, nr_of(0), lane, lam, lsum);
-  if (ph == 0 && nchunks > 1) dtn = dt_of(1);
+  load_bc<HB, 1>(rows_of(0), nr_of(0), ld, colB, dB0, dof, w);
+  load_x<HB>(rows_of(0), nr_of(0), ld, colX, sX0, dof, w);
+  chunk_decay(sD[0][hh], dt_of(0), A, bias, nr_of(0), lane, ph, lam, lsum);
+  if (nchunks > 1) dtn = dt_of(1);
 
-  auto step = [&](int q, bf16_t* sBc, bf16_t (*sXc)[kQ * kP], bf16_t* sBn, bf16_t (*sXn)[kQ * kP], Decay* dc,
-                  Decay* dn) {
+  auto step = [&](int q, const bf16_t* sBc, bf16_t (*sXc)[kQ * kP], bf16_t* const (&dBn)[1],
+                  bf16_t (*sXn)[kQ * kP], Decay* dc, Decay* dn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // chunk q rows and decay visible; chunk q-1 done with the other stage
     float dtn2 = 0.f;
     if (q + 1 < nchunks) {
-      load_chunk<HB, false>(rows_of(q + 1), nr_of(q + 1), ld, colB, 0, colX, sBn, nullptr, sXn, dof, w);
-      if (ph == 0 && q + 2 < nchunks) dtn2 = dt_of(q + 2);
+      load_bc<HB, 1>(rows_of(q + 1), nr_of(q + 1), ld, colB, dBn, dof, w);
+      load_x<HB>(rows_of(q + 1), nr_of(q + 1), ld, colX, sXn, dof, w);
+      if (q + 2 < nchunks) dtn2 = dt_of(q + 2);
     }
     u32x4 xt[2][2];
 #pragma unroll
@@ -369,22 +420,23 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __
 #pragma unroll
       for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sXc[hh] + lo.xt[t], m);
     state_update(S, xt, sBc, lo, dc[hh], lane);
-    if (ph == 0 && q + 1 < nchunks) chunk_decay(dn[hh], dtn, A, bias, nr_of(q + 1), lane, lam, lsum);
+    if (q + 1 < nchunks) chunk_decay(dn[hh], dtn, A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
   };
 
   for (int q = 0; q < nchunks; q += 2) {
-    step(q, sB0, sX0, sB1, sX1, sD[0], sD[1]);
-    if (q + 1 < nchunks) step(q + 1, sB1, sX1, sB0, sX0, sD[1], sD[0]);
+    step(q, sB0, sX0, dB1, sX1, sD[0], sD[1]);
+    if (q + 1 < nchunks) step(q + 1, sB1, sX1, dB0, sX0, sD[1], sD[0]);
   }
 
   const float lam_end = uniformf(sD[(nchunks - 1) & 1][hh].lam_next);
   float* out = sp.seg_state + ((size_t)seg * H + h) * (size_t)(kP * kN);
+  const int lane_st = opaque(lane);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
-      *reinterpret_cast<f32x4*>(out + state_elem(ph, t, nb, lane)) = S[t][nb] * lam_end;
+      *reinterpret_cast<f32x4*>(out + state_elem(ph, t, nb, lane_st)) = S[t][nb] * lam_end;
   if (ph == 0 && lane == 0) sp.seg_decay[(size_t)seg * H + h] = __expf(lsum);
 }
 
@@ -416,13 +468,18 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
   const int Di = H * kP;
   const uint32_t ld = (uint32_t)(Di + 2 * G * kN);
   const int grp = h0 / (H / G);
-  const uint32_t colB = (uint32_t)(Di + grp * kN), colC = (uint32_t)(Di + (G + grp) * kN);
+  const uint32_t colBC[2] = {(uint32_t)(Di + grp * kN), (uint32_t)(Di + (G + grp) * kN)};
   const uint32_t colX = (uint32_t)(h0 * kP);
-  const float A = __expf(a_log[h]), bias = dt_bias[h], dh = Dp[h];
+  const float A = __expf(a_log[h]), bias = dt_bias[h];
+  float Dh[HB];
+#pragma unroll
+  for (int i = 0; i < HB; ++i) Dh[i] = Dp[h0 + i];
   const int nchunks = (si.z + kQ - 1) / kQ;
   const Lofs lo = lane_offsets(lane, ph);
-  const DmaOfs dof = dma_offsets(lane, ld);
+  const DmaOfs dof = dma_offsets(lane, w, ld);
   const uint32_t yvoff = 2u * ((uint32_t)c * (uint32_t)Di + 4u * (uint32_t)g);
+  bf16_t* const dBC0[2] = {sB0, sC0};
+  bf16_t* const dBC1[2] = {sB1, sC1};
 
   auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
   auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
@@ -442,27 +499,64 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
   }
 
   float lam = 1.f, lsum = 0.f, dtn = 0.f;
-  load_chunk<HB, true>(rows_of(0), nr_of(0), ld, colB, colC, colX, sB0, sC0, sX, dof, w);
-  if (ph == 0) chunk_decay(sD[0][hh], dt_of(0), A, bias, nr_of(0), lane, lam, lsum);
-  if (ph == 0 && nchunks > 1) dtn = dt_of(1);
+  load_bc<HB, 2>(rows_of(0), nr_of(0), ld, colBC, dBC0, dof, w);
+  load_x<HB>(rows_of(0), nr_of(0), ld, colX, sX, dof, w);
+  chunk_decay(sD[0][hh], dt_of(0), A, bias, nr_of(0), lane, ph, lam, lsum);
+  if (nchunks > 1) dtn = dt_of(1);
 
-  auto step = [&](int q, bf16_t* sBc, bf16_t* sCc, bf16_t* sBn, bf16_t* sCn, Decay* dc, Decay* dn) {
+  // M^T tile t = (jb, ib) of head `head` from the G^T tile, in operand order, hi and lo;
+  // D sits on the diagonal (divided by the row scale when that is applied afterwards).
+  // gq, cq: the lane's g and c, recomputed per chunk (see opaque).
+  auto m_tile = [&](const f32x4& gt, int t, int jb, int ib, int head, const Decay* dc, int gq, int cq) {
+    const Decay& d = dc[head];
+    float v[4];
+    if (uniform(d.exact)) {
+      if (jb < ib) {
+        const f32x4 ef = *reinterpret_cast<const f32x4*>(&d.ef[16 * jb + 4 * gq]);
+        const float er = d.er[jb][16 * ib + cq];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = gt[r] * (ef[r] * er);
+      } else {
+        const float csi = d.cs[16 * ib + cq];
+        const f32x4 csj = *reinterpret_cast<const f32x4*>(&d.cs[16 * jb + 4 * gq]);
+        const f32x4 dtj = *reinterpret_cast<const f32x4*>(&d.f[16 * jb + 4 * gq]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = 4 * gq + r == cq ? Dh[head] : 0.f;
+          v[r] = 4 * gq + r > cq ? 0.f : fmaf(gt[r], __expf(csi - csj[r]) * dtj[r], e);
+        }
+      }
+    } else {
+      const f32x4 fj = *reinterpret_cast<const f32x4*>(&d.f[16 * jb + 4 * gq]);
+      if (jb < ib) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = gt[r] * fj[r];
+      } else {
+        const float dd = Dh[head] * __builtin_amdgcn_rcpf(d.e[16 * ib + cq]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float e = 4 * gq + r == cq ? dd : 0.f;
+          v[r] = 4 * gq + r > cq ? 0.f : fmaf(gt[r], fj[r], e);
+        }
+      }
+    }
+    sM[head][t][lane] = split4(v[0], v[1], v[2], v[3]);
+  };
+
+  auto step = [&](int q, const bf16_t* sBc, const bf16_t* sCc, bf16_t* const (&dn_bc)[2], Decay* dc, Decay* dn) {
     const int r0 = si.y + q * kQ;
     const int nr = nr_of(q);
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // (1) chunk q rows and decay visible; chunk q-1 done with x and M
+    __syncthreads();  // (1) chunk q rows and decay visible; chunk q-1 done with x, M, the other stage
+    if (q + 1 < nchunks) load_bc<HB, 2>(rows_of(q + 1), nr_of(q + 1), ld, colBC, dn_bc, dof, w);
+    const int gq = opaque(g), cq = opaque(c);
 
-    // ---- phase 1: x operands; G^T tiles and M^T for the workgroup's heads ----
+    // ---- phase 1: x operands; G^T tiles and M^T for the workgroup's heads; S C^T ----
     u32x4 xt[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sX[hh] + lo.xt[t], m);
-    u32x2 xd[2][4];  // x[i = 16 ib + c][p = 32 ph + 16 t + 4 g ..+3] for D x
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int ib = 0; ib < 4; ++ib) xd[t][ib] = lds8(sX[hh] + lo.xd[t] + 16 * ib * kP);
 
     auto gt_tile = [&](int jb, int ib) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -472,25 +566,6 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
                    lds16(sCc + lo.gt[kk & 1] + 16 * ib * kN + 64 * (kk >> 1)), acc);
       return acc;
     };
-    auto m_tile = [&](const f32x4& gt, int t, int jb, int ib, int head) {
-      const Decay& d = dc[head];
-      const f32x4 fj = *reinterpret_cast<const f32x4*>(&d.f[16 * jb + 4 * g]);
-      float v[4];
-      if (uniform(d.exact)) {
-        const float csi = d.cs[16 * ib + c];
-        const f32x4 csj = *reinterpret_cast<const f32x4*>(&d.cs[16 * jb + 4 * g]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = gt[r] * (__expf(csi - csj[r]) * fj[r]);
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = gt[r] * fj[r];
-      }
-      if (jb == ib) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = (4 * g + r > c) ? 0.f : v[r];
-      }
-      sM[head][t][lane] = split4(v[0], v[1], v[2], v[3]);
-    };
     // tiles 0..7 for every head, one per wave (two per wave with four waves)
 #pragma unroll
     for (int i = 0; i < 8 / (2 * HB); ++i) {
@@ -499,21 +574,13 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
       const int jb = t - ib * (ib + 1) / 2;
       const f32x4 gt = gt_tile(jb, ib);
 #pragma unroll
-      for (int head = 0; head < HB; ++head) m_tile(gt, t, jb, ib, head);
+      for (int head = 0; head < HB; ++head) m_tile(gt, t, jb, ib, head, dc, gq, cq);
     }
     // tiles 8 = (2, 3) and 9 = (3, 3) for the wave's own head
-    if (ph == 0) m_tile(gt_tile(2, 3), 8, 2, 3, hh);
-    else m_tile(gt_tile(3, 3), 9, 3, 3, hh);
-    __syncthreads();  // (2) M^T visible; x of chunk q no longer read
+    if (ph == 0) m_tile(gt_tile(2, 3), 8, 2, 3, hh, dc, gq, cq);
+    else m_tile(gt_tile(3, 3), 9, 3, 3, hh, dc, gq, cq);
 
-    float dtn2 = 0.f;
-    if (q + 1 < nchunks) {
-      load_chunk<HB, true>(rows_of(q + 1), nr_of(q + 1), ld, colB, colC, colX, sBn, sCn, sX, dof, w);
-      if (ph == 0 && q + 2 < nchunks) dtn2 = dt_of(q + 2);
-    }
-
-    // ---- phase 2: Y^T(pb, ib) = S C^T + x^T M^T (row scales), + D x ----
-    const Decay& d = dc[hh];
+    // Y^T(pb, ib) = S C^T, the state operand split from the accumulators
     f32x4 Y[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -525,9 +592,9 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         const f32x4 a = S[t][2 * kk], b = S[t][2 * kk + 1];
-        const u32x4 s0 = split4(a[0], a[1], a[2], a[3]), s1 = split4(b[0], b[1], b[2], b[3]);
-        sh[t] = u32x4{s0[0], s0[1], s1[0], s1[1]};
-        sl[t] = u32x4{s0[2], s0[3], s1[2], s1[3]};
+        sh[t] = u32x4{pk(a[0], a[1]), pk(a[2], a[3]), pk(b[0], b[1]), pk(b[2], b[3])};
+        sl[t] = u32x4{pk(a[0] - lo_f(sh[t][0]), a[1] - hi_f(sh[t][0])), pk(a[2] - lo_f(sh[t][1]), a[3] - hi_f(sh[t][1])),
+                      pk(b[0] - lo_f(sh[t][2]), b[1] - hi_f(sh[t][2])), pk(b[2] - lo_f(sh[t][3]), b[3] - hi_f(sh[t][3]))};
       }
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
@@ -542,16 +609,26 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
         }
       }
     }
+    const Decay& d = dc[hh];
     const bool exact = uniform(d.exact) != 0;
     float ei[4];
 #pragma unroll
-    for (int ib = 0; ib < 4; ++ib) ei[ib] = d.e[16 * ib + c];
+    for (int ib = 0; ib < 4; ++ib) ei[ib] = d.e[16 * ib + cq];
     if (exact) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) Y[t][ib] *= ei[ib];
     }
+    __syncthreads();  // (2) M^T visible; x of chunk q no longer read
+
+    float dtn2 = 0.f;
+    if (q + 1 < nchunks) {
+      load_x<HB>(rows_of(q + 1), nr_of(q + 1), ld, colX, sX, dof, w);
+      if (q + 2 < nchunks) dtn2 = dt_of(q + 2);
+    }
+
+    // ---- phase 2: + x^T M^T (D x on its diagonal), row scales, store ----
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) {
 #pragma unroll
@@ -573,36 +650,32 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
     for (int ib = 0; ib < 4; ++ib) {
       // rows 16 ib.. of the chunk; rows at or past nr are dropped by the range
       const Rsrc yr = make_rsrc(y + (size_t)(r0 + 16 * ib) * Di, ((int64_t)nr - 16 * ib) * Di * 2);
-      const float sc = exact ? 1.f : ei[ib];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const u32x2 xv = xd[t][ib];
-        const float o0 = fmaf(dh, lo_f(xv.x), Y[t][ib][0] * sc);
-        const float o1 = fmaf(dh, hi_f(xv.x), Y[t][ib][1] * sc);
-        const float o2 = fmaf(dh, lo_f(xv.y), Y[t][ib][2] * sc);
-        const float o3 = fmaf(dh, hi_f(xv.y), Y[t][ib][3] * sc);
-        bst8(yr, yvoff, 2u * (uint32_t)(h * kP + 32 * ph + 16 * t), u32x2{pk(o0, o1), pk(o2, o3)});
+        const f32x4 o = exact ? Y[t][ib] : Y[t][ib] * ei[ib];
+        bst8(yr, yvoff, 2u * (uint32_t)(h * kP + 32 * ph + 16 * t), u32x2{pk(o[0], o[1]), pk(o[2], o[3])});
       }
     }
 
     // ---- state update ----
     state_update(S, xt, sBc, lo, d, lane);
-    if (ph == 0 && q + 1 < nchunks) chunk_decay(dn[hh], dtn, A, bias, nr_of(q + 1), lane, lam, lsum);
+    if (q + 1 < nchunks) chunk_decay(dn[hh], dtn, A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
   };
 
   for (int q = 0; q < nchunks; q += 2) {
-    step(q, sB0, sC0, sB1, sC1, sD[0], sD[1]);
-    if (q + 1 < nchunks) step(q + 1, sB1, sC1, sB0, sC0, sD[1], sD[0]);
+    step(q, sB0, sC0, dBC1, sD[0], sD[1]);
+    if (q + 1 < nchunks) step(q + 1, sB1, sC1, dBC0, sD[1], sD[0]);
   }
   if (last) {
     const float lam_end = uniformf(sD[(nchunks - 1) & 1][hh].lam_next);
     float* out = pool + ((size_t)slots[si.x] * H + h) * (size_t)(kP * kN);
+    const int lane_st = opaque(lane);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb)
-        *reinterpret_cast<f32x4*>(out + state_elem(ph, t, nb, lane)) = S[t][nb] * lam_end;
+        *reinterpret_cast<f32x4*>(out + state_elem(ph, t, nb, lane_st)) = S[t][nb] * lam_end;
   }
 }
 
