@@ -30,10 +30,11 @@
 // per wave, plus the last two tiles per head), scaled per head into M^T and shared through
 // LDS in operand order.  Chunk rows of B, C and x are copied global -> LDS by buffer loads
 // that write LDS directly (B and C double-buffered), XOR-swizzled in 16-byte units; the
-// transposed operands (x^T, B^T) come from the gfx950 transposing LDS read.  Every
-// contraction over chunk rows (j) and state columns (n) uses the same permuted k order
-// within a 32-wide k block: slot s of lane group g is index 16 (s / 4) + 4 g + s % 4, the
-// row order of two stacked 16 x 16 accumulator tiles.
+// transposed operands (x^T, B^T) come from the gfx950 transposing LDS read.  Contractions
+// use permuted k orders that match the accumulator layout (lane group g holds rows 4 g..4 g+3
+// of a 16 x 16 tile): over chunk rows j, slot s of group g in k block m is
+// j = 32 m + 16 (s / 4) + 4 g + s % 4 (two stacked tiles); over state columns n in S C^T,
+// block kk pairs state tiles kk and kk + 4: n = 16 kk + 64 (s / 4) + 4 g + s % 4.
 #include "common.h"
 
 namespace m2 {
@@ -101,8 +102,15 @@ __device__ __forceinline__ float uniformf(float v) {
 }
 
 // Split 4 fp32 values into packed bf16 hi (x, y) and lo (z, w) halves.
+// The packed hi halves pass through an empty asm so that the lo halves are formed from
+// them (one shift or mask each) instead of from a second conversion.
+__device__ __forceinline__ uint32_t pk_hi(float lo, float hi) {
+  uint32_t h = pk(lo, hi);
+  asm("" : "+v"(h));
+  return h;
+}
 __device__ __forceinline__ u32x4 split4(float v0, float v1, float v2, float v3) {
-  const uint32_t h01 = pk(v0, v1), h23 = pk(v2, v3);
+  const uint32_t h01 = pk_hi(v0, v1), h23 = pk_hi(v2, v3);
   return u32x4{h01, h23, pk(v0 - lo_f(h01), v1 - hi_f(h01)), pk(v2 - lo_f(h23), v3 - hi_f(h23))};
 }
 
@@ -113,13 +121,34 @@ __device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
   const int n = bytes <= 0 ? 0 : (int)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
+// bf16 bits of dt[r0 + lane][h] for lanes below nr, else 0: a branch-free load whose value
+// is only waited for where it is converted.
+__device__ __forceinline__ uint32_t dt_bits(const bf16_t* dt, int r0, int nr, int H, int h, int lane) {
+  const Rsrc r = make_rsrc(dt + (size_t)r0 * H + h, (int64_t)nr * H * 2);
+  return __builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)(lane * H * 2), 0, 0);
+}
 __device__ __forceinline__ void bst8(Rsrc r, uint32_t voff, uint32_t soff, u32x2 v) {
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
 }
-// 16 bytes per lane from the buffer into LDS at lds + 16 * lane (lds wave-uniform).
-__device__ __forceinline__ void dma16(Rsrc r, const bf16_t* lds, uint32_t voff, uint32_t soff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (M2_LDS void*)lds, 16, voff, soff, 0, 0);
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds wave-uniform): a
+// buffer load that writes LDS, over `bytes` bytes from `base` (lane offsets at or past the
+// end write zeros).  Issued from inline assembly so that the compiler, which cannot tell
+// these LDS writes apart from the tiles being read meanwhile, adds no waits of its own;
+// the copies are waited for (vmcnt 0) before the barrier that publishes them.
+typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // m0 is set here and used by nothing else
+__device__ __forceinline__ void dma16(const void* base, int64_t bytes, const bf16_t* lds, uint32_t voff,
+                                      uint32_t soff) {
+  const uint64_t a = (uint64_t)base;
+  const u32x4s rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes <= 0 ? 0u : (uint32_t)bytes, 0x00020000u};
+  const uint32_t m0 = (uint32_t)(uintptr_t)(const M2_LDS void*)lds;
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
+               : "m0");
 }
+#pragma clang diagnostic pop
 
 // XOR swizzle of 16-byte units within a tile row: four consecutive rows (transposing
 // reads) and eight consecutive rows (row reads) land on distinct bank groups.  It depends
@@ -143,7 +172,7 @@ __device__ __forceinline__ u32x2 tr8(const bf16_t* p) {
 // Lane (c, g) = (lane % 16, lane / 16); q = (lane % 16) / 4, b = (lane % 4) / 2.
 struct Lofs {
   int gt[2];     // B / C row 16 jb + c, elements 32 kk + 8 g..: + 16 jb*128 + 64 (kk/2), [kk%2]
-  int cf[2][2];  // C row 16 ib + c, elements 32 kk + 16 h + 4 g..: + 16 ib*128 + 64 (kk/2), [kk%2][h]
+  int cf[4];     // C row 16 ib + c, elements 16 kk + 4 g.. (and + 64): + 16 ib*128, [kk]
   int bt[4];     // B^T transposing read for column block nb: + row0*128 + 64 (nb/4), [nb%4]
   int xt[2];     // x^T transposing read for p block 32 ph + 16 t: + row0*64, [t]
   int xd[2];     // x row 16 ib + c, elements 32 ph + 16 t + 4 g..: + 16 ib*64, [t]
@@ -155,9 +184,9 @@ __device__ __forceinline__ Lofs lane_offsets(int lane, int ph) {
 #pragma unroll
   for (int a = 0; a < 2; ++a) {
     o.gt[a] = c * kN + (((4 * a + g) ^ sc) << 3);
-#pragma unroll
-    for (int h = 0; h < 2; ++h) o.cf[a][h] = c * kN + (((4 * a + 2 * h + (g >> 1)) ^ sc) << 3) + 4 * (g & 1);
   }
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) o.cf[kk] = c * kN + (((2 * kk + (g >> 1)) ^ sc) << 3) + 4 * (g & 1);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) o.bt[nb] = (4 * g + q) * kN + (((2 * nb + b) ^ sq) << 3) + e;
 #pragma unroll
@@ -198,7 +227,14 @@ __device__ __forceinline__ float lane_value(float v, int l) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
 }
 
-__device__ __forceinline__ constexpr int tile_index(int jb, int ib) { return ib * (ib + 1) / 2 + jb; }
+// M^T operand (ib, m), m <= ib / 2, holds tiles jb = 2 m (slots 0..3) and 2 m + 1 (slots
+// 4..7) of column block ib.  LDS keeps it in 1 KB units of [64 lanes][16 bytes]: two units
+// (hi, lo) for a full operand; one unit {hi of jb, lo of jb} when tile 2 m + 1 lies above
+// the diagonal (operands (0, 0) and (2, 1)).
+__device__ __forceinline__ constexpr int m_unit(int ib, int m) {
+  return ib == 0 ? 0 : ib == 1 ? 1 : ib == 2 ? (m == 0 ? 3 : 5) : (m == 0 ? 6 : 8);
+}
+__device__ __forceinline__ constexpr bool m_half(int ib, int m) { return (ib == 0) || (ib == 2 && m == 1); }
 
 // Workgroup b runs on XCD b % 8; give each XCD a contiguous range of work items so the
 // head groups of one segment share that XCD's L2.
@@ -276,8 +312,8 @@ __device__ __forceinline__ void load_bc(const bf16_t* rows, int nr, uint32_t ld,
   for (int i = 0; i < 16 * NT / nW; ++i) {
     const int tile = nW * i / 16;  // compile time
     const int k = (w + nW * i) & 15;
-    const Rsrc r = make_rsrc(rows + (size_t)(4 * k) * ld, ((int64_t)nr - 4 * k) * ld * 2);
-    dma16(r, dst[tile] + 512 * k, o.bc, 2u * col[tile]);  // k % 2 == w % 2
+    dma16(rows + (size_t)(4 * k) * ld, ((int64_t)nr - 4 * k) * ld * 2, dst[tile] + 512 * k, o.bc,
+          2u * col[tile]);  // k % 2 == w % 2
   }
 }
 template <int HB>
@@ -288,8 +324,8 @@ __device__ __forceinline__ void load_x(const bf16_t* rows, int nr, uint32_t ld, 
   for (int i = 0; i < 8 * HB / nW; ++i) {
     const int t = w + nW * i;
     const int hh = t >> 3, k = t & 7;
-    const Rsrc r = make_rsrc(rows + (size_t)(8 * k) * ld, ((int64_t)nr - 8 * k) * ld * 2);
-    dma16(r, sX[hh] + 512 * k, o.x, 2u * (colX + (uint32_t)(hh * kP)));
+    dma16(rows + (size_t)(8 * k) * ld, ((int64_t)nr - 8 * k) * ld * 2, sX[hh] + 512 * k, o.x,
+          2u * (colX + (uint32_t)(hh * kP)));
   }
 }
 
@@ -387,10 +423,7 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __
 
   auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
   auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
-  auto dt_of = [&](int q) {
-    const int r0 = si.y + q * kQ;
-    return lane < nr_of(q) ? bf16_to_f32(dt[(size_t)(r0 + lane) * H + h]) : 0.f;
-  };
+  auto dt_of = [&](int q) { return dt_bits(dt, si.y + q * kQ, nr_of(q), H, h, lane); };
 
   f32x4 S[2][8];
 #pragma unroll
@@ -398,17 +431,18 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) S[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  float lam = 1.f, lsum = 0.f, dtn = 0.f;
+  float lam = 1.f, lsum = 0.f;
+  uint32_t dtn = 0;
   load_bc<HB, 1>(rows_of(0), nr_of(0), ld, colB, dB0, dof, w);
   load_x<HB>(rows_of(0), nr_of(0), ld, colX, sX0, dof, w);
-  chunk_decay(sD[0][hh], dt_of(0), A, bias, nr_of(0), lane, ph, lam, lsum);
+  chunk_decay(sD[0][hh], bf16_to_f32(dt_of(0)), A, bias, nr_of(0), lane, ph, lam, lsum);
   if (nchunks > 1) dtn = dt_of(1);
 
   auto step = [&](int q, const bf16_t* sBc, bf16_t (*sXc)[kQ * kP], bf16_t* const (&dBn)[1],
                   bf16_t (*sXn)[kQ * kP], Decay* dc, Decay* dn) {
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // chunk q rows and decay visible; chunk q-1 done with the other stage
-    float dtn2 = 0.f;
+    uint32_t dtn2 = 0;
     if (q + 1 < nchunks) {
       load_bc<HB, 1>(rows_of(q + 1), nr_of(q + 1), ld, colB, dBn, dof, w);
       load_x<HB>(rows_of(q + 1), nr_of(q + 1), ld, colX, sXn, dof, w);
@@ -420,7 +454,7 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __
 #pragma unroll
       for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sXc[hh] + lo.xt[t], m);
     state_update(S, xt, sBc, lo, dc[hh], lane);
-    if (q + 1 < nchunks) chunk_decay(dn[hh], dtn, A, bias, nr_of(q + 1), lane, ph, lam, lsum);
+    if (q + 1 < nchunks) chunk_decay(dn[hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
   };
 
@@ -483,10 +517,7 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
 
   auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
   auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
-  auto dt_of = [&](int q) {
-    const int r0 = si.y + q * kQ;
-    return lane < nr_of(q) ? bf16_to_f32(dt[(size_t)(r0 + lane) * H + h]) : 0.f;
-  };
+  auto dt_of = [&](int q) { return dt_bits(dt, si.y + q * kQ, nr_of(q), H, h, lane); };
 
   // the state entering the segment (written by the pass kernel), frame scale 1
   f32x4 S[2][8];
@@ -498,10 +529,11 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
       for (int nb = 0; nb < 8; ++nb) S[t][nb] = *reinterpret_cast<const f32x4*>(in + state_elem(ph, t, nb, lane));
   }
 
-  float lam = 1.f, lsum = 0.f, dtn = 0.f;
+  float lam = 1.f, lsum = 0.f;
+  uint32_t dtn = 0;
   load_bc<HB, 2>(rows_of(0), nr_of(0), ld, colBC, dBC0, dof, w);
   load_x<HB>(rows_of(0), nr_of(0), ld, colX, sX, dof, w);
-  chunk_decay(sD[0][hh], dt_of(0), A, bias, nr_of(0), lane, ph, lam, lsum);
+  chunk_decay(sD[0][hh], bf16_to_f32(dt_of(0)), A, bias, nr_of(0), lane, ph, lam, lsum);
   if (nchunks > 1) dtn = dt_of(1);
 
   // M^T tile t = (jb, ib) of head `head` from the G^T tile, in operand order, hi and lo;
@@ -540,7 +572,15 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
         }
       }
     }
-    sM[head][t][lane] = split4(v[0], v[1], v[2], v[3]);
+    const u32x4 hl = split4(v[0], v[1], v[2], v[3]);
+    const int m = jb >> 1, u = m_unit(ib, m);
+    if (m_half(ib, m)) {
+      sM[head][u][lane] = hl;
+    } else {
+      u32x2* hp = reinterpret_cast<u32x2*>(&sM[head][u][lane]) + (jb & 1);
+      hp[0] = u32x2{hl[0], hl[1]};
+      hp[128] = u32x2{hl[2], hl[3]};  // the lo unit, 64 lanes x 16 bytes further
+    }
   };
 
   auto step = [&](int q, const bf16_t* sBc, const bf16_t* sCc, bf16_t* const (&dn_bc)[2], Decay* dc, Decay* dn) {
@@ -566,7 +606,8 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
                    lds16(sCc + lo.gt[kk & 1] + 16 * ib * kN + 64 * (kk >> 1)), acc);
       return acc;
     };
-    // tiles 0..7 for every head, one per wave (two per wave with four waves)
+    // tiles 0..7 for every head, one per wave (two per wave with four waves); tiles
+    // 8 = (2, 3) and 9 = (3, 3) for the wave's own head
 #pragma unroll
     for (int i = 0; i < 8 / (2 * HB); ++i) {
       const int t = w + 2 * HB * i;
@@ -576,7 +617,6 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
 #pragma unroll
       for (int head = 0; head < HB; ++head) m_tile(gt, t, jb, ib, head, dc, gq, cq);
     }
-    // tiles 8 = (2, 3) and 9 = (3, 3) for the wave's own head
     if (ph == 0) m_tile(gt_tile(2, 3), 8, 2, 3, hh, dc, gq, cq);
     else m_tile(gt_tile(3, 3), 9, 3, 3, hh, dc, gq, cq);
 
@@ -591,16 +631,16 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
       u32x4 sh[2], sl[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const f32x4 a = S[t][2 * kk], b = S[t][2 * kk + 1];
-        sh[t] = u32x4{pk(a[0], a[1]), pk(a[2], a[3]), pk(b[0], b[1]), pk(b[2], b[3])};
-        sl[t] = u32x4{pk(a[0] - lo_f(sh[t][0]), a[1] - hi_f(sh[t][0])), pk(a[2] - lo_f(sh[t][1]), a[3] - hi_f(sh[t][1])),
-                      pk(b[0] - lo_f(sh[t][2]), b[1] - hi_f(sh[t][2])), pk(b[2] - lo_f(sh[t][3]), b[3] - hi_f(sh[t][3]))};
+        const f32x4 a = S[t][kk], b = S[t][kk + 4];
+        const u32x4 sa = split4(a[0], a[1], a[2], a[3]), sb = split4(b[0], b[1], b[2], b[3]);
+        sh[t] = u32x4{sa[0], sa[1], sb[0], sb[1]};
+        sl[t] = u32x4{sa[2], sa[3], sb[2], sb[3]};
       }
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
-        const bf16_t* cb = sCc + 16 * ib * kN + 64 * (kk >> 1);
-        const u32x2 c0 = lds8(cb + lo.cf[kk & 1][0]);
-        const u32x2 c1 = lds8(cb + lo.cf[kk & 1][1]);
+        const bf16_t* cb = sCc + 16 * ib * kN + lo.cf[kk];
+        const u32x2 c0 = lds8(cb);       // n = 16 kk + 4 g ..
+        const u32x2 c1 = lds8(cb + 64);  // n = 16 kk + 64 + 4 g .. (XOR keeps bit 3: +8 units)
         const u32x4 cf = u32x4{c0.x, c0.y, c1.x, c1.y};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -622,7 +662,7 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
     }
     __syncthreads();  // (2) M^T visible; x of chunk q no longer read
 
-    float dtn2 = 0.f;
+    uint32_t dtn2 = 0;
     if (q + 1 < nchunks) {
       load_x<HB>(rows_of(q + 1), nr_of(q + 1), ld, colX, sX, dof, w);
       if (q + 2 < nchunks) dtn2 = dt_of(q + 2);
@@ -634,10 +674,15 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
         if (m <= (ib >> 1)) {
-          const u32x4 t0 = sM[hh][tile_index(2 * m, ib)][lane];
-          const u32x4 t1 = (2 * m + 1 <= ib) ? sM[hh][tile_index(2 * m + 1, ib)][lane] : u32x4{0u, 0u, 0u, 0u};
-          const u32x4 mh = u32x4{t0[0], t0[1], t1[0], t1[1]};
-          const u32x4 ml = u32x4{t0[2], t0[3], t1[2], t1[3]};
+          u32x4 mh, ml;
+          if (m_half(ib, m)) {
+            const u32x4 t0 = sM[hh][m_unit(ib, m)][lane];
+            mh = u32x4{t0[0], t0[1], 0u, 0u};
+            ml = u32x4{t0[2], t0[3], 0u, 0u};
+          } else {
+            mh = sM[hh][m_unit(ib, m)][lane];
+            ml = sM[hh][m_unit(ib, m) + 1][lane];
+          }
 #pragma unroll
           for (int t = 0; t < 2; ++t) {
             Y[t][ib] = mfma(xt[t][m], mh, Y[t][ib]);
@@ -659,7 +704,7 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
 
     // ---- state update ----
     state_update(S, xt, sBc, lo, d, lane);
-    if (q + 1 < nchunks) chunk_decay(dn[hh], dtn, A, bias, nr_of(q + 1), lane, ph, lam, lsum);
+    if (q + 1 < nchunks) chunk_decay(dn[hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
   };
 
