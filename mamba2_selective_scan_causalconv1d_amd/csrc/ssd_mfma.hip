@@ -388,16 +388,15 @@ __device__ __forceinline__ size_t state_elem(int ph, int t, int nb, int lane) {
 
 // ---------------------------------------------------------------- segment states
 
+// Two heads per workgroup fit two workgroups per CU (LDS and registers), four heads one.
 template <int HB>
-__global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __restrict__ xbc,
-                                                                const bf16_t* __restrict__ dt,
-                                                                const float* __restrict__ a_log,
-                                                                const float* __restrict__ dt_bias, SegPtrs sp,
-                                                                int H, int G, int nitems) {
-  __shared__ __attribute__((aligned(16))) bf16_t sB0[kQ * kN];
-  __shared__ __attribute__((aligned(16))) bf16_t sB1[kQ * kN];
-  __shared__ __attribute__((aligned(16))) bf16_t sX0[HB][kQ * kP];
-  __shared__ __attribute__((aligned(16))) bf16_t sX1[HB][kQ * kP];
+__global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_state_kernel(const bf16_t* __restrict__ xbc,
+                                                                             const bf16_t* __restrict__ dt,
+                                                                             const float* __restrict__ a_log,
+                                                                             const float* __restrict__ dt_bias,
+                                                                             SegPtrs sp, int H, int G, int nitems) {
+  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sX[2][HB][kQ * kP];
   __shared__ __attribute__((aligned(16))) Decay sD[2][HB];
 
   const int nhg = H / HB;
@@ -418,12 +417,15 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __
   const int nchunks = (si.z + kQ - 1) / kQ;
   const Lofs lo = lane_offsets(lane, ph);
   const DmaOfs dof = dma_offsets(lane, w, ld);
-  bf16_t* const dB0[1] = {sB0};
-  bf16_t* const dB1[1] = {sB1};
 
   auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
   auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
   auto dt_of = [&](int q) { return dt_bits(dt, si.y + q * kQ, nr_of(q), H, h, lane); };
+  auto load = [&](int q) {
+    bf16_t* const dst[1] = {sB[q & 1]};
+    load_bc<HB, 1>(rows_of(q), nr_of(q), ld, colB, dst, dof, w);
+    load_x<HB>(rows_of(q), nr_of(q), ld, colX, sX[q & 1], dof, w);
+  };
 
   f32x4 S[2][8];
 #pragma unroll
@@ -432,35 +434,27 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __
     for (int nb = 0; nb < 8; ++nb) S[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   float lam = 1.f, lsum = 0.f;
-  uint32_t dtn = 0;
-  load_bc<HB, 1>(rows_of(0), nr_of(0), ld, colB, dB0, dof, w);
-  load_x<HB>(rows_of(0), nr_of(0), ld, colX, sX0, dof, w);
+  load(0);
   chunk_decay(sD[0][hh], bf16_to_f32(dt_of(0)), A, bias, nr_of(0), lane, ph, lam, lsum);
-  if (nchunks > 1) dtn = dt_of(1);
+  uint32_t dtn = nchunks > 1 ? dt_of(1) : 0u;
 
-  auto step = [&](int q, const bf16_t* sBc, bf16_t (*sXc)[kQ * kP], bf16_t* const (&dBn)[1],
-                  bf16_t (*sXn)[kQ * kP], Decay* dc, Decay* dn) {
+  for (int q = 0; q < nchunks; ++q) {
+    const int st = q & 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // chunk q rows and decay visible; chunk q-1 done with the other stage
     uint32_t dtn2 = 0;
     if (q + 1 < nchunks) {
-      load_bc<HB, 1>(rows_of(q + 1), nr_of(q + 1), ld, colB, dBn, dof, w);
-      load_x<HB>(rows_of(q + 1), nr_of(q + 1), ld, colX, sXn, dof, w);
+      load(q + 1);
       if (q + 2 < nchunks) dtn2 = dt_of(q + 2);
     }
     u32x4 xt[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sXc[hh] + lo.xt[t], m);
-    state_update(S, xt, sBc, lo, dc[hh], lane);
-    if (q + 1 < nchunks) chunk_decay(dn[hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
+      for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sX[st][hh] + lo.xt[t], m);
+    state_update(S, xt, sB[st], lo, sD[st][hh], lane);
+    if (q + 1 < nchunks) chunk_decay(sD[st ^ 1][hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
-  };
-
-  for (int q = 0; q < nchunks; q += 2) {
-    step(q, sB0, sX0, dB1, sX1, sD[0], sD[1]);
-    if (q + 1 < nchunks) step(q + 1, sB1, sX1, dB0, sX0, sD[1], sD[0]);
   }
 
   const float lam_end = uniformf(sD[(nchunks - 1) & 1][hh].lam_next);
@@ -476,15 +470,16 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_state_kernel(const bf16_t* __
 
 // ---------------------------------------------------------------- outputs
 
+// Per chunk: (1) tiles and decay visible -> phase 1: x^T operands, G^T tiles and M^T of the
+// workgroup's heads, Y = S C^T, the state update; (2) M^T visible, tiles free -> copies of
+// the next chunk, phase 2: Y += x^T M^T, row scales, store, next chunk's decay.
 template <int HB>
-__global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
+__global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
     bf16_t* __restrict__ y, const bf16_t* __restrict__ xbc, const bf16_t* __restrict__ dt,
     const float* __restrict__ a_log, const float* __restrict__ dt_bias, const float* __restrict__ Dp,
     float* __restrict__ pool, const int32_t* __restrict__ slots, SegPtrs sp, int H, int G, int nitems) {
-  __shared__ __attribute__((aligned(16))) bf16_t sB0[kQ * kN];
-  __shared__ __attribute__((aligned(16))) bf16_t sB1[kQ * kN];
-  __shared__ __attribute__((aligned(16))) bf16_t sC0[kQ * kN];
-  __shared__ __attribute__((aligned(16))) bf16_t sC1[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sC[kQ * kN];
   __shared__ __attribute__((aligned(16))) bf16_t sX[HB][kQ * kP];
   __shared__ __attribute__((aligned(16))) u32x4 sM[HB][kTiles][64];
   __shared__ __attribute__((aligned(16))) Decay sD[2][HB];
@@ -512,12 +507,15 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
   const Lofs lo = lane_offsets(lane, ph);
   const DmaOfs dof = dma_offsets(lane, w, ld);
   const uint32_t yvoff = 2u * ((uint32_t)c * (uint32_t)Di + 4u * (uint32_t)g);
-  bf16_t* const dBC0[2] = {sB0, sC0};
-  bf16_t* const dBC1[2] = {sB1, sC1};
+  bf16_t* const dBC[2] = {sB, sC};
 
   auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
   auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
   auto dt_of = [&](int q) { return dt_bits(dt, si.y + q * kQ, nr_of(q), H, h, lane); };
+  auto load = [&](int q) {
+    load_bc<HB, 2>(rows_of(q), nr_of(q), ld, colBC, dBC, dof, w);
+    load_x<HB>(rows_of(q), nr_of(q), ld, colX, sX, dof, w);
+  };
 
   // the state entering the segment (written by the pass kernel), frame scale 1
   f32x4 S[2][8];
@@ -530,16 +528,14 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
   }
 
   float lam = 1.f, lsum = 0.f;
-  uint32_t dtn = 0;
-  load_bc<HB, 2>(rows_of(0), nr_of(0), ld, colBC, dBC0, dof, w);
-  load_x<HB>(rows_of(0), nr_of(0), ld, colX, sX, dof, w);
+  load(0);
   chunk_decay(sD[0][hh], bf16_to_f32(dt_of(0)), A, bias, nr_of(0), lane, ph, lam, lsum);
-  if (nchunks > 1) dtn = dt_of(1);
+  uint32_t dtn = nchunks > 1 ? dt_of(1) : 0u;
 
   // M^T tile t = (jb, ib) of head `head` from the G^T tile, in operand order, hi and lo;
   // D sits on the diagonal (divided by the row scale when that is applied afterwards).
   // gq, cq: the lane's g and c, recomputed per chunk (see opaque).
-  auto m_tile = [&](const f32x4& gt, int t, int jb, int ib, int head, const Decay* dc, int gq, int cq) {
+  auto m_tile = [&](const f32x4& gt, int jb, int ib, int head, const Decay* dc, int gq, int cq) {
     const Decay& d = dc[head];
     float v[4];
     if (uniform(d.exact)) {
@@ -583,15 +579,15 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
     }
   };
 
-  auto step = [&](int q, const bf16_t* sBc, const bf16_t* sCc, bf16_t* const (&dn_bc)[2], Decay* dc, Decay* dn) {
+  for (int q = 0; q < nchunks; ++q) {
     const int r0 = si.y + q * kQ;
     const int nr = nr_of(q);
+    const Decay* dc = sD[q & 1];
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // (1) chunk q rows and decay visible; chunk q-1 done with x, M, the other stage
-    if (q + 1 < nchunks) load_bc<HB, 2>(rows_of(q + 1), nr_of(q + 1), ld, colBC, dn_bc, dof, w);
+    __syncthreads();  // (1) chunk q tiles and decay visible; chunk q-1 done with M
     const int gq = opaque(g), cq = opaque(c);
 
-    // ---- phase 1: x operands; G^T tiles and M^T for the workgroup's heads; S C^T ----
+    // ---- phase 1: x operands; G^T tiles and M^T for the workgroup's heads; S C^T; state ----
     u32x4 xt[2][2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -602,8 +598,8 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = mfma(lds16(sBc + lo.gt[kk & 1] + 16 * jb * kN + 64 * (kk >> 1)),
-                   lds16(sCc + lo.gt[kk & 1] + 16 * ib * kN + 64 * (kk >> 1)), acc);
+        acc = mfma(lds16(sB + lo.gt[kk & 1] + 16 * jb * kN + 64 * (kk >> 1)),
+                   lds16(sC + lo.gt[kk & 1] + 16 * ib * kN + 64 * (kk >> 1)), acc);
       return acc;
     };
     // tiles 0..7 for every head, one per wave (two per wave with four waves); tiles
@@ -615,10 +611,10 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
       const int jb = t - ib * (ib + 1) / 2;
       const f32x4 gt = gt_tile(jb, ib);
 #pragma unroll
-      for (int head = 0; head < HB; ++head) m_tile(gt, t, jb, ib, head, dc, gq, cq);
+      for (int head = 0; head < HB; ++head) m_tile(gt, jb, ib, head, dc, gq, cq);
     }
-    if (ph == 0) m_tile(gt_tile(2, 3), 8, 2, 3, hh, dc, gq, cq);
-    else m_tile(gt_tile(3, 3), 9, 3, 3, hh, dc, gq, cq);
+    if (ph == 0) m_tile(gt_tile(2, 3), 2, 3, hh, dc, gq, cq);
+    else m_tile(gt_tile(3, 3), 3, 3, hh, dc, gq, cq);
 
     // Y^T(pb, ib) = S C^T, the state operand split from the accumulators
     f32x4 Y[2][4];
@@ -638,7 +634,7 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
       }
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
-        const bf16_t* cb = sCc + 16 * ib * kN + lo.cf[kk];
+        const bf16_t* cb = sC + 16 * ib * kN + lo.cf[kk];
         const u32x2 c0 = lds8(cb);       // n = 16 kk + 4 g ..
         const u32x2 c1 = lds8(cb + 64);  // n = 16 kk + 64 + 4 g .. (XOR keeps bit 3: +8 units)
         const u32x4 cf = u32x4{c0.x, c0.y, c1.x, c1.y};
@@ -660,11 +656,12 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
 #pragma unroll
         for (int ib = 0; ib < 4; ++ib) Y[t][ib] *= ei[ib];
     }
-    __syncthreads();  // (2) M^T visible; x of chunk q no longer read
+    state_update(S, xt, sB, lo, d, lane);
+    __syncthreads();  // (2) M^T visible; the tiles of chunk q no longer read
 
     uint32_t dtn2 = 0;
     if (q + 1 < nchunks) {
-      load_x<HB>(rows_of(q + 1), nr_of(q + 1), ld, colX, sX, dof, w);
+      load(q + 1);
       if (q + 2 < nchunks) dtn2 = dt_of(q + 2);
     }
 
@@ -701,16 +698,8 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
         bst8(yr, yvoff, 2u * (uint32_t)(h * kP + 32 * ph + 16 * t), u32x2{pk(o[0], o[1]), pk(o[2], o[3])});
       }
     }
-
-    // ---- state update ----
-    state_update(S, xt, sBc, lo, d, lane);
-    if (q + 1 < nchunks) chunk_decay(dn[hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
+    if (q + 1 < nchunks) chunk_decay(sD[(q + 1) & 1][hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
-  };
-
-  for (int q = 0; q < nchunks; q += 2) {
-    step(q, sB0, sC0, dBC1, sD[0], sD[1]);
-    if (q + 1 < nchunks) step(q + 1, sB1, sC1, dBC0, sD[1], sD[0]);
   }
   if (last) {
     const float lam_end = uniformf(sD[(nchunks - 1) & 1][hh].lam_next);
@@ -724,7 +713,7 @@ __global__ __launch_bounds__(128 * HB, 1) void ssd_scan_kernel(
   }
 }
 
-int heads_per_block(const mamba2_dims& d) { return (d.nheads / d.ngroups) % 4 == 0 ? 4 : 2; }
+int heads_per_block(const mamba2_dims& d) { (void)d; return 2; }
 
 }  // namespace
 
@@ -736,11 +725,11 @@ bool scan_mfma_supported(const mamba2_dims* d) {
          (d->nheads / d->ngroups) % 2 == 0 && Dc * kQ * 2 < ((int64_t)1 << 31);
 }
 
-// Segment length for the MFMA path: aim at three workgroups per CU (one resident at a
-// time on each of 256 CUs), 64..4096 rows per segment.
+// Segment length for the MFMA path: aim at three rounds of workgroups (two resident per CU
+// on each of 256 CUs), 64..4096 rows per segment.
 int32_t scan_mfma_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims* d) {
   const int64_t groups = d->nheads / heads_per_block(*d);
-  const int64_t target = 3 * 256;
+  const int64_t target = 3 * 512;
   int64_t L = ((int64_t)rb->num_rows * groups + target - 1) / target;
   L = (L + kQ - 1) / kQ * kQ;
   if (L < kQ) L = kQ;
