@@ -8,15 +8,13 @@
 //   y_i  = exp(cs_i) C_i . S + sum_{j<=i} G_ij exp(cs_i - cs_j) dt'_j x_j + D x_i
 //   S'   = exp(cs_63) S + sum_j exp(cs_63 - cs_j) dt'_j x_j (x) B_j
 //
-// Two rewritings keep the element-wise work small:
-//  * State frame.  The state is carried as S = lam * Sh.  The chunk decay then folds into
-//    per-row weights (y's row scale exp(cs_i) lam, the update weights
-//    exp(cs_63 - cs_j) dt'_j / lam'), and Sh is only rescaled when lam' = lam exp(cs_63)
-//    drops below 2^-20 (then Sh <- lam' Sh, lam' <- 1).
-//  * Factored intra-chunk weights.  While the chunk's log-decay span -cs_63 is at most 40,
-//    exp(cs_i - cs_j) = exp(cs_i) exp(-cs_j): y_i = exp(cs_i) lam [C_i . Sh + sum_j G_ij
-//    f_j x_j] with f_j = exp(-cs_j) dt'_j / lam, so the masked matrix M = G o f needs one
-//    multiply per element.  Wider spans use exp(cs_i - cs_j) per element.
+// The state is carried in a frame, S = lam * Sh: the chunk decay then folds into per-row
+// weights (y's row scale exp(cs_i) lam, the update weights exp(cs_63 - cs_j) dt'_j / lam'),
+// and Sh is only rescaled when lam' = lam exp(cs_63) drops below 2^-20 (Sh <- lam' Sh,
+// lam' <- 1), or restarted from zero when the chunk decays by more than e^-60 (the carried
+// state's share is then below fp32 resolution).  Intra-chunk weights exp(cs_i - cs_j) are
+// per element on the diagonal 16 x 16 blocks and exp(cs_i - cs_b) exp(cs_b - cs_j), b the
+// last row of j's block (both factors at most 1), off the diagonal.
 //
 // Contractions run on v_mfma_f32_16x16x32_bf16 (fp32 accumulate).  x, B and C are exact in
 // bf16; M, Sh and w o x are fp32 values split into bf16 hi + lo halves (two MFMAs each): y
@@ -52,7 +50,6 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 constexpr int kP = 64;   // head dim
 constexpr int kN = 128;  // state dim
 constexpr int kQ = 64;   // chunk rows
-constexpr float kSpanMax = 40.f;       // largest log-decay span with factored weights
 constexpr float kFrameMin = 0x1p-20f;  // smallest state-frame scale before a rescale
 constexpr float kDropSpan = 60.f;      // a chunk decaying by more than e^-60 drops the carried state
 constexpr int kTiles = 10;             // lower-triangular 16 x 16 tiles of a 64 x 64 chunk
@@ -60,15 +57,14 @@ constexpr int kTiles = 10;             // lower-triangular 16 x 16 tiles of a 64
 // Per-chunk decay quantities of one head (written by the head's two waves, read by all).
 struct Decay {
   float e[kQ];      // exp(cs_i) lam
-  float f[kQ];      // factored: exp(-cs_j) dt'_j / lam; exact: dt'_j
+  float dt[kQ];     // dt'_j
   float cs[kQ];     // cs_i
   float w[kQ];      // exp(cs_63 - cs_j) dt'_j / lam'
-  float ef[kQ];     // exact: exp(cs_b - cs_j) dt'_j, b the last row of j's 16-row block
-  float er[3][kQ];  // exact: exp(cs_i - cs_b), b = 16 jb + 15, for rows i past block jb
+  float ef[kQ];     // exp(cs_b - cs_j) dt'_j, b the last row of j's 16-row block
+  float er[3][kQ];  // exp(cs_i - cs_b), b = 16 jb + 15, for rows i past block jb
   float scale;      // state factor before this chunk's update: 1 keep, 0 drop, else rescale
-  int exact;        // 1: intra-chunk weights without the exp(cs_i) exp(-cs_j) factoring
   float lam_next;   // lam'
-  float pad;
+  float pad[2];
 };
 
 struct SegPtrs {
@@ -246,37 +242,32 @@ __device__ __forceinline__ int work_item(int b, int n) {
 // ------------------------------------------------------------------ per-chunk pieces
 
 // Decay quantities of one head for a chunk (lane = chunk row, v = raw dt).  Both waves of
-// the head compute dt' and the prefix sums; half 0 writes the row scales and intra-chunk
-// weights, half 1 the update weights and the scalars.  lam is the frame scale entering the
-// chunk; it and lsum (sum of chunk log-decays) advance in both waves.
+// the head compute dt' and the prefix sums; half 0 writes the row scales and the diagonal
+// weights, half 1 the update and off-diagonal weights and the scalars.  lam is the frame
+// scale entering the chunk; it and lsum (sum of chunk log-decays) advance in both waves.
 __device__ __forceinline__ void chunk_decay(Decay& d, float v, float A, float bias, int nr, int lane, int ph,
                                             float& lam, float& lsum) {
   const float dtp = lane < nr ? softplus_f32(v + bias) : 0.f;
   const float cs = wave_scan_incl(-A * dtp);
   const float cend = lane_value(cs, 63);
-  const bool exact = -cend > kSpanMax;
   const float tent = lam * __expf(cend);
   const bool reset = tent < kFrameMin;
   const float lam_next = reset ? 1.f : tent;
+  const float b0 = lane_value(cs, 15), b1 = lane_value(cs, 31), b2 = lane_value(cs, 47);
   if (ph == 0) {
     d.e[lane] = __expf(cs) * lam;
-    d.f[lane] = exact ? dtp : __expf(-cs) * dtp * __builtin_amdgcn_rcpf(lam);
+    d.dt[lane] = dtp;
     d.cs[lane] = cs;
-    if (exact) {
-#pragma unroll
-      for (int jb = 0; jb < 3; ++jb) d.er[jb][lane] = __expf(cs - lane_value(cs, 16 * jb + 15));
-    }
+    d.er[0][lane] = __expf(cs - b0);
+    d.er[1][lane] = __expf(cs - b1);
+    d.er[2][lane] = __expf(cs - b2);
   } else {
     d.w[lane] = __expf(cend - cs) * dtp * __builtin_amdgcn_rcpf(lam_next);
-    if (exact) {
-      const int r = lane >> 4;
-      const float b0 = lane_value(cs, 15), b1 = lane_value(cs, 31), b2 = lane_value(cs, 47);
-      const float cb = r == 0 ? b0 : r == 1 ? b1 : r == 2 ? b2 : cend;
-      d.ef[lane] = __expf(cb - cs) * dtp;
-    }
+    const int r = lane >> 4;
+    const float cb = r == 0 ? b0 : r == 1 ? b1 : r == 2 ? b2 : cend;
+    d.ef[lane] = __expf(cb - cs) * dtp;
     if (lane == 0) {
       d.scale = -cend > kDropSpan ? 0.f : (reset ? tent : 1.f);
-      d.exact = exact ? 1 : 0;
       d.lam_next = lam_next;
     }
   }
@@ -532,40 +523,24 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
   chunk_decay(sD[0][hh], bf16_to_f32(dt_of(0)), A, bias, nr_of(0), lane, ph, lam, lsum);
   uint32_t dtn = nchunks > 1 ? dt_of(1) : 0u;
 
-  // M^T tile t = (jb, ib) of head `head` from the G^T tile, in operand order, hi and lo;
-  // D sits on the diagonal (divided by the row scale when that is applied afterwards).
-  // gq, cq: the lane's g and c, recomputed per chunk (see opaque).
+  // M^T tile (jb, ib) of head `head` from the G^T tile, in operand order, hi and lo, with D
+  // on the diagonal.  gq, cq: the lane's g and c, recomputed per chunk (see opaque).
   auto m_tile = [&](const f32x4& gt, int jb, int ib, int head, const Decay* dc, int gq, int cq) {
     const Decay& d = dc[head];
     float v[4];
-    if (uniform(d.exact)) {
-      if (jb < ib) {
-        const f32x4 ef = *reinterpret_cast<const f32x4*>(&d.ef[16 * jb + 4 * gq]);
-        const float er = d.er[jb][16 * ib + cq];
+    if (jb < ib) {
+      const f32x4 ef = *reinterpret_cast<const f32x4*>(&d.ef[16 * jb + 4 * gq]);
+      const float er = d.er[jb][16 * ib + cq];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = gt[r] * (ef[r] * er);
-      } else {
-        const float csi = d.cs[16 * ib + cq];
-        const f32x4 csj = *reinterpret_cast<const f32x4*>(&d.cs[16 * jb + 4 * gq]);
-        const f32x4 dtj = *reinterpret_cast<const f32x4*>(&d.f[16 * jb + 4 * gq]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = 4 * gq + r == cq ? Dh[head] : 0.f;
-          v[r] = 4 * gq + r > cq ? 0.f : fmaf(gt[r], __expf(csi - csj[r]) * dtj[r], e);
-        }
-      }
+      for (int r = 0; r < 4; ++r) v[r] = gt[r] * (ef[r] * er);
     } else {
-      const f32x4 fj = *reinterpret_cast<const f32x4*>(&d.f[16 * jb + 4 * gq]);
-      if (jb < ib) {
+      const float csi = d.cs[16 * ib + cq];
+      const f32x4 csj = *reinterpret_cast<const f32x4*>(&d.cs[16 * jb + 4 * gq]);
+      const f32x4 dtj = *reinterpret_cast<const f32x4*>(&d.dt[16 * jb + 4 * gq]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = gt[r] * fj[r];
-      } else {
-        const float dd = Dh[head] * __builtin_amdgcn_rcpf(d.e[16 * ib + cq]);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float e = 4 * gq + r == cq ? dd : 0.f;
-          v[r] = 4 * gq + r > cq ? 0.f : fmaf(gt[r], fj[r], e);
-        }
+      for (int r = 0; r < 4; ++r) {
+        const float e = 4 * gq + r == cq ? Dh[head] : 0.f;
+        v[r] = 4 * gq + r > cq ? 0.f : fmaf(gt[r], __expf(csi - csj[r]) * dtj[r], e);
       }
     }
     const u32x4 hl = split4(v[0], v[1], v[2], v[3]);
@@ -616,7 +591,8 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
     if (ph == 0) m_tile(gt_tile(2, 3), 2, 3, hh, dc, gq, cq);
     else m_tile(gt_tile(3, 3), 3, 3, hh, dc, gq, cq);
 
-    // Y^T(pb, ib) = S C^T, the state operand split from the accumulators
+    // Y^T(pb, ib) = S C^T, the state operand split from the accumulators; then the update
+    const Decay& d = dc[hh];
     f32x4 Y[2][4];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
@@ -635,8 +611,8 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
         const bf16_t* cb = sC + 16 * ib * kN + lo.cf[kk];
-        const u32x2 c0 = lds8(cb);       // n = 16 kk + 4 g ..
-        const u32x2 c1 = lds8(cb + 64);  // n = 16 kk + 64 + 4 g .. (XOR keeps bit 3: +8 units)
+        const u32x2 c0 = lds8(cb);
+        const u32x2 c1 = lds8(cb + 64);
         const u32x4 cf = u32x4{c0.x, c0.y, c1.x, c1.y};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
@@ -645,18 +621,14 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
         }
       }
     }
-    const Decay& d = dc[hh];
-    const bool exact = uniform(d.exact) != 0;
+    state_update(S, xt, sB, lo, d, lane);
     float ei[4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) ei[ib] = d.e[16 * ib + cq];
-    if (exact) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int ib = 0; ib < 4; ++ib) Y[t][ib] *= ei[ib];
-    }
-    state_update(S, xt, sB, lo, d, lane);
+      for (int ib = 0; ib < 4; ++ib) Y[t][ib] *= ei[ib];
     __syncthreads();  // (2) M^T visible; the tiles of chunk q no longer read
 
     uint32_t dtn2 = 0;
@@ -694,7 +666,7 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
       const Rsrc yr = make_rsrc(y + (size_t)(r0 + 16 * ib) * Di, ((int64_t)nr - 16 * ib) * Di * 2);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const f32x4 o = exact ? Y[t][ib] : Y[t][ib] * ei[ib];
+        const f32x4 o = Y[t][ib];
         bst8(yr, yvoff, 2u * (uint32_t)(h * kP + 32 * ph + 16 * t), u32x2{pk(o[0], o[1]), pk(o[2], o[3])});
       }
     }
