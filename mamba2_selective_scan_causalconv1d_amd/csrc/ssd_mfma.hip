@@ -134,8 +134,7 @@ __device__ __forceinline__ void bst8(Rsrc r, uint32_t voff, uint32_t soff, u32x2
 typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is set here and used by nothing else
-__device__ __forceinline__ void dma16(const void* base, int64_t bytes, const bf16_t* lds, uint32_t voff,
-                                      uint32_t soff) {
+__device__ __forceinline__ void dma16(const char* base, int bytes, const bf16_t* lds, uint32_t voff, uint32_t soff) {
   const uint64_t a = (uint64_t)base;
   const u32x4s rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes <= 0 ? 0u : (uint32_t)bytes, 0x00020000u};
   const uint32_t m0 = (uint32_t)(uintptr_t)(const M2_LDS void*)lds;
@@ -294,29 +293,32 @@ __device__ __forceinline__ DmaOfs dma_offsets(int lane, int w, uint32_t ld) {
 // (4 rows of a [64][128] B or C tile, 8 rows of a [64][64] x tile), each lane fetching the
 // global 16-byte unit that the swizzle places at its LDS slot; rows past nr read as zero.
 // Instructions are dealt round robin to the 2 HB waves.
+// rows: the chunk's first row; nrb: its valid bytes (rows x row pitch); ldb: row pitch in bytes
 template <int HB, int NT>
-__device__ __forceinline__ void load_bc(const bf16_t* rows, int nr, uint32_t ld, const uint32_t (&col)[NT],
+__device__ __forceinline__ void load_bc(const bf16_t* rows, int nrb, uint32_t ldb, const uint32_t (&col)[NT],
                                         bf16_t* const (&dst)[NT], const DmaOfs& o, int w) {
   constexpr int nW = 2 * HB;
   static_assert(16 % nW == 0, "instruction split");
+  const char* base = reinterpret_cast<const char*>(rows);
 #pragma unroll
   for (int i = 0; i < 16 * NT / nW; ++i) {
     const int tile = nW * i / 16;  // compile time
     const int k = (w + nW * i) & 15;
-    dma16(rows + (size_t)(4 * k) * ld, ((int64_t)nr - 4 * k) * ld * 2, dst[tile] + 512 * k, o.bc,
-          2u * col[tile]);  // k % 2 == w % 2
+    const uint32_t off = (uint32_t)(4 * k) * ldb;
+    dma16(base + off, nrb - (int)off, dst[tile] + 512 * k, o.bc, 2u * col[tile]);  // k % 2 == w % 2
   }
 }
 template <int HB>
-__device__ __forceinline__ void load_x(const bf16_t* rows, int nr, uint32_t ld, uint32_t colX,
+__device__ __forceinline__ void load_x(const bf16_t* rows, int nrb, uint32_t ldb, uint32_t colX,
                                        bf16_t (*sX)[kQ * kP], const DmaOfs& o, int w) {
   constexpr int nW = 2 * HB;
+  const char* base = reinterpret_cast<const char*>(rows);
 #pragma unroll
   for (int i = 0; i < 8 * HB / nW; ++i) {
     const int t = w + nW * i;
     const int hh = t >> 3, k = t & 7;
-    dma16(rows + (size_t)(8 * k) * ld, ((int64_t)nr - 8 * k) * ld * 2, sX[hh] + 512 * k, o.x,
-          2u * (colX + (uint32_t)(hh * kP)));
+    const uint32_t off = (uint32_t)(8 * k) * ldb;
+    dma16(base + off, nrb - (int)off, sX[hh] + 512 * k, o.x, 2u * (colX + (uint32_t)(hh * kP)));
   }
 }
 
@@ -414,8 +416,9 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_state_kernel(co
   auto dt_of = [&](int q) { return dt_bits(dt, si.y + q * kQ, nr_of(q), H, h, lane); };
   auto load = [&](int q) {
     bf16_t* const dst[1] = {sB[q & 1]};
-    load_bc<HB, 1>(rows_of(q), nr_of(q), ld, colB, dst, dof, w);
-    load_x<HB>(rows_of(q), nr_of(q), ld, colX, sX[q & 1], dof, w);
+    const int nrb = nr_of(q) * (int)ld * 2;
+    load_bc<HB, 1>(rows_of(q), nrb, 2u * ld, colB, dst, dof, w);
+    load_x<HB>(rows_of(q), nrb, 2u * ld, colX, sX[q & 1], dof, w);
   };
 
   f32x4 S[2][8];
@@ -504,8 +507,9 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
   auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
   auto dt_of = [&](int q) { return dt_bits(dt, si.y + q * kQ, nr_of(q), H, h, lane); };
   auto load = [&](int q) {
-    load_bc<HB, 2>(rows_of(q), nr_of(q), ld, colBC, dBC, dof, w);
-    load_x<HB>(rows_of(q), nr_of(q), ld, colX, sX, dof, w);
+    const int nrb = nr_of(q) * (int)ld * 2;
+    load_bc<HB, 2>(rows_of(q), nrb, 2u * ld, colBC, dBC, dof, w);
+    load_x<HB>(rows_of(q), nrb, 2u * ld, colX, sX, dof, w);
   };
 
   // the state entering the segment (written by the pass kernel), frame scale 1
