@@ -446,7 +446,9 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_state_kernel(co
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sX[st][hh] + lo.xt[t], m);
+    __builtin_amdgcn_s_setprio(1);
     state_update(S, xt, sB[st], lo, sD[st][hh], lane);
+    __builtin_amdgcn_s_setprio(0);
     if (q + 1 < nchunks) chunk_decay(sD[st ^ 1][hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
   }
@@ -595,7 +597,10 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
     if (ph == 0) m_tile(gt_tile(2, 3), 2, 3, hh, dc, gq, cq);
     else m_tile(gt_tile(3, 3), 3, 3, hh, dc, gq, cq);
 
-    // Y^T(pb, ib) = S C^T, the state operand split from the accumulators; then the update
+    // Y^T(pb, ib) = S C^T, the state operand split from the accumulators; then the update.
+    // The MFMA-heavy stretch runs at raised wave priority so that the SIMD's other wave fills
+    // the matrix core's gaps with its vector work rather than the reverse.
+    __builtin_amdgcn_s_setprio(1);
     const Decay& d = dc[hh];
     f32x4 Y[2][4];
 #pragma unroll
@@ -626,6 +631,7 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
       }
     }
     state_update(S, xt, sB, lo, d, lane);
+    __builtin_amdgcn_s_setprio(0);
     float ei[4];
 #pragma unroll
     for (int ib = 0; ib < 4; ++ib) ei[ib] = d.e[16 * ib + cq];
