@@ -7,8 +7,10 @@ activations, fp32 states.  ``value`` is prefill tokens/s.  The decode half of th
 timed on the batched-decode workload (256 one-row requests on a 512-slot pool, 64
 successive steps of conv + decode scan + norm) and reported as ``decode_us_per_step``.
 
-Inputs are seeded synthetic tensors resident in HBM before the timed region.  Per-kernel
-durations come from HIP events the library records on the launch stream; the roofline
+Inputs are seeded synthetic tensors resident in HBM before the timed region, and 40 warm-up
+steps let the clocks settle first.  Per-kernel durations come from HIP events the library
+records on the launch stream around every launch, in a second pass of the same steps (the
+events cost a few us per launch, so they stay out of the timed pass); the roofline
 object uses the dominant kernel's algorithmic bytes (or flops) per launch over its average
 duration.  The CPU oracle is timed on a bounded sample on the host cores as a reported
 baseline.  Prints ONE JSON line.
@@ -16,6 +18,7 @@ baseline.  Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -24,6 +27,9 @@ import time
 import numpy as np
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+ROOT = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(ROOT, "mamba2_selective_scan_causalconv1d_amd", "csrc")
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic_long_prefill_4x16384.txt")
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 
 
@@ -31,7 +37,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="prefill only (for counter runs)")
@@ -59,6 +65,31 @@ def kernel_bytes_flops(name, wl, nrows):
     if name == "scan_decode":
         return (T * (Dc + H + Di) * a + (S + resumed) * H * P * N * 4), 6 * T * H * P * N
     return None, None
+
+
+def sources_sha1(names):
+    h = hashlib.sha1()
+    for n in names:
+        with open(os.path.join(CSRC, n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the counter table (FETCH_SIZE / WRITE_SIZE runs),
+    or None when the table has no entry or the kernel's sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_TABLE):
+        return None
+    for line in open(TRAFFIC_TABLE):
+        if not line.startswith("kernel="):
+            continue
+        kv = dict(f.split("=", 1) for f in line.split())
+        if kv["kernel"] != kernel:
+            continue
+        if sources_sha1(kv["sources"].split(",")) != kv["sha1"]:
+            return None
+        return float(kv["bytes"])
+    return None
 
 
 def main():
@@ -103,6 +134,7 @@ def main():
     torch.cuda.synchronize()
     ref_digest = (float(out.float().sum().item()), float(y.float().abs().sum().item()))
 
+    # warm-up long enough for the clocks to settle (~40 ms of steps), then the timed steps
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -116,13 +148,16 @@ def main():
     digest = (float(out.float().sum().item()), float(y.float().abs().sum().item()))
     assert digest == ref_digest, "timed output differs from the parity run: %s vs %s" % (digest, ref_digest)
 
-    # per-kernel durations (HIP events recorded by the library on the launch stream)
+    # per-kernel durations: the same K steps again, with the library's HIP events recorded on
+    # the launch stream around every kernel (they add a few us per launch, hence a pass of
+    # their own)
     ops.timing_enable(64 * max(1, args.steps))
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     recs = ops.timing_collect(64 * max(1, args.steps))
     ops.timing_enable(0)
+
     per = {}
     for name, ms in recs:
         per.setdefault(name, []).append(ms)
@@ -144,7 +179,7 @@ def main():
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
     dr = rooflines.get(dom, {})
     roofline = {"kernel": dom, "bound": "hbm", "achieved": dr.get("achieved_GBs"), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": dr.get("frac_hbm"), "traffic": None,
+                "unit": "GB/s", "frac": dr.get("frac_hbm"), "traffic": measured_traffic(dom),
                 "avg_us": kernels[dom]["avg_us"]}
 
     if args.copy_calibration_mb:
@@ -236,6 +271,7 @@ def run_decode(args, torch, ops, W, dev, e0, e1):
         times.append(e0.elapsed_time(e1))
         assert float(dout.float().sum().item()) == dref
     decode_us = 1e3 * float(np.median(times)) / len(dsteps)
+    # per-kernel durations: one more run with the library's HIP events around every launch
     cpool.copy_(pristine_conv)
     spool.copy_(pristine_ssm)
     ops.timing_enable(4096)
