@@ -29,6 +29,10 @@
  *   - Layout: row-major, last index contiguous.  An xBC row is
  *     [x (H*P, head h at h*P+p) | B (G*N, group g at g*N+n) | C (G*N)],
  *     Dc = H*P + 2*G*N channels; Di = H*P.
+ *   - Alignment: dst, x/xbc, z, the state pools and the conv/norm weight and
+ *     bias vectors must be 16-byte aligned (the kernels move them in 16-byte
+ *     units), else MAMBA2_INVALID_ARGUMENT; dt, a_log, dt_bias and d need only
+ *     their element alignment.
  *   - Types: activations, conv state and outputs in the activation type
  *     (MAMBA2_DTYPE_F32 or MAMBA2_DTYPE_BF16; bf16 as its 16 raw bits); SSM
  *     state, weights, biases, A_log, dt_bias and D are fp32.
@@ -140,6 +144,9 @@ size_t mamba2_scan_prefill_workspace_bytes(const mamba2_recurrent_batch* rb,
  * One-row decode step of the same recurrence (every run length must be 1):
  * each sequence's fp32 state is read once from its slot (not at all when fresh)
  * and written back once.  Arguments as mamba2_scan_prefill, no workspace.
+ * Needs d_state % 4 == 0 with d_state / 4 a power of two <= 64, and
+ * headdim * d_state / 4 a multiple of 512, equal to 256, or below 256 and a
+ * multiple of 64 (whole 64-lane wavefronts), else MAMBA2_NOT_IMPLEMENTED.
  */
 mamba2_status mamba2_scan_decode(void* dst, const void* xbc, const void* dt, const float* a_log,
                                  const float* dt_bias, const float* d, float* ssm_state,

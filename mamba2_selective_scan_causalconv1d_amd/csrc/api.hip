@@ -4,6 +4,7 @@
 // nothing is written.  The library allocates no device memory and never
 // synchronises the host with the stream.
 #include <algorithm>
+#include <initializer_list>
 #include <vector>
 
 #include "common.h"
@@ -53,6 +54,13 @@ mamba2_status check_batch(const mamba2_recurrent_batch* rb, const mamba2_dims* d
   return MAMBA2_OK;
 }
 
+// The kernels move activations, states and weight vectors in 16-byte units.
+bool aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (((uintptr_t)p & 15) != 0) return false;
+  return true;
+}
+
 mamba2_status check_all(const mamba2_recurrent_batch* rb, const mamba2_dims* d, bool decode) {
   mamba2_status st = check_dims(d);
   if (st != MAMBA2_OK) return st;
@@ -86,6 +94,7 @@ mamba2_status mamba2_conv1d(void* dst, const void* x, const float* weight, const
   if (st != MAMBA2_OK) return st;
   if (!rb) return MAMBA2_INVALID_ARGUMENT;
   if (rb->num_rows > 0 && (!dst || !x || !weight || !bias || !conv_state)) return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({dst, x, weight, bias, conv_state})) return MAMBA2_INVALID_ARGUMENT;
   st = check_batch(rb, dims, false);
   if (st != MAMBA2_OK) return st;
   const int64_t Dc = (int64_t)dims->nheads * dims->headdim + 2 * (int64_t)dims->ngroups * dims->d_state;
@@ -111,6 +120,7 @@ mamba2_status mamba2_scan_prefill(void* dst, const void* xbc, const void* dt, co
   if (!rb) return MAMBA2_INVALID_ARGUMENT;
   if (rb->num_rows > 0 && (!dst || !xbc || !dt || !a_log || !dt_bias || !d || !ssm_state))
     return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({dst, xbc, ssm_state})) return MAMBA2_INVALID_ARGUMENT;
   st = check_batch(rb, dims, false);
   if (st != MAMBA2_OK) return st;
   if (!scan_supported(dims)) return MAMBA2_NOT_IMPLEMENTED;
@@ -132,9 +142,10 @@ mamba2_status mamba2_scan_decode(void* dst, const void* xbc, const void* dt, con
   if (!rb) return MAMBA2_INVALID_ARGUMENT;
   if (rb->num_rows > 0 && (!dst || !xbc || !dt || !a_log || !dt_bias || !d || !ssm_state))
     return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({dst, xbc, ssm_state})) return MAMBA2_INVALID_ARGUMENT;
   st = check_batch(rb, dims, true);
   if (st != MAMBA2_OK) return st;
-  if (!decode_supported(*dims)) return MAMBA2_NOT_IMPLEMENTED;
+  if (!decode_supported(*dims) || !decode_grid_fits(*dims, rb->num_seqs)) return MAMBA2_NOT_IMPLEMENTED;
   if (rb->num_rows == 0) return MAMBA2_OK;
   return from_hip(launch_scan_decode(dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims,
                                      (hipStream_t)stream));
@@ -147,6 +158,7 @@ mamba2_status mamba2_gated_rmsnorm(void* dst, const void* x, const void* z, cons
   if (act_dtype != MAMBA2_DTYPE_F32 && act_dtype != MAMBA2_DTYPE_BF16) return MAMBA2_INVALID_ARGUMENT;
   if (!(eps >= 0.f) || eps == __builtin_inff()) return MAMBA2_INVALID_ARGUMENT;
   if (rows > 0 && (!dst || !x || !z || !weight)) return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({dst, x, z, weight})) return MAMBA2_INVALID_ARGUMENT;
   if ((int64_t)rows * d_inner >= ((int64_t)1 << 40)) return MAMBA2_INVALID_ARGUMENT;
   if ((d_inner / groups) % act_vec(act_dtype) != 0) return MAMBA2_NOT_IMPLEMENTED;
   if (rows == 0) return MAMBA2_OK;

@@ -8,7 +8,8 @@
 // Mapping: one thread owns one 16-byte channel vector (8 bf16 / 4 fp32 channels)
 // of a tile of R consecutive packed rows and slides a K-tap window down them in
 // registers; a wavefront covers 64 consecutive vectors of a row, so every row
-// access is a contiguous 1 KiB.
+// access is a contiguous 1 KiB.  A batch with one row per sequence (a decode step)
+// takes a separate kernel that maps thread -> (row, vector) directly.
 //
 // Slot ownership: the first K-1 rows of a sequence (its "head", the rows that read
 // history) are processed by the tile that holds the sequence's first row, even
@@ -91,12 +92,22 @@ __global__ __launch_bounds__(256) void conv1d_silu_kernel(
 #pragma unroll
       for (int r = 0; r < H1; ++r) Act<T>::unpack(raw[r], win[r]);
       const int L = en - st0;
+      // new state row r = win[L + r]: history rows shifted up by L (constant indices
+      // only, so raw stays in registers), then rows of the sequence
       uint4 nst[H1];
+#pragma unroll
+      for (int r = 0; r < H1; ++r) nst[r] = raw[r];
+#pragma unroll
+      for (int step = 0; step < H1; ++step) {
+        if (step < L) {
+#pragma unroll
+          for (int r = 0; r + 1 < H1; ++r) nst[r] = nst[r + 1];
+        }
+      }
 #pragma unroll
       for (int r = 0; r < H1; ++r) {
         const int idx = L + r;  // position in win = history ++ rows
-        nst[r] = idx < H1 ? raw[idx]
-                          : *reinterpret_cast<const uint4*>(x + (size_t)(st0 + idx - H1) * Dc + col);
+        if (idx >= H1) nst[r] = *reinterpret_cast<const uint4*>(x + (size_t)(st0 + idx - H1) * Dc + col);
       }
 #pragma unroll
       for (int r = 0; r < H1; ++r)
@@ -151,11 +162,79 @@ __global__ __launch_bounds__(256) void conv1d_silu_kernel(
   }
 }
 
+// Every sequence one row (a decode step: S == T, so row r is sequence r): one thread per
+// 16-byte channel vector of a row.  The slot's K-1 rows and the new row are read
+// together, the output is the window's dot product, and the slot is rewritten shifted
+// by one row.  No sequence lookup, so the only dependent load is the slot index.
+template <typename T, int K>
+__global__ __launch_bounds__(256) void conv1d_silu_step_kernel(
+    T* __restrict__ dst, const T* __restrict__ x, const float* __restrict__ w,
+    const float* __restrict__ b, T* __restrict__ conv_state, const int32_t* __restrict__ slots,
+    const uint8_t* __restrict__ fresh, int S, int Dc) {
+  constexpr int V = Act<T>::kVec;
+  constexpr int H1 = K - 1;
+  const int NV = Dc / V;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)S * NV) return;
+  const int r = (int)(gid / NV);
+  const size_t col = (size_t)(gid % NV) * V;
+  uint4 raw[K];
+  raw[H1] = *reinterpret_cast<const uint4*>(x + (size_t)r * Dc + col);
+  const size_t sbase = (size_t)slots[r] * H1 * Dc + col;
+#pragma unroll
+  for (int i = 0; i < H1; ++i) raw[i] = make_uint4(0, 0, 0, 0);
+  if (!fresh[r]) {  // a fresh sequence never reads its slot
+#pragma unroll
+    for (int i = 0; i < H1; ++i) raw[i] = *reinterpret_cast<const uint4*>(conv_state + sbase + (size_t)i * Dc);
+  }
+  // weights of this thread's channels: V * K contiguous floats starting at col * K
+  float wr[V * K];
+  const float4* wp = reinterpret_cast<const float4*>(w + col * K);
+#pragma unroll
+  for (int i = 0; i < V * K / 4; ++i) {
+    const float4 t4 = wp[i];
+    wr[4 * i] = t4.x;
+    wr[4 * i + 1] = t4.y;
+    wr[4 * i + 2] = t4.z;
+    wr[4 * i + 3] = t4.w;
+  }
+  float br[V];
+  const float4* bp = reinterpret_cast<const float4*>(b + col);
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) {
+    const float4 t4 = bp[i];
+    br[4 * i] = t4.x;
+    br[4 * i + 1] = t4.y;
+    br[4 * i + 2] = t4.z;
+    br[4 * i + 3] = t4.w;
+  }
+#pragma unroll
+  for (int i = 0; i < H1; ++i) *reinterpret_cast<uint4*>(conv_state + sbase + (size_t)i * Dc) = raw[i + 1];
+  float win[K][V];
+#pragma unroll
+  for (int k = 0; k < K; ++k) Act<T>::unpack(raw[k], win[k]);
+  float out[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    float pre = br[i];
+#pragma unroll
+    for (int k = 0; k < K; ++k) pre = fmaf(wr[i * K + k], win[k][i], pre);
+    out[i] = silu_f32(pre);
+  }
+  *reinterpret_cast<uint4*>(dst + (size_t)r * Dc + col) = Act<T>::pack(out);
+}
+
 template <typename T, int K>
 hipError_t launch_t(void* dst, const void* x, const float* w, const float* b, void* cs,
                     const BatchDev& bd, int32_t Dc, hipStream_t st) {
   constexpr int V = Act<T>::kVec;
   const int NV = Dc / V;
+  if (bd.num_rows == bd.num_seqs) {
+    const int64_t n = (int64_t)bd.num_seqs * NV;
+    M2_LAUNCH("conv1d_silu", (conv1d_silu_step_kernel<T, K>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
+              st, (T*)dst, (const T*)x, w, b, (T*)cs, bd.slots, bd.fresh, bd.num_seqs, Dc);
+    return hipSuccess;
+  }
   const int64_t work = (int64_t)bd.num_rows * NV;
   // rows per thread: enough threads to fill the chip (~512K), at most 32 rows each
   int R = (int)((work + 524287) / 524288);

@@ -8,7 +8,9 @@
 // written once: a streaming HBM-bound kernel).  Each group owns a contiguous run of
 // L = 64 / groups lanes, and its 16-byte vectors are dealt to those lanes round robin,
 // so every load instruction touches whole 128-byte lines and the group's sum of squares
-// is an xor-shuffle over L lanes.  Shapes that do not fit (groups not dividing 64, rows
+// is an xor-shuffle over L lanes.  Four rows per workgroup; a launch of fewer than 4096
+// rows (a decode step) uses one-wave workgroups and loads the weights before the
+// reduction.  Shapes that do not fit (groups not dividing 64, rows
 // not a multiple of 64 vectors) use the unit kernel: one wavefront per (row, group).
 #include "common.h"
 
@@ -107,7 +109,9 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_wide_kernel(T* __restrict__
   }
 }
 
-template <typename T, int NVPL>
+// kEarlyW: load the weight vectors before the row's reduction, so a short launch (few
+// rows, one pass per wave) waits on one round of loads instead of two.
+template <typename T, int NVPL, bool kEarlyW>
 __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ dst, const T* __restrict__ x,
                                                                 const T* __restrict__ z,
                                                                 const float* __restrict__ w, int lanes_per_group,
@@ -121,6 +125,23 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ 
   const int jl = lane & (lanes_per_group - 1);    // its place in the group's lanes
   const int gv = NVPL * lanes_per_group;          // vectors per group
   const size_t base = (size_t)row * Di;
+  float wf[NVPL][V];
+  auto load_w = [&](int k) {
+    const int vi = q * gv + jl + lanes_per_group * k;
+    const float4* wp = reinterpret_cast<const float4*>(w + (size_t)vi * V);
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+      const float4 t4 = wp[i];
+      wf[k][4 * i] = t4.x;
+      wf[k][4 * i + 1] = t4.y;
+      wf[k][4 * i + 2] = t4.z;
+      wf[k][4 * i + 3] = t4.w;
+    }
+  };
+  if (kEarlyW) {
+#pragma unroll
+    for (int k = 0; k < NVPL; ++k) load_w(k);
+  }
   float g[NVPL][V];
   float ss = 0.f;
 #pragma unroll
@@ -140,19 +161,10 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ 
 #pragma unroll
   for (int k = 0; k < NVPL; ++k) {
     const int vi = q * gv + jl + lanes_per_group * k;
-    const float4* wp = reinterpret_cast<const float4*>(w + (size_t)vi * V);
-    float wf[V];
-#pragma unroll
-    for (int i = 0; i < V / 4; ++i) {
-      const float4 t4 = wp[i];
-      wf[4 * i] = t4.x;
-      wf[4 * i + 1] = t4.y;
-      wf[4 * i + 2] = t4.z;
-      wf[4 * i + 3] = t4.w;
-    }
+    if (!kEarlyW) load_w(k);
     float out[V];
 #pragma unroll
-    for (int i = 0; i < V; ++i) out[i] = g[k][i] * inv * wf[i];
+    for (int i = 0; i < V; ++i) out[i] = g[k][i] * inv * wf[k][i];
     *reinterpret_cast<uint4*>(dst + base + (size_t)vi * V) = Act<T>::pack(out);
   }
 }
@@ -163,9 +175,16 @@ hipError_t launch_row(void* dst, const void* x, const void* z, const float* w, i
   const int lpg = 64 / groups;
   int log2_lpg = 0;
   while ((1 << log2_lpg) < lpg) ++log2_lpg;
+  const float inv_gs = 1.f / (float)(Di / groups);
+  if (rows < 4096) {
+    // few rows (a decode step): one wave per workgroup, weights loaded up front
+    M2_LAUNCH("gated_rmsnorm", (gated_rmsnorm_row_kernel<T, NVPL, true>), dim3((unsigned)rows), dim3(64), 0, st,
+              (T*)dst, (const T*)x, (const T*)z, w, lpg, log2_lpg, eps, inv_gs, rows, Di);
+    return hipSuccess;
+  }
   const dim3 grid((unsigned)((rows + 3) / 4));
-  M2_LAUNCH("gated_rmsnorm", (gated_rmsnorm_row_kernel<T, NVPL>), grid, dim3(256), 0, st, (T*)dst, (const T*)x,
-            (const T*)z, w, lpg, log2_lpg, eps, 1.f / (float)(Di / groups), rows, Di);
+  M2_LAUNCH("gated_rmsnorm", (gated_rmsnorm_row_kernel<T, NVPL, false>), grid, dim3(256), 0, st, (T*)dst,
+            (const T*)x, (const T*)z, w, lpg, log2_lpg, eps, inv_gs, rows, Di);
   return hipSuccess;
 }
 

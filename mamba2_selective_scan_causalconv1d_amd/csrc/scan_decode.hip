@@ -7,16 +7,22 @@
 // head h reading B and C of group h / (H / G); a fresh sequence starts from zero and
 // never reads its slot.
 //
-// Mapping: one workgroup per (sequence, head).  The head's fp32 state [P][N] is
-// streamed once in and once out with 16-byte accesses; consecutive threads take
-// consecutive float4s, so each wave instruction touches 1 KiB of contiguous state.
-// A thread keeps the same four state columns for every row it visits, so its B and
-// C values are loaded once; the row sums of h * C are reduced over the N/4 lanes
-// that share a row.  This is an HBM-streaming kernel (~0.75 flop per byte).
+// Mapping: the head's fp32 state [P][N] is cut into blocks of whole rows, one
+// workgroup per (sequence, head, block); for P = 64, N = 128 a block is 16 rows
+// (8 KiB), two float4s per thread.  The state is streamed once in and once out with
+// 16-byte non-temporal accesses (it is not reused within the step, and keeping it out
+// of the caches leaves them to the step's small operands); consecutive threads take
+// consecutive float4s.  A thread keeps the same four state columns for every row it
+// visits, so its B and C values are loaded once; the row sums of h * C are reduced
+// over the N/4 lanes that share a row.  Small blocks with few loads per thread keep
+// many workgroups in flight, which is what this HBM-streaming kernel (~0.75 flop per
+// byte) needs.
 #include "common.h"
 
 namespace m2 {
 namespace {
+
+typedef float f4v __attribute__((ext_vector_type(4)));
 
 template <typename T>
 __device__ __forceinline__ void load4(const T* p, float* f);
@@ -39,15 +45,19 @@ __device__ __forceinline__ void load4<bf16_t>(const bf16_t* p, float* f) {
   f[3] = bf16_to_f32(v.y >> 16);
 }
 
-// KP float4s per thread; Q4 = N / 4 lanes share a state row (Q4 divides 64).
+// KP float4s per thread; workgroup (r * H + h) * nblk + blk covers KP * blockDim.x
+// float4s (block blk) of head h's state of sequence r; Q4 = N / 4 lanes share a state
+// row (Q4 divides 64).
 template <typename T, int KP>
 __global__ __launch_bounds__(256) void scan_decode_kernel(
     T* __restrict__ y, const T* __restrict__ xbc, const T* __restrict__ dt,
     const float* __restrict__ a_log, const float* __restrict__ dt_bias,
     const float* __restrict__ Dp, float* __restrict__ pool, const int32_t* __restrict__ slots,
-    const uint8_t* __restrict__ fresh, int H, int P, int N, int G) {
-  const int h = blockIdx.x;
-  const int r = blockIdx.y;
+    const uint8_t* __restrict__ fresh, int H, int P, int N, int G, int nblk) {
+  const int hb = blockIdx.x % (H * nblk);
+  const int r = blockIdx.x / (H * nblk);
+  const int h = hb / nblk;
+  const int blk = hb - h * nblk;
   const int tid = threadIdx.x;
   const int nthr = blockDim.x;
   const int Q4 = N >> 2;
@@ -55,31 +65,33 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(
   const size_t Dc = (size_t)Di + 2 * (size_t)G * N;
   const int g = h / (H / G);
   const T* row = xbc + (size_t)r * Dc;
+  const int f0 = blk * KP * nthr;  // first float4 of the block within the head
 
   const float v = Act<T>::load(dt + (size_t)r * H + h) + dt_bias[h];
-  const float dtp = softplus_f32(v);
-  const float dA = __expf(-__expf(a_log[h]) * dtp);
   const int n0 = 4 * (tid % Q4);
   float Bv[4], Cv[4];
   load4<T>(row + Di + (size_t)g * N + n0, Bv);
   load4<T>(row + Di + (size_t)G * N + (size_t)g * N + n0, Cv);
 
-  float4* st = reinterpret_cast<float4*>(pool + ((size_t)slots[r] * H + h) * (size_t)P * N);
-  float4 hv[KP];
+  f4v* st = reinterpret_cast<f4v*>(pool + ((size_t)slots[r] * H + h) * (size_t)P * N) + f0;
+  f4v hv[KP];
   if (fresh[r]) {
 #pragma unroll
-    for (int k = 0; k < KP; ++k) hv[k] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < KP; ++k) hv[k] = f4v{0.f, 0.f, 0.f, 0.f};
   } else {
 #pragma unroll
-    for (int k = 0; k < KP; ++k) hv[k] = st[k * nthr + tid];
+    for (int k = 0; k < KP; ++k) hv[k] = __builtin_nontemporal_load(st + k * nthr + tid);
   }
-  float part[KP], xs[KP];
+  float xs[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) xs[k] = Act<T>::load(row + (size_t)h * P + (f0 + k * nthr + tid) / Q4);
+  const float dtp = softplus_f32(v);
+  const float dA = __expf(-__expf(a_log[h]) * dtp);
+  float part[KP];
 #pragma unroll
   for (int k = 0; k < KP; ++k) {
-    const int p = (k * nthr + tid) / Q4;
-    xs[k] = Act<T>::load(row + (size_t)h * P + p);
     const float c = dtp * xs[k];
-    float4 s = hv[k];
+    f4v s = hv[k];
     s.x = fmaf(c, Bv[0], s.x * dA);
     s.y = fmaf(c, Bv[1], s.y * dA);
     s.z = fmaf(c, Bv[2], s.z * dA);
@@ -88,7 +100,7 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(
     part[k] = fmaf(s.x, Cv[0], fmaf(s.y, Cv[1], fmaf(s.z, Cv[2], s.w * Cv[3])));
   }
 #pragma unroll
-  for (int k = 0; k < KP; ++k) st[k * nthr + tid] = hv[k];
+  for (int k = 0; k < KP; ++k) __builtin_nontemporal_store(hv[k], st + k * nthr + tid);
 #pragma unroll
   for (int k = 0; k < KP; ++k) {
     float s = part[k];
@@ -99,53 +111,61 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(
     const float d = Dp[h];
 #pragma unroll
     for (int k = 0; k < KP; ++k) {
-      const int p = (k * nthr + tid) / Q4;
+      const int p = (f0 + k * nthr + tid) / Q4;
       Act<T>::store(y + (size_t)r * Di + (size_t)h * P + p, fmaf(d, xs[k], part[k]));
     }
   }
+}
+
+// Block shape: 512 float4s (two per thread) when the head's state is a multiple of
+// that, else the whole head in one workgroup (f4 = 256: one per thread; f4 < 256: f4
+// threads, one each).
+struct DecodeShape {
+  int nthr, kp, nblk;
+};
+
+DecodeShape decode_shape(const mamba2_dims& dm) {
+  const int64_t f4 = (int64_t)dm.headdim * (dm.d_state / 4);  // float4s per head state
+  if (f4 % 512 == 0) return DecodeShape{256, 2, (int)(f4 / 512)};
+  return DecodeShape{(int)f4, 1, 1};
 }
 
 template <typename T>
 hipError_t launch_t(void* y, const void* xbc, const void* dt, const float* a_log,
                     const float* dt_bias, const float* D, float* pool, const BatchDev& bd,
                     const mamba2_dims& dm, hipStream_t st) {
-  const int Q4 = dm.d_state / 4;
-  const int64_t f4 = (int64_t)dm.headdim * Q4;  // float4s per head state
-  const int nthr = (int)(f4 < 256 ? f4 : 256);
-  const int KP = (int)(f4 / nthr);
-  const dim3 grid((unsigned)dm.nheads, (unsigned)bd.num_seqs);
-#define M2_DEC(kp)                                                                           \
-  case kp:                                                                                   \
-    M2_LAUNCH("scan_decode", (scan_decode_kernel<T, kp>), grid, dim3(nthr), 0, st, (T*)y,   \
-              (const T*)xbc, (const T*)dt, a_log, dt_bias, D, pool, bd.slots, bd.fresh,       \
-              dm.nheads, dm.headdim, dm.d_state, dm.ngroups);                                \
-    return hipSuccess;
-  switch (KP) {
-    M2_DEC(1)
-    M2_DEC(2)
-    M2_DEC(4)
-    M2_DEC(8)
-    M2_DEC(16)
+  const DecodeShape sh = decode_shape(dm);
+  const dim3 grid((unsigned)((int64_t)bd.num_seqs * dm.nheads * sh.nblk));
+  if (sh.kp == 2) {
+    M2_LAUNCH("scan_decode", (scan_decode_kernel<T, 2>), grid, dim3(sh.nthr), 0, st, (T*)y, (const T*)xbc,
+              (const T*)dt, a_log, dt_bias, D, pool, bd.slots, bd.fresh, dm.nheads, dm.headdim, dm.d_state,
+              dm.ngroups, sh.nblk);
+  } else {
+    M2_LAUNCH("scan_decode", (scan_decode_kernel<T, 1>), grid, dim3(sh.nthr), 0, st, (T*)y, (const T*)xbc,
+              (const T*)dt, a_log, dt_bias, D, pool, bd.slots, bd.fresh, dm.nheads, dm.headdim, dm.d_state,
+              dm.ngroups, sh.nblk);
   }
-#undef M2_DEC
-  return hipErrorInvalidValue;
+  return hipSuccess;
 }
 
 }  // namespace
 
-// Shapes the decode kernel covers: N % 4 == 0 with N/4 a power of two <= 64, and
-// P*N/4 either < 256 and a multiple of 64, or a multiple of 256 with at most 16
-// float4s per thread.
+// Shapes the decode kernel covers: N % 4 == 0 with N/4 a power of two <= 64 (a state
+// row's lanes lie in one wavefront), and P*N/4 float4s per head either a multiple of
+// 512, exactly 256, or below 256 and a multiple of 64 (whole wavefronts).
 bool decode_supported(const mamba2_dims& dm) {
   const int N = dm.d_state;
   if (N % 4 != 0) return false;
   const int Q4 = N / 4;
   if (Q4 > 64 || (Q4 & (Q4 - 1)) != 0) return false;
   const int64_t f4 = (int64_t)dm.headdim * Q4;
-  if (f4 < 256) return f4 % 64 == 0;
-  if (f4 % 256 != 0) return false;
-  const int64_t kp = f4 / 256;
-  return kp == 1 || kp == 2 || kp == 4 || kp == 8 || kp == 16;
+  return f4 % 512 == 0 || f4 == 256 || (f4 < 256 && f4 % 64 == 0);
+}
+
+// The launch is one-dimensional: S * H * blocks workgroups, under 2^32 work-items.
+bool decode_grid_fits(const mamba2_dims& dm, int32_t num_seqs) {
+  const DecodeShape sh = decode_shape(dm);
+  return (int64_t)num_seqs * dm.nheads * sh.nblk * sh.nthr < ((int64_t)1 << 32);
 }
 
 hipError_t launch_scan_decode(void* y, const void* xbc, const void* dt, const float* a_log,

@@ -104,6 +104,16 @@ def test_entry_points_reject_before_launch(ops):
     L = ops.LIB
     # null pointers
     assert L.mamba2_conv1d(None, p, p, p, p, b.ref(), ctypes.byref(d), None) == _lib.INVALID_ARGUMENT
+    # device buffers moved in 16-byte units must be 16-byte aligned
+    assert p % 16 == 0
+    q = p + 4
+    assert L.mamba2_conv1d(p, q, p, p, p, b.ref(), ctypes.byref(d), None) == _lib.INVALID_ARGUMENT
+    assert L.mamba2_conv1d(p, p, p, p, q, b.ref(), ctypes.byref(d), None) == _lib.INVALID_ARGUMENT
+    assert L.mamba2_scan_prefill(p, q, p, p, p, p, p, b.ref(), ctypes.byref(d), p, 1 << 20, None) == \
+        _lib.INVALID_ARGUMENT
+    assert L.mamba2_scan_prefill(p, p, p, p, p, p, q, b.ref(), ctypes.byref(d), p, 1 << 20, None) == \
+        _lib.INVALID_ARGUMENT
+    assert L.mamba2_gated_rmsnorm(p, p, q, p, 2, 1e-5, 4, 64, 1, None) == _lib.INVALID_ARGUMENT
     # bad dims
     bad = _dims(ops, nheads=3)  # not a multiple of ngroups
     assert L.mamba2_validate(b.ref(), ctypes.byref(bad), 0) == _lib.INVALID_ARGUMENT

@@ -158,6 +158,57 @@ def test_decode_64_steps(gpu):
     _check_pools(wl, wl.slots, gpu.ops.to_host(sp_g), sp_o, gpu.ops.to_host(cp_g), cp_o)
 
 
+DECODE_SHAPES = {
+    # float4s per head state: 64 (one 64-lane workgroup), 256 (one 256-lane workgroup),
+    # 512 (one two-per-thread block), 2048 and 4096 (several blocks per head)
+    "f32_p16n16": W.Shape(nheads=4, headdim=16, d_state=16, ngroups=2, conv_kernel=4, chunk_size=16,
+                          norm_groups=2, pool_slots=10, act="f32"),
+    "p64n16_k3": W.Shape(nheads=4, headdim=64, d_state=16, ngroups=1, conv_kernel=3, chunk_size=16,
+                         norm_groups=1, pool_slots=10, act="bf16"),
+    "p32n64_k2": W.Shape(nheads=6, headdim=32, d_state=64, ngroups=3, conv_kernel=2, chunk_size=16,
+                         norm_groups=3, pool_slots=10, act="bf16"),
+    "f32_p64n128": W.Shape(nheads=4, headdim=64, d_state=128, ngroups=2, conv_kernel=4, chunk_size=16,
+                           norm_groups=4, pool_slots=10, act="f32"),
+    "p128n128": W.Shape(nheads=2, headdim=128, d_state=128, ngroups=1, conv_kernel=4, chunk_size=16,
+                        norm_groups=2, pool_slots=10, act="bf16"),
+}
+
+
+@pytest.mark.parametrize("shape", list(DECODE_SHAPES))
+def test_decode_shapes(gpu, shape):
+    """Three decode steps of 7 one-row sequences (3 fresh on step 0) for each block shape of the
+    decode kernel; every op against the oracle on the same inputs, pools carried by each side."""
+    sh = DECODE_SHAPES[shape]
+    bar = bar_for(sh.act)
+    R = 7
+    wl = W.random_prefill(60, sh, [1] * R, fresh=[1, 0, 0, 1, 0, 1, 0])
+    p = gpu.Params(wl)
+    dims = gpu.dims_of(sh)
+    cp_o, sp_o = wl.conv_pool.copy(), wl.ssm_pool.copy()
+    cp_g, sp_g = gpu.ops.to_device(wl.conv_pool), gpu.ops.to_device(wl.ssm_pool)
+    for step in range(3):
+        src = wl if step == 0 else W.random_prefill(60 + step, sh, [1] * R, fresh=wl.fresh, slots=wl.slots)
+        fresh = wl.fresh if step == 0 else np.zeros_like(wl.fresh)
+        b = gpu.batch_of(wl, fresh=fresh)
+        x = gpu.ops.to_device(src.xbc)
+        xa = torch.empty_like(x)
+        gpu.ops.conv1d(xa, x, p.conv_w, p.conv_b, cp_g, b, dims)
+        y = torch.empty((R, sh.d_inner), dtype=x.dtype, device="cuda")
+        gpu.ops.scan_decode(y, xa, gpu.ops.to_device(src.dt), p.a_log, p.dt_bias, p.D, sp_g, b, dims)
+        out = torch.empty_like(y)
+        gpu.ops.gated_rmsnorm(out, y, gpu.ops.to_device(src.z), p.norm_w, sh.norm_groups, sh.eps)
+        torch.cuda.synchronize()
+        xa_h, y_h, out_h = gpu.ops.to_host(xa), gpu.ops.to_host(y), gpu.ops.to_host(out)
+        xa_o, cp_o = oracle_conv(wl, xbc=src.xbc, conv_pool=cp_o, fresh=fresh, inplace=True)
+        y_o, sp_o = oracle_scan(wl, xa_h, dt=src.dt, ssm_pool=sp_o, fresh=fresh, decode=True, inplace=True)
+        out_o = oracle_norm(wl, y_h, z=src.z)
+        say("  [%s] step %d: conv %.3g, y %.3g, out %.3g of bar" % (
+            shape, step, assert_close(gpu.f32(xa_h), gpu.f32(xa_o), bar, "conv step %d" % step),
+            assert_close(gpu.f32(y_h), gpu.f32(y_o), bar, "y step %d" % step),
+            assert_close(gpu.f32(out_h), gpu.f32(out_o), bar, "out step %d" % step)))
+    _check_pools(wl, wl.slots, gpu.ops.to_host(sp_g), sp_o, gpu.ops.to_host(cp_g), cp_o)
+
+
 # ------------------------------------------------------------ invariants and edge cases
 
 SMALL = W.Shape(nheads=4, headdim=8, d_state=8, ngroups=2, conv_kernel=4, chunk_size=16, norm_groups=2,
