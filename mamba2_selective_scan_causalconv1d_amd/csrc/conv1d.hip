@@ -8,7 +8,8 @@
 // Mapping: one thread owns one 16-byte channel vector (8 bf16 / 4 fp32 channels)
 // of a tile of R consecutive packed rows and slides a K-tap window down them in
 // registers; a wavefront covers 64 consecutive vectors of a row, so every row
-// access is a contiguous 1 KiB.  A batch with one row per sequence (a decode step)
+// access is a contiguous 1 KiB.  Input rows are read with non-temporal loads (each
+// is read once per launch).  A batch with one row per sequence (a decode step)
 // takes a separate kernel that maps thread -> (row, vector) directly.
 //
 // Slot ownership: the first K-1 rows of a sequence (its "head", the rows that read
@@ -33,6 +34,15 @@ __device__ __forceinline__ int seq_of_row(const int32_t* __restrict__ cu, int S,
       hi = mid - 1;
   }
   return lo;
+}
+
+// 16 bytes of input read once by the launch: a non-temporal load, so the stream of rows
+// does not displace cached data (the next kernels' inputs, pending writes).
+template <typename T>
+__device__ __forceinline__ uint4 load_stream(const T* p) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 template <typename T, int K>
@@ -130,7 +140,7 @@ __global__ __launch_bounds__(256) void conv1d_silu_kernel(
       uint4 xv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        xv[j] = j < n ? *reinterpret_cast<const uint4*>(x + (size_t)(t + j) * Dc + col) : make_uint4(0, 0, 0, 0);
+        xv[j] = j < n ? load_stream(x + (size_t)(t + j) * Dc + col) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int j = 0; j < 4; ++j) Act<T>::unpack(xv[j], xf[H1 + j]);
 #pragma unroll

@@ -8,9 +8,9 @@
 // written once: a streaming HBM-bound kernel).  Each group owns a contiguous run of
 // L = 64 / groups lanes, and its 16-byte vectors are dealt to those lanes round robin,
 // so every load instruction touches whole 128-byte lines and the group's sum of squares
-// is an xor-shuffle over L lanes.  Four rows per workgroup; a launch of fewer than 4096
-// rows (a decode step) uses one-wave workgroups and loads the weights before the
-// reduction.  Shapes that do not fit (groups not dividing 64, rows
+// is an xor-shuffle over L lanes.  Four rows per workgroup, rows streamed with
+// non-temporal accesses; a launch of fewer than 4096 rows (a decode step) uses one-wave
+// workgroups and loads the weights before the reduction.  Shapes that do not fit (groups not dividing 64, rows
 // not a multiple of 64 vectors) use the unit kernel: one wavefront per (row, group).
 #include "common.h"
 
@@ -109,9 +109,13 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_wide_kernel(T* __restrict__
   }
 }
 
-// kEarlyW: load the weight vectors before the row's reduction, so a short launch (few
-// rows, one pass per wave) waits on one round of loads instead of two.
-template <typename T, int NVPL, bool kEarlyW>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// kShort: a short launch (few rows, one pass per wave) loads the weight vectors before the
+// row's reduction, so it waits on one round of loads instead of two.  Otherwise the rows
+// are streamed: x, z and dst use non-temporal accesses (each byte is touched once), which
+// keeps the stream from displacing cached data.
+template <typename T, int NVPL, bool kShort>
 __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ dst, const T* __restrict__ x,
                                                                 const T* __restrict__ z,
                                                                 const float* __restrict__ w, int lanes_per_group,
@@ -138,18 +142,23 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ 
       wf[k][4 * i + 3] = t4.w;
     }
   };
-  if (kEarlyW) {
+  if (kShort) {
 #pragma unroll
     for (int k = 0; k < NVPL; ++k) load_w(k);
   }
+  auto load_row = [&](const T* p) -> uint4 {
+    if (kShort) return *reinterpret_cast<const uint4*>(p);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+  };
   float g[NVPL][V];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < NVPL; ++k) {
     const int vi = q * gv + jl + lanes_per_group * k;
     float xf[V], zf[V];
-    Act<T>::unpack(*reinterpret_cast<const uint4*>(x + base + (size_t)vi * V), xf);
-    Act<T>::unpack(*reinterpret_cast<const uint4*>(z + base + (size_t)vi * V), zf);
+    Act<T>::unpack(load_row(x + base + (size_t)vi * V), xf);
+    Act<T>::unpack(load_row(z + base + (size_t)vi * V), zf);
 #pragma unroll
     for (int i = 0; i < V; ++i) {
       g[k][i] = xf[i] * silu_f32(zf[i]);
@@ -161,11 +170,16 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ 
 #pragma unroll
   for (int k = 0; k < NVPL; ++k) {
     const int vi = q * gv + jl + lanes_per_group * k;
-    if (!kEarlyW) load_w(k);
+    if (!kShort) load_w(k);
     float out[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) out[i] = g[k][i] * inv * wf[k][i];
-    *reinterpret_cast<uint4*>(dst + base + (size_t)vi * V) = Act<T>::pack(out);
+    const uint4 pv = Act<T>::pack(out);
+    if (kShort) {
+      *reinterpret_cast<uint4*>(dst + base + (size_t)vi * V) = pv;
+    } else {
+      __builtin_nontemporal_store(u32x4{pv.x, pv.y, pv.z, pv.w}, reinterpret_cast<u32x4*>(dst + base + (size_t)vi * V));
+    }
   }
 }
 
