@@ -72,8 +72,16 @@ struct Act<bf16_t> {
 
 // ------------------------------------------------------------------ math
 
+// log(1 + e) for e >= 0 from the hardware log: with u = fl(1 + e), log(u) * e / (u - 1)
+// cancels the rounding of u (D. Goldberg, "What every computer scientist should know about
+// floating-point arithmetic", 1991, Theorem 4); a few ulp.
+__device__ __forceinline__ float log1p_pos(float e) {
+  const float u = 1.f + e;
+  return u == 1.f ? e : __logf(u) * (e * __builtin_amdgcn_rcpf(u - 1.f));
+}
+
 // softplus without a clamp; above 20 the identity is exact to fp32 precision.
-__device__ __forceinline__ float softplus_f32(float v) { return v > 20.f ? v : log1pf(__expf(v)); }
+__device__ __forceinline__ float softplus_f32(float v) { return v > 20.f ? v : log1p_pos(__expf(v)); }
 
 // silu(v) = v / (1 + e^-v); the reciprocal is the hardware approximation (~1 ulp), far
 // below the bf16 / fp32 output rounding of every op that uses it.

@@ -35,6 +35,8 @@
 // block kk pairs state tiles kk and kk + 4: n = 16 kk + 64 (s / 4) + 4 g + s % 4.
 #include "common.h"
 
+#include <type_traits>
+
 namespace m2 {
 namespace {
 
@@ -274,6 +276,27 @@ __device__ __forceinline__ void chunk_decay(Decay& d, float v, float A, float bi
   lsum += cend;
 }
 
+// The segment-state pass needs only the update weights and the frame scalars: both waves
+// of the head compute them, half 1 writes them.
+__device__ __forceinline__ void chunk_decay_update(Decay& d, float v, float A, float bias, int nr, int lane, int ph,
+                                                   float& lam, float& lsum) {
+  const float dtp = lane < nr ? softplus_f32(v + bias) : 0.f;
+  const float cs = wave_scan_incl(-A * dtp);
+  const float cend = lane_value(cs, 63);
+  const float tent = lam * __expf(cend);
+  const bool reset = tent < kFrameMin;
+  const float lam_next = reset ? 1.f : tent;
+  if (ph == 1) {
+    d.w[lane] = __expf(cend - cs) * dtp * __builtin_amdgcn_rcpf(lam_next);
+    if (lane == 0) {
+      d.scale = -cend > kDropSpan ? 0.f : (reset ? tent : 1.f);
+      d.lam_next = lam_next;
+    }
+  }
+  lam = lam_next;
+  lsum += cend;
+}
+
 // A wave's B / C instructions all have block index k of the wave's parity (see load_bc).
 struct DmaOfs {
   uint32_t bc;  // B / C block rows
@@ -429,7 +452,7 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_state_kernel(co
 
   float lam = 1.f, lsum = 0.f;
   load(0);
-  chunk_decay(sD[0][hh], bf16_to_f32(dt_of(0)), A, bias, nr_of(0), lane, ph, lam, lsum);
+  chunk_decay_update(sD[0][hh], bf16_to_f32(dt_of(0)), A, bias, nr_of(0), lane, ph, lam, lsum);
   uint32_t dtn = nchunks > 1 ? dt_of(1) : 0u;
 
   for (int q = 0; q < nchunks; ++q) {
@@ -449,7 +472,8 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_state_kernel(co
     __builtin_amdgcn_s_setprio(1);
     state_update(S, xt, sB[st], lo, sD[st][hh], lane);
     __builtin_amdgcn_s_setprio(0);
-    if (q + 1 < nchunks) chunk_decay(sD[st ^ 1][hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
+    if (q + 1 < nchunks)
+      chunk_decay_update(sD[st ^ 1][hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
   }
 
@@ -584,23 +608,42 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
       return acc;
     };
     // tiles 0..7 for every head, one per wave (two per wave with four waves); tiles
-    // 8 = (2, 3) and 9 = (3, 3) for the wave's own head
+    // 8 = (2, 3) and 9 = (3, 3) for the wave's own head.  Instantiated per wave index, so
+    // every tile position and weight form is fixed at compile time (one uniform branch).
+    auto wave_tiles = [&](auto wc) {
+      constexpr int W = decltype(wc)::value;
 #pragma unroll
-    for (int i = 0; i < 8 / (2 * HB); ++i) {
-      const int t = w + 2 * HB * i;
-      const int ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-      const int jb = t - ib * (ib + 1) / 2;
-      const f32x4 gt = gt_tile(jb, ib);
+      for (int i = 0; i < 8 / (2 * HB); ++i) {
+        const int t = W + 2 * HB * i;
+        const int ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+        const int jb = t - ib * (ib + 1) / 2;
+        const f32x4 gt = gt_tile(jb, ib);
 #pragma unroll
-      for (int head = 0; head < HB; ++head) m_tile(gt, jb, ib, head, dc, gq, cq);
+        for (int head = 0; head < HB; ++head) m_tile(gt, jb, ib, head, dc, gq, cq);
+      }
+      if ((W & 1) == 0) m_tile(gt_tile(2, 3), 2, 3, W >> 1, dc, gq, cq);
+      else m_tile(gt_tile(3, 3), 3, 3, W >> 1, dc, gq, cq);
+    };
+    static_assert(2 * HB <= 8, "wave dispatch");
+    auto wave_case = [&](auto wc) {
+      if constexpr (decltype(wc)::value < 2 * HB) wave_tiles(wc);
+    };
+    switch (w) {
+      case 0: wave_case(std::integral_constant<int, 0>{}); break;
+      case 1: wave_case(std::integral_constant<int, 1>{}); break;
+      case 2: wave_case(std::integral_constant<int, 2>{}); break;
+      case 3: wave_case(std::integral_constant<int, 3>{}); break;
+      case 4: wave_case(std::integral_constant<int, 4>{}); break;
+      case 5: wave_case(std::integral_constant<int, 5>{}); break;
+      case 6: wave_case(std::integral_constant<int, 6>{}); break;
+      default: wave_case(std::integral_constant<int, 7>{}); break;
     }
-    if (ph == 0) m_tile(gt_tile(2, 3), 2, 3, hh, dc, gq, cq);
-    else m_tile(gt_tile(3, 3), 3, 3, hh, dc, gq, cq);
 
     // Y^T(pb, ib) = S C^T, the state operand split from the accumulators; then the update.
     // The MFMA-heavy stretch runs at raised wave priority so that the SIMD's other wave fills
     // the matrix core's gaps with its vector work rather than the reverse.
     __builtin_amdgcn_s_setprio(1);
+    __builtin_amdgcn_iglp_opt(1);  // interleave the splits' vector work with the MFMAs
     const Decay& d = dc[hh];
     f32x4 Y[2][4];
 #pragma unroll
