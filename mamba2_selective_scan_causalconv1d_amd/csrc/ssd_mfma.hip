@@ -147,11 +147,18 @@ __device__ __forceinline__ void dma16(const char* base, int bytes, const bf16_t*
 }
 #pragma clang diagnostic pop
 
-// XOR swizzle of 16-byte units within a tile row: four consecutive rows (transposing
-// reads) and eight consecutive rows (row reads) land on distinct bank groups.  It depends
-// on row % 8 only, and every access below keeps the XOR inside per-lane bits so that the
-// loop indices stay additive (immediate offsets on a few per-lane bases).
-__device__ __forceinline__ int swz(int row) { return ((row & 3) << 1) | ((row >> 2) & 1); }
+// XOR swizzles of 16-byte units within tile rows, linear in the bits of row % 16.  B and C
+// tiles (256-byte rows, 16 units) use a 4-bit map and x tiles (128-byte rows, 8 units) a
+// 3-bit one; both were chosen by timing every such map on the reads below (row reads of 16
+// consecutive rows, 8-byte fragment reads, transposing reads of 4-row groups), which then
+// run without bank conflicts.  Offsets that cross into the other half of a B / C row flip
+// unit bit 3 (element offset bit 6), so they are applied with XOR, not addition.
+__device__ __forceinline__ int swz_bc(int row) {
+  return ((row & 1) ? 3 : 0) ^ ((row & 2) ? 6 : 0) ^ ((row & 4) ? 8 : 0) ^ ((row & 8) ? 12 : 0);
+}
+__device__ __forceinline__ int swz_x(int row) {
+  return ((row & 1) ? 4 : 0) ^ ((row & 2) ? 5 : 0) ^ ((row & 4) ? 6 : 0) ^ ((row & 8) ? 4 : 0);
+}
 
 template <typename T>
 __device__ __forceinline__ u32x4 lds16(const T* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -168,29 +175,23 @@ __device__ __forceinline__ u32x2 tr8(const bf16_t* p) {
 // Per-lane element offsets into the swizzled tiles (B and C: [64][128], x: [64][64]).
 // Lane (c, g) = (lane % 16, lane / 16); q = (lane % 16) / 4, b = (lane % 4) / 2.
 struct Lofs {
-  int gt[2];     // B / C row 16 jb + c, elements 32 kk + 8 g..: + 16 jb*128 + 64 (kk/2), [kk%2]
-  int cf[4];     // C row 16 ib + c, elements 16 kk + 4 g.. (and + 64): + 16 ib*128, [kk]
-  int bt[4];     // B^T transposing read for column block nb: + row0*128 + 64 (nb/4), [nb%4]
-  int xt[2];     // x^T transposing read for p block 32 ph + 16 t: + row0*64, [t]
-  int xd[2];     // x row 16 ib + c, elements 32 ph + 16 t + 4 g..: + 16 ib*64, [t]
+  int gt[2];  // B / C row 16 jb + c, elements 32 kk + 8 g..: + 16 jb*128, [kk%2], ^ 64 (kk/2)
+  int cf[4];  // C row 16 ib + c, elements 16 kk + 4 g.. (and ^ 64): + 16 ib*128, [kk]
+  int bt[4];  // B^T transposing read for column block nb: + row0*128, [nb%4], ^ 64 (nb/4)
+  int xt[2];  // x^T transposing read for p block 32 ph + 16 t: + row0*64, [t]
 };
 __device__ __forceinline__ Lofs lane_offsets(int lane, int ph) {
   const int g = lane >> 4, c = lane & 15, q = (lane & 15) >> 2, b = (lane & 3) >> 1, e = 4 * (lane & 1);
-  const int sc = swz(c), sq = swz(4 * g + q);
+  const int sc = swz_bc(c), sq = swz_bc(4 * g + q), sx = swz_x(4 * g + q);
   Lofs o;
 #pragma unroll
-  for (int a = 0; a < 2; ++a) {
-    o.gt[a] = c * kN + (((4 * a + g) ^ sc) << 3);
-  }
+  for (int a = 0; a < 2; ++a) o.gt[a] = c * kN + (((4 * a + g) ^ sc) << 3);
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) o.cf[kk] = c * kN + (((2 * kk + (g >> 1)) ^ sc) << 3) + 4 * (g & 1);
 #pragma unroll
   for (int nb = 0; nb < 4; ++nb) o.bt[nb] = (4 * g + q) * kN + (((2 * nb + b) ^ sq) << 3) + e;
 #pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    o.xt[t] = (4 * g + q) * kP + (((4 * ph + 2 * t + b) ^ sq) << 3) + e;
-    o.xd[t] = c * kP + (((4 * ph + 2 * t + (g >> 1)) ^ sc) << 3) + 4 * (g & 1);
-  }
+  for (int t = 0; t < 2; ++t) o.xt[t] = (4 * g + q) * kP + (((4 * ph + 2 * t + b) ^ sx) << 3) + e;
   return o;
 }
 
@@ -297,18 +298,18 @@ __device__ __forceinline__ void chunk_decay_update(Decay& d, float v, float A, f
   lsum += cend;
 }
 
-// A wave's B / C instructions all have block index k of the wave's parity (see load_bc).
+// A wave's B / C copy instructions all have block index k = w (mod 4) and its x copies
+// k = w (mod 2) (see load_bc, load_x), so one lane offset per wave serves each kind.
 struct DmaOfs {
   uint32_t bc;  // B / C block rows
   uint32_t x;   // x block rows
 };
 __device__ __forceinline__ DmaOfs dma_offsets(int lane, int w, uint32_t ld) {
   DmaOfs o;
-  const int r = lane >> 4;
-  // swz(4 k + r) = 2 r | (k % 2)
-  o.bc = 2u * ((uint32_t)r * ld + 8u * (uint32_t)((lane & 15) ^ (2 * r + (w & 1))));
-  const int rx = lane >> 3;
-  o.x = 2u * ((uint32_t)rx * ld + 8u * (uint32_t)((lane & 7) ^ swz(rx)));
+  const int r = lane >> 4;  // row 4 k + r of the tile, unit lane % 16
+  o.bc = 2u * ((uint32_t)r * ld + 8u * (uint32_t)((lane & 15) ^ swz_bc(4 * (w & 3) + r)));
+  const int rx = lane >> 3;  // row 8 k + rx, unit lane % 8
+  o.x = 2u * ((uint32_t)rx * ld + 8u * (uint32_t)((lane & 7) ^ swz_x(8 * (w & 1) + rx)));
   return o;
 }
 
@@ -328,7 +329,7 @@ __device__ __forceinline__ void load_bc(const bf16_t* rows, int nrb, uint32_t ld
     const int tile = nW * i / 16;  // compile time
     const int k = (w + nW * i) & 15;
     const uint32_t off = (uint32_t)(4 * k) * ldb;
-    dma16(base + off, nrb - (int)off, dst[tile] + 512 * k, o.bc, 2u * col[tile]);  // k % 2 == w % 2
+    dma16(base + off, nrb - (int)off, dst[tile] + 512 * k, o.bc, 2u * col[tile]);  // k % 4 == w % 4
   }
 }
 template <int HB>
@@ -364,7 +365,7 @@ __device__ __forceinline__ void su_mfma(f32x4 (&S)[2][8], const u32x4 (&wh)[2][2
   for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const u32x4 bt = tr_frag<kN>(sB + lo.bt[nb & 3] + 64 * (nb >> 2), m);
+      const u32x4 bt = tr_frag<kN>(sB + (lo.bt[nb & 3] ^ (64 * (nb >> 2))), m);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         S[t][nb] = mfma(bt, wh[t][m], (kFresh && m == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][nb]);
@@ -404,15 +405,16 @@ __device__ __forceinline__ size_t state_elem(int ph, int t, int nb, int lane) {
 
 // ---------------------------------------------------------------- segment states
 
-// Two heads per workgroup fit two workgroups per CU (LDS and registers), four heads one.
+// Single-buffered tiles: with two heads per workgroup three workgroups fit a CU (LDS and
+// registers), and each one's copies are covered by the other two's work.
 template <int HB>
-__global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_state_kernel(const bf16_t* __restrict__ xbc,
+__global__ __launch_bounds__(128 * HB, HB == 2 ? 3 : 1) void ssd_state_kernel(const bf16_t* __restrict__ xbc,
                                                                              const bf16_t* __restrict__ dt,
                                                                              const float* __restrict__ a_log,
                                                                              const float* __restrict__ dt_bias,
                                                                              SegPtrs sp, int H, int G, int nitems) {
-  __shared__ __attribute__((aligned(16))) bf16_t sB[2][kQ * kN];
-  __shared__ __attribute__((aligned(16))) bf16_t sX[2][HB][kQ * kP];
+  __shared__ __attribute__((aligned(16))) bf16_t sB[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sX[HB][kQ * kP];
   __shared__ __attribute__((aligned(16))) Decay sD[2][HB];
 
   const int nhg = H / HB;
@@ -438,10 +440,10 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_state_kernel(co
   auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
   auto dt_of = [&](int q) { return dt_bits(dt, si.y + q * kQ, nr_of(q), H, h, lane); };
   auto load = [&](int q) {
-    bf16_t* const dst[1] = {sB[q & 1]};
+    bf16_t* const dst[1] = {sB};
     const int nrb = nr_of(q) * (int)ld * 2;
     load_bc<HB, 1>(rows_of(q), nrb, 2u * ld, colB, dst, dof, w);
-    load_x<HB>(rows_of(q), nrb, 2u * ld, colX, sX[q & 1], dof, w);
+    load_x<HB>(rows_of(q), nrb, 2u * ld, colX, sX, dof, w);
   };
 
   f32x4 S[2][8];
@@ -458,20 +460,21 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_state_kernel(co
   for (int q = 0; q < nchunks; ++q) {
     const int st = q & 1;
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();  // chunk q rows and decay visible; chunk q-1 done with the other stage
+    __syncthreads();  // chunk q rows and decay visible
+    u32x4 xt[2][2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sX[hh] + lo.xt[t], m);
+    __builtin_amdgcn_s_setprio(1);
+    state_update(S, xt, sB, lo, sD[st][hh], lane);
+    __builtin_amdgcn_s_setprio(0);
+    __syncthreads();  // the tiles are free for the next chunk's copies
     uint32_t dtn2 = 0;
     if (q + 1 < nchunks) {
       load(q + 1);
       if (q + 2 < nchunks) dtn2 = dt_of(q + 2);
     }
-    u32x4 xt[2][2];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int m = 0; m < 2; ++m) xt[t][m] = tr_frag<kP>(sX[st][hh] + lo.xt[t], m);
-    __builtin_amdgcn_s_setprio(1);
-    state_update(S, xt, sB[st], lo, sD[st][hh], lane);
-    __builtin_amdgcn_s_setprio(0);
     if (q + 1 < nchunks)
       chunk_decay_update(sD[st ^ 1][hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
@@ -603,8 +606,8 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        acc = mfma(lds16(sB + lo.gt[kk & 1] + 16 * jb * kN + 64 * (kk >> 1)),
-                   lds16(sC + lo.gt[kk & 1] + 16 * ib * kN + 64 * (kk >> 1)), acc);
+        acc = mfma(lds16(sB + (lo.gt[kk & 1] ^ (64 * (kk >> 1))) + 16 * jb * kN),
+                   lds16(sC + (lo.gt[kk & 1] ^ (64 * (kk >> 1))) + 16 * ib * kN), acc);
       return acc;
     };
     // tiles 0..7 for every head, one per wave (two per wave with four waves); tiles
@@ -662,9 +665,8 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
       }
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
-        const bf16_t* cb = sC + 16 * ib * kN + lo.cf[kk];
-        const u32x2 c0 = lds8(cb);
-        const u32x2 c1 = lds8(cb + 64);
+        const u32x2 c0 = lds8(sC + 16 * ib * kN + lo.cf[kk]);
+        const u32x2 c1 = lds8(sC + 16 * ib * kN + (lo.cf[kk] ^ 64));
         const u32x4 cf = u32x4{c0.x, c0.y, c1.x, c1.y};
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
