@@ -12,8 +12,10 @@ steps let the clocks settle first.  Per-kernel durations come from HIP events th
 records on the launch stream around every launch, in a second pass of the same steps (the
 events cost a few us per launch, so they stay out of the timed pass); the roofline
 object uses the dominant kernel's algorithmic bytes (or flops) per launch over its average
-duration.  The CPU oracle is timed on a bounded sample on the host cores as a reported
-baseline.  Prints ONE JSON line.
+duration.  The two smaller prefill workloads (the packed variable-length batch and one
+2048-row 130m-shaped layer) are timed the same way and reported under ``other_workloads``.  The
+CPU oracle is timed on a bounded sample on the host cores as a reported baseline.  Prints ONE
+JSON line.
 """
 from __future__ import annotations
 
@@ -40,7 +42,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--decode-reps", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-decode", action="store_true", help="prefill only (for counter runs)")
+    ap.add_argument("--no-decode", action="store_true", help="the long prefill only (for counter runs)")
+    ap.add_argument("--no-others", action="store_true", help="skip the smaller prefill workloads")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this many MB (calibrates traffic counters)")
     ap.add_argument("--cpu-sample-rows", type=int, default=16384)
@@ -197,6 +200,9 @@ def main():
     if not args.no_decode:
         decode_us, dkern, dec_roof, R, dsh, dsteps = run_decode(args, torch, ops, W, dev, e0, e1)
 
+    # ---------------------------------------------------------------- smaller prefills
+    others = None if (args.no_others or args.no_decode) else run_other_prefills(args, torch, ops, W, dev)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -227,6 +233,7 @@ def main():
         "rooflines": rooflines,
         "decode_kernels": dkern,
         "decode_roofline": dec_roof,
+        "other_workloads": others,
     }
     print(json.dumps(res))
 
@@ -291,6 +298,62 @@ def run_decode(args, torch, ops, W, dev, e0, e1):
     dec_roof["frac_hbm"] = dec_roof["achieved_GBs"] / HBM_PEAK_GBS
 
     return decode_us, dkern, dec_roof, R, dsh, dsteps
+
+
+def run_other_prefills(args, torch, ops, W, dev):
+    """The two smaller prefill workloads: the packed variable-length batch (8 sequences of
+    100..4000 rows, half resuming from their slots) and one 2048-row layer of the 130m shape.
+    Whole-step time (conv + scan + norm) and per-kernel HIP-event times; the pools are restored
+    from pristine copies before each timed pass, outside it."""
+    res = {}
+    for wl in (W.varlen_prefill(), W.layer_130m_prefill()):
+        sh = wl.shape
+        T = wl.num_rows
+        d = ops.to_device
+        dims = ops.make_dims(sh.nheads, sh.headdim, sh.d_state, sh.ngroups, sh.conv_kernel, sh.chunk_size,
+                             sh.pool_slots, sh.act)
+        cw, cb, al, db, DD, nw = (d(a) for a in (wl.conv_w, wl.conv_b, wl.a_log, wl.dt_bias, wl.D, wl.norm_w))
+        xbc, z, dt = d(wl.xbc), d(wl.z), d(wl.dt)
+        cp0, sp0 = d(wl.conv_pool), d(wl.ssm_pool)
+        cp, sp = cp0.clone(), sp0.clone()
+        b = ops.RecurrentBatch(wl.run_lengths, wl.slots, wl.fresh, device=dev)
+        xa = torch.empty_like(xbc)
+        y = torch.empty((T, sh.d_inner), dtype=xbc.dtype, device=dev)
+        out = torch.empty_like(y)
+        ws = torch.empty(max(256, ops.scan_prefill_workspace_bytes(b, dims)), dtype=torch.uint8, device=dev)
+
+        def step():
+            ops.conv1d(xa, xbc, cw, cb, cp, b, dims)
+            ops.scan_prefill(y, xa, dt, al, db, DD, sp, b, dims, workspace=ws)
+            ops.gated_rmsnorm(out, y, z, nw, sh.norm_groups, sh.eps)
+
+        for _ in range(args.warmup):
+            step()
+        cp.copy_(cp0)
+        sp.copy_(sp0)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        cp.copy_(cp0)
+        sp.copy_(sp0)
+        torch.cuda.synchronize()
+        ops.timing_enable(64 * max(1, args.steps))
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+        per = {}
+        for name, t in ops.timing_collect(64 * max(1, args.steps)):
+            per.setdefault(name, []).append(t)
+        ops.timing_enable(0)
+        res[wl.name] = {"rows": T, "sequences": len(wl.run_lengths), "us_per_step": 1e3 * ms,
+                        "tokens_per_s": T / (ms * 1e-3),
+                        "kernels_us": {k: 1e3 * float(np.mean(v)) * len(v) / args.steps for k, v in per.items()}}
+    return res
 
 
 def cpu_baseline(args, W, wl, sh):

@@ -62,12 +62,26 @@ __global__ __launch_bounds__(256) void conv1d_silu_kernel(
   const int bnd = min(T_rows, a + R);
   const size_t col = (size_t)v * V;
 
+  // the thread's weights (V * K contiguous floats) and biases in 16-byte loads
   float wr[V][K], br[V];
+  {
+    const float4* wp = reinterpret_cast<const float4*>(w + col * K);
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    br[i] = b[col + i];
+    for (int i = 0; i < V * K / 4; ++i) {
+      const float4 t4 = wp[i];
+      const float f[4] = {t4.x, t4.y, t4.z, t4.w};
 #pragma unroll
-    for (int k = 0; k < K; ++k) wr[i][k] = w[(col + i) * K + k];
+      for (int e = 0; e < 4; ++e) wr[(4 * i + e) / K][(4 * i + e) % K] = f[e];
+    }
+    const float4* bp = reinterpret_cast<const float4*>(b + col);
+#pragma unroll
+    for (int i = 0; i < V / 4; ++i) {
+      const float4 t4 = bp[i];
+      br[4 * i] = t4.x;
+      br[4 * i + 1] = t4.y;
+      br[4 * i + 2] = t4.z;
+      br[4 * i + 3] = t4.w;
+    }
   }
 
   int s = seq_of_row(cu, S, a);
@@ -246,9 +260,10 @@ hipError_t launch_t(void* dst, const void* x, const float* w, const float* b, vo
     return hipSuccess;
   }
   const int64_t work = (int64_t)bd.num_rows * NV;
-  // rows per thread: enough threads to fill the chip (~512K), at most 32 rows each
+  // rows per thread: enough threads to fill the chip (~512K), 4 to 32 rows each (fewer than
+  // 4 would reload each thread's weights for too little work: 19 us -> 9 us on 2048 rows)
   int R = (int)((work + 524287) / 524288);
-  R = R < 1 ? 1 : (R > 32 ? 32 : R);
+  R = R < 4 ? 4 : (R > 32 ? 32 : R);
   const int64_t tiles = (bd.num_rows + R - 1) / R;
   const int64_t nthreads = tiles * NV;
   const dim3 grid((unsigned)((nthreads + 255) / 256));

@@ -57,7 +57,12 @@ __global__ __launch_bounds__(kSetupThreads) void scan_setup_kernel(const int32_t
   }
 }
 
-// One thread per float4 of a head's state, walking one sequence's segments in order.
+// One thread per float4 of a head's state, walking one sequence's segments in order.  The
+// segments' local states and decays are loaded kBatch at a time before the chain runs
+// through them in registers, so a long chain waits on one round of loads per batch rather
+// than one per segment.
+constexpr int kBatch = 8;
+
 __global__ __launch_bounds__(256) void scan_pass_kernel(const int2* __restrict__ seq_info,
                                                         const float* __restrict__ seg_decay,
                                                         float4* __restrict__ seg_state,
@@ -72,19 +77,27 @@ __global__ __launch_bounds__(256) void scan_pass_kernel(const int2* __restrict__
   const int2 si = seq_info[s];
   float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
   if (!fresh[s]) S = pool[((size_t)slots[s] * H + h) * f4 + f];
-  for (int k = 0; k < si.y; ++k) {
-    const int64_t seg = si.x + k;
-    float4* p = seg_state + ((size_t)seg * H + h) * f4 + f;
-    if (k + 1 < si.y) {
-      const float4 loc = *p;  // S_loc(k), written by the segment-state kernel
-      *p = S;                 // S_in(k)
-      const float d = seg_decay[seg * H + h];
-      S.x = fmaf(d, S.x, loc.x);
-      S.y = fmaf(d, S.y, loc.y);
-      S.z = fmaf(d, S.z, loc.z);
-      S.w = fmaf(d, S.w, loc.w);
-    } else {
-      *p = S;
+  for (int k0 = 0; k0 < si.y; k0 += kBatch) {
+    // S_loc(k) and the decays of segments k0.. (the sequence's last segment has no S_loc)
+    float4 loc[kBatch];
+    float dec[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int k = k0 + i;
+      const int64_t seg = si.x + k;
+      loc[i] = k + 1 < si.y ? seg_state[((size_t)seg * H + h) * f4 + f] : make_float4(0.f, 0.f, 0.f, 0.f);
+      dec[i] = k + 1 < si.y ? seg_decay[seg * H + h] : 0.f;
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int k = k0 + i;
+      if (k < si.y) {
+        seg_state[((size_t)(si.x + k) * H + h) * f4 + f] = S;  // S_in(k)
+        S.x = fmaf(dec[i], S.x, loc[i].x);
+        S.y = fmaf(dec[i], S.y, loc[i].y);
+        S.z = fmaf(dec[i], S.z, loc[i].z);
+        S.w = fmaf(dec[i], S.w, loc[i].w);
+      }
     }
   }
 }
