@@ -48,9 +48,15 @@ def lib() -> ctypes.CDLL:
         L.oracle_scan.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
                                   i32, i32, i32, i32, i32, i32, vp, i32]
         L.oracle_gated_rmsnorm.argtypes = [vp, vp, vp, vp, i32, f32, i32, i32, i32]
+        L.oracle_conv1d_snap.argtypes = L.oracle_conv1d.argtypes + [vp, i32]
+        L.oracle_scan_snap.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
+                                       i32, i32, i32, i32, i32, i32, vp, i32]
+        L.oracle_commit.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32]
+        L.oracle_snapshot_count.argtypes = [i32, vp, i32]
+        L.oracle_snapshot_count.restype = ctypes.c_longlong
         L.oracle_check_batch.argtypes = [i32, i32, vp, vp, i32, i32]
         for f in (L.oracle_conv1d, L.oracle_scan, L.oracle_gated_rmsnorm, L.oracle_check_batch,
-                  L.oracle_max_threads):
+                  L.oracle_max_threads, L.oracle_conv1d_snap, L.oracle_scan_snap, L.oracle_commit):
             f.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [i32]
         L.oracle_set_threads.restype = None
@@ -101,6 +107,45 @@ def scan(y, xbc, dt, a_log, dt_bias, d, ssm_state, run_lengths, slots, fresh, ng
     return lib().oracle_scan(_p(y), _p(xbc), _p(dt), _p(a_log), _p(dt_bias), _p(d), _p(ssm_state),
                              len(rl), xbc.shape[0], _p(rl), _p(sl), _p(fr), H, P, N, ngroups, M,
                              _act_of(xbc), _p(hm), 1 if decode else 0)
+
+
+def snapshot_count(run_lengths, snap_every) -> int:
+    """Snapshots a batch holds at stride E: sum over sequences of floor((L - 1) / E)."""
+    rl = np.ascontiguousarray(run_lengths, dtype=np.int32)
+    return int(lib().oracle_snapshot_count(len(rl), _p(rl), int(snap_every)))
+
+
+def conv1d_snap(dst, x, weight, bias, conv_state, snaps, snap_every, run_lengths, slots, fresh) -> int:
+    """conv1d plus conv-state snapshots every E rows: snaps [count, K-1, Dc] act."""
+    rl, sl, fr = _batch(run_lengths, slots, fresh)
+    Dc = x.shape[1]
+    K = weight.shape[1]
+    M = conv_state.shape[0]
+    return lib().oracle_conv1d_snap(_p(dst), _p(x), _p(weight), _p(bias), _p(conv_state), len(rl),
+                                    x.shape[0], _p(rl), _p(sl), _p(fr), Dc, K, M, _act_of(x), _p(snaps),
+                                    int(snap_every))
+
+
+def scan_snap(y, xbc, dt, a_log, dt_bias, d, ssm_state, snaps, snap_every, run_lengths, slots, fresh,
+              ngroups) -> int:
+    """scan plus SSM-state snapshots every E rows: snaps [count, H, P, N] f32."""
+    rl, sl, fr = _batch(run_lengths, slots, fresh)
+    M, H, P, N = ssm_state.shape
+    return lib().oracle_scan_snap(_p(y), _p(xbc), _p(dt), _p(a_log), _p(dt_bias), _p(d), _p(ssm_state),
+                                  len(rl), xbc.shape[0], _p(rl), _p(sl), _p(fr), H, P, N, ngroups, M,
+                                  _act_of(xbc), _p(snaps), int(snap_every))
+
+
+def commit(ssm_state, conv_state, ssm_snaps, conv_snaps, snap_every, accepted, run_lengths, slots) -> int:
+    """Rollback to the accepted prefix: slots take the snapshots at the accepted boundary."""
+    rl = np.ascontiguousarray(run_lengths, dtype=np.int32)
+    sl = np.ascontiguousarray(slots, dtype=np.int32)
+    acc = np.ascontiguousarray(accepted, dtype=np.int32)
+    M, H, P, N = ssm_state.shape
+    K1, Dc = conv_state.shape[1], conv_state.shape[2]
+    act = F32 if conv_state.dtype == np.float32 else BF16
+    return lib().oracle_commit(_p(ssm_state), _p(conv_state), _p(ssm_snaps), _p(conv_snaps), int(snap_every),
+                               _p(acc), len(rl), _p(rl), _p(sl), H, P, N, Dc, K1 + 1, act)
 
 
 def gated_rmsnorm(dst, x, z, weight, groups, eps) -> int:

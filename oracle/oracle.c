@@ -15,7 +15,9 @@
  *   [InfiniLM#575] "feat(mamba2): integrate model loading and recurrent
  *              inference", section "Motivation" (conv + FP32 SSM state per
  *              request) and "Notes for Reviewers" (head-wise D, gated RMSNorm
- *              after gating, unbounded time steps).
+ *              after gating, unbounded time steps; prefix-state snapshots and
+ *              speculative rollback named as variants that adaptation leaves
+ *              out, which the snapshot functions below provide).
  *
  * Arithmetic: every operation is carried out in double from values widened
  * from their stored type.  Results are rounded once to the activation type
@@ -120,6 +122,35 @@ static void first_rows(int S, const int32_t* len, long long* r0) {
   }
 }
 
+/* --------------------------------------------------------------- snapshots */
+
+/*
+ * State snapshots.  A snapshot at boundary b of a sequence is the state that a
+ * run of only its first b rows would leave in the slot: for the SSM the state
+ * after row b (the recurrence's h), for the conv the last K-1 entries of
+ * history ++ rows[0, b).  With a stride E >= 1 the boundaries are b = E, 2E, ...
+ * strictly inside the run (b < L; the state after the whole run is the slot).
+ * Snapshots are packed sequence after sequence in batch order; sequence s owns
+ * floor((L_s - 1) / E) of them, boundary j E at index first[s] + j - 1.
+ */
+static void snap_first(int S, const int32_t* len, int E, long long* first) {
+  long long n = 0;
+  for (int s = 0; s < S; ++s) {
+    first[s] = n;
+    n += (len[s] - 1) / E;
+  }
+}
+
+long long oracle_snapshot_count(int S, const int32_t* len, int E) {
+  if (S < 0 || E < 1) return -1;
+  long long n = 0;
+  for (int s = 0; s < S; ++s) {
+    if (len[s] < 1) return -1;
+    n += (len[s] - 1) / E;
+  }
+  return n;
+}
+
 /* ------------------------------------------------------------------ conv */
 
 /*
@@ -135,16 +166,19 @@ static void first_rows(int S, const int32_t* len, long long* r0) {
  * Layouts: x, dst [T][Dc] act; w [Dc][K] f32; b [Dc] f32;
  *          conv_state [M][K-1][Dc] act, row 0 the oldest.
  */
-int oracle_conv1d(void* dst, const void* x, const float* w, const float* b, void* conv_state,
-                  int S, int T, const int32_t* len, const int32_t* slot, const uint8_t* fresh,
-                  int Dc, int K, int M, int act) {
+static int conv_impl(void* dst, const void* x, const float* w, const float* b, void* conv_state,
+                     int S, int T, const int32_t* len, const int32_t* slot, const uint8_t* fresh,
+                     int Dc, int K, int M, int act, void* snaps, int E) {
   if (Dc <= 0 || K < 1 || (act != ORC_F32 && act != ORC_BF16)) return ORC_INVALID_ARGUMENT;
+  if (snaps != NULL && E < 1) return ORC_INVALID_ARGUMENT;
   int st = check_batch(S, T, len, slot, M, 0);
   if (st != ORC_OK) return st;
   if (S == 0) return ORC_OK;
   if (fresh == NULL) return ORC_INVALID_ARGUMENT;
   long long* r0 = (long long*)malloc(sizeof(long long) * (size_t)S);
   first_rows(S, len, r0);
+  long long* sf = (long long*)malloc(sizeof(long long) * (size_t)S);
+  if (snaps != NULL) snap_first(S, len, E, sf);
   const size_t es = act_size(act);
   const int H1 = K - 1;
 
@@ -178,6 +212,22 @@ int oracle_conv1d(void* dst, const void* x, const float* w, const float* b, void
         double out = pre / (1.0 + exp(-pre));
         store_act(dst, (size_t)(r0[s] + t) * Dc + c, act, out);
       }
+      /* snapshots: at boundary bd the last K-1 entries of win[0, H1 + bd) */
+      if (snaps != NULL) {
+        for (int j = 1; (long long)j * E < L; ++j) {
+          const int bd = j * E;
+          unsigned char* sb = (unsigned char*)snaps + (size_t)(sf[s] + j - 1) * (size_t)H1 * Dc * es;
+          for (int r = 0; r < H1; ++r) {
+            int idx = bd + r;
+            const unsigned char* src;
+            if (idx < H1)
+              src = hb + (size_t)idx * es;
+            else
+              src = xb + ((size_t)(r0[s] + idx - H1) * Dc + c) * es;
+            memcpy(sb + ((size_t)r * Dc + c) * es, src, es);
+          }
+        }
+      }
       /* new state: the last K-1 entries of win (win has H1 + L entries) */
       for (int r = 0; r < H1; ++r) {
         int idx = L + r;
@@ -192,7 +242,21 @@ int oracle_conv1d(void* dst, const void* x, const float* w, const float* b, void
     }
   }
   free(r0);
+  free(sf);
   return ORC_OK;
+}
+
+int oracle_conv1d(void* dst, const void* x, const float* w, const float* b, void* conv_state,
+                  int S, int T, const int32_t* len, const int32_t* slot, const uint8_t* fresh,
+                  int Dc, int K, int M, int act) {
+  return conv_impl(dst, x, w, b, conv_state, S, T, len, slot, fresh, Dc, K, M, act, NULL, 0);
+}
+
+/* The conv plus its state snapshots every E rows: snaps [count][K-1][Dc] act. */
+int oracle_conv1d_snap(void* dst, const void* x, const float* w, const float* b, void* conv_state,
+                       int S, int T, const int32_t* len, const int32_t* slot, const uint8_t* fresh,
+                       int Dc, int K, int M, int act, void* snaps, int E) {
+  return conv_impl(dst, x, w, b, conv_state, S, T, len, slot, fresh, Dc, K, M, act, snaps, E);
 }
 
 /* ------------------------------------------------------------------ scan */
@@ -216,18 +280,21 @@ int oracle_conv1d(void* dst, const void* x, const float* w, const float* b, void
  * decode != 0 applies the decode rule (every run length is 1); the arithmetic
  * is the same function.
  */
-int oracle_scan(void* y, const void* xbc, const void* dt, const float* a_log, const float* dt_bias,
-                const float* d, float* ssm_state, int S, int T, const int32_t* len,
-                const int32_t* slot, const uint8_t* fresh, int H, int P, int N, int G, int M,
-                int act, const uint8_t* head_mask, int decode) {
+static int scan_impl(void* y, const void* xbc, const void* dt, const float* a_log, const float* dt_bias,
+                     const float* d, float* ssm_state, int S, int T, const int32_t* len,
+                     const int32_t* slot, const uint8_t* fresh, int H, int P, int N, int G, int M,
+                     int act, const uint8_t* head_mask, int decode, float* snaps, int E) {
   if (H <= 0 || P <= 0 || N <= 0 || G <= 0 || H % G != 0 || (act != ORC_F32 && act != ORC_BF16))
     return ORC_INVALID_ARGUMENT;
+  if (snaps != NULL && E < 1) return ORC_INVALID_ARGUMENT;
   int st = check_batch(S, T, len, slot, M, decode);
   if (st != ORC_OK) return st;
   if (S == 0) return ORC_OK;
   if (fresh == NULL) return ORC_INVALID_ARGUMENT;
   long long* r0 = (long long*)malloc(sizeof(long long) * (size_t)S);
   first_rows(S, len, r0);
+  long long* sf = (long long*)malloc(sizeof(long long) * (size_t)S);
+  if (snaps != NULL) snap_first(S, len, E, sf);
   const size_t Di = (size_t)H * P;
   const size_t Dc = Di + 2 * (size_t)G * N;
   const int heads_per_group = H / G;
@@ -263,12 +330,64 @@ int oracle_scan(void* y, const void* xbc, const void* dt, const float* a_log, co
           acc += (double)d[hh] * xv;
           store_act(y, row * Di + (size_t)hh * P + p, act, acc);
         }
+        /* h is now the state after row t + 1 of the run */
+        const int bd = t + 1;
+        if (snaps != NULL && bd < len[s] && bd % E == 0)
+          memcpy(snaps + ((size_t)(sf[s] + bd / E - 1) * H + hh) * (size_t)P * N, h,
+                 sizeof(float) * (size_t)P * N);
       }
       memcpy(st_slot, h, sizeof(float) * (size_t)P * N);
       free(h);
     }
   }
   free(r0);
+  free(sf);
+  return ORC_OK;
+}
+
+int oracle_scan(void* y, const void* xbc, const void* dt, const float* a_log, const float* dt_bias,
+                const float* d, float* ssm_state, int S, int T, const int32_t* len,
+                const int32_t* slot, const uint8_t* fresh, int H, int P, int N, int G, int M,
+                int act, const uint8_t* head_mask, int decode) {
+  return scan_impl(y, xbc, dt, a_log, dt_bias, d, ssm_state, S, T, len, slot, fresh, H, P, N, G, M, act,
+                   head_mask, decode, NULL, 0);
+}
+
+/* The scan plus its state snapshots every E rows: snaps [count][H][P][N] f32. */
+int oracle_scan_snap(void* y, const void* xbc, const void* dt, const float* a_log, const float* dt_bias,
+                     const float* d, float* ssm_state, int S, int T, const int32_t* len,
+                     const int32_t* slot, const uint8_t* fresh, int H, int P, int N, int G, int M,
+                     int act, float* snaps, int E) {
+  return scan_impl(y, xbc, dt, a_log, dt_bias, d, ssm_state, S, T, len, slot, fresh, H, P, N, G, M, act,
+                   NULL, 0, snaps, E);
+}
+
+/*
+ * Rollback after a verified run (speculative decoding): sequence s accepted the
+ * first m = accepted[s] rows of its run.  When 1 <= m < L and m is a boundary
+ * (m % E == 0), its slots take the snapshots at m; otherwise (m == L: the slots
+ * already hold the state after the run; anything else) they are left as they
+ * are.  Either snapshot array may be NULL (that pool is then not touched).
+ */
+int oracle_commit(float* ssm_state, void* conv_state, const float* ssm_snaps, const void* conv_snaps,
+                  int E, const int32_t* accepted, int S, const int32_t* len, const int32_t* slot,
+                  int H, int P, int N, int Dc, int K, int act) {
+  if (E < 1 || S < 0 || (S > 0 && (accepted == NULL || len == NULL || slot == NULL))) return ORC_INVALID_ARGUMENT;
+  long long* sf = (long long*)malloc(sizeof(long long) * (size_t)(S > 0 ? S : 1));
+  snap_first(S, len, E, sf);
+  const size_t es = act_size(act);
+  const size_t spn = (size_t)H * P * N;
+  const size_t cst = (size_t)(K - 1) * Dc;
+  for (int s = 0; s < S; ++s) {
+    const int m = accepted[s];
+    if (m < 1 || m >= len[s] || m % E != 0) continue;
+    const long long idx = sf[s] + m / E - 1;
+    if (ssm_snaps != NULL) memcpy(ssm_state + (size_t)slot[s] * spn, ssm_snaps + (size_t)idx * spn, spn * 4);
+    if (conv_snaps != NULL)
+      memcpy((unsigned char*)conv_state + (size_t)slot[s] * cst * es,
+             (const unsigned char*)conv_snaps + (size_t)idx * cst * es, cst * es);
+  }
+  free(sf);
   return ORC_OK;
 }
 

@@ -70,3 +70,34 @@ def oracle_norm(wl: W.Workload, y, z=None, weight=None, groups=None):
                               sh.norm_groups if groups is None else groups, sh.eps)
     assert st == 0, st
     return out
+
+
+def oracle_conv_snap(wl: W.Workload, snap_every, xbc=None, conv_pool=None, run_lengths=None, slots=None,
+                     fresh=None):
+    """oracle conv with conv-state snapshots every `snap_every` rows: (out, pool, snaps)."""
+    xbc = wl.xbc if xbc is None else xbc
+    pool = (wl.conv_pool if conv_pool is None else conv_pool).copy()
+    rl = wl.run_lengths if run_lengths is None else run_lengths
+    n = oracle.snapshot_count(rl, snap_every)
+    snaps = np.zeros((n, wl.shape.conv_kernel - 1, wl.shape.conv_dim), dtype=xbc.dtype)
+    out = np.zeros_like(xbc)
+    st = oracle.conv1d_snap(out, xbc, wl.conv_w, wl.conv_b, pool, snaps, snap_every, rl,
+                            wl.slots if slots is None else slots, wl.fresh if fresh is None else fresh)
+    assert st == 0, st
+    return out, pool, snaps
+
+
+def oracle_scan_snap(wl: W.Workload, xa, snap_every, dt=None, ssm_pool=None, run_lengths=None, slots=None,
+                     fresh=None):
+    """oracle scan with SSM-state snapshots every `snap_every` rows: (y, pool, snaps)."""
+    sh = wl.shape
+    pool = (wl.ssm_pool if ssm_pool is None else ssm_pool).copy()
+    rl = wl.run_lengths if run_lengths is None else run_lengths
+    n = oracle.snapshot_count(rl, snap_every)
+    snaps = np.zeros((n, sh.nheads, sh.headdim, sh.d_state), dtype=np.float32)
+    y = np.zeros((xa.shape[0], sh.d_inner), dtype=xa.dtype)
+    st = oracle.scan_snap(y, xa, wl.dt if dt is None else dt, wl.a_log, wl.dt_bias, wl.D, pool, snaps,
+                          snap_every, rl, wl.slots if slots is None else slots,
+                          wl.fresh if fresh is None else fresh, sh.ngroups)
+    assert st == 0, st
+    return y, pool, snaps

@@ -6,7 +6,9 @@ the pages state, or a brute force on tiny inputs.  Sources:
   * "feat(backend): Mamba2 ops, with CPU reference implementations" (gllm PR #85), sections
     "Ops", "CPU reference" and "Testing";
   * "feat(mamba2): integrate model loading and recurrent inference" (InfiniLM PR #575),
-    section "Motivation".
+    sections "Motivation" and "Notes for Reviewers" (prefix-state snapshots and speculative
+    rollback, which that adaptation leaves out: a snapshot at boundary b is the state a run of
+    the first b rows leaves in the slot, pinned below against such runs).
 """
 import json
 import math
@@ -17,7 +19,7 @@ import pytest
 
 import oracle
 from mamba2_selective_scan_causalconv1d_amd import workloads as W
-from _util import oracle_conv, oracle_norm, oracle_scan
+from _util import oracle_conv, oracle_conv_snap, oracle_norm, oracle_scan, oracle_scan_snap
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -447,3 +449,72 @@ def test_thread_count_does_not_change_results(orc):
             assert np.array_equal(a, b)
     finally:
         oracle.set_threads(n0)
+
+
+# ------------------------------------------------------------ snapshots and rollback
+
+
+def test_snapshot_count_brute_force(orc):
+    rng = np.random.default_rng(70)
+    for _ in range(50):
+        lens = rng.integers(1, 40, rng.integers(0, 6)).tolist()
+        E = int(rng.integers(1, 12))
+        want = sum(len([b for b in range(1, L) if b % E == 0]) for L in lens)
+        assert oracle.snapshot_count(lens, E) == want
+
+
+def _prefix_states(wl, s, b):
+    """Slot states a run of only the first b rows of sequence s leaves (conv, ssm)."""
+    r0 = int(np.sum(wl.run_lengths[:s]))
+    rows = slice(r0, r0 + b)
+    one = dict(run_lengths=[b], slots=[wl.slots[s]], fresh=[wl.fresh[s]])
+    xa, cp = oracle_conv(wl, xbc=np.ascontiguousarray(wl.xbc[rows]), **one)
+    _, sp = oracle_scan(wl, xa, dt=np.ascontiguousarray(wl.dt[rows]), **one)
+    return cp[wl.slots[s]], sp[wl.slots[s]]
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+@pytest.mark.parametrize("E", [1, 3, 8])
+def test_snapshots_equal_prefix_runs(orc, act, E):
+    """A snapshot at boundary b equals, bit for bit, the slot state after a run of the first b
+    rows of its sequence (conv: including history rows when b < K-1); the outputs and the final
+    slots are those of the same call without snapshots."""
+    wl = _small(71, [9, 1, 17, 4], fresh=[1, 0, 0, 1], slots=[5, 0, 2, 3], act=act)
+    xa, cp, csn = oracle_conv_snap(wl, E)
+    y, sp, ssn = oracle_scan_snap(wl, xa, E)
+    xa0, cp0 = oracle_conv(wl)
+    y0, sp0 = oracle_scan(wl, xa0)
+    assert np.array_equal(xa, xa0) and np.array_equal(y, y0)
+    assert np.array_equal(cp, cp0) and np.array_equal(sp, sp0)
+    idx = 0
+    for s, L in enumerate(wl.run_lengths):
+        for b in range(E, L, E):
+            c_ref, s_ref = _prefix_states(wl, s, b)
+            assert np.array_equal(csn[idx], c_ref), (s, b)
+            assert np.array_equal(ssn[idx], s_ref), (s, b)
+            idx += 1
+    assert idx == len(ssn) == len(csn)
+
+
+@pytest.mark.parametrize("E", [1, 4])
+def test_commit_rolls_back_to_accepted_prefix(orc, E):
+    """After a verified run, committing accepted[s] = m puts the state of the first m rows in
+    the slots when m is a boundary below L; m == L keeps the whole run's state; other values
+    (0, beyond L, between boundaries) leave the slots as they are; other slots are untouched."""
+    lens = [5, 8, 1, 9, 8]
+    wl = _small(72, lens, fresh=[0, 1, 0, 0, 1], slots=[4, 1, 0, 5, 2], act="bf16")
+    xa, cp, csn = oracle_conv_snap(wl, E)
+    _, sp, ssn = oracle_scan_snap(wl, xa, E)
+    accepted = [4, 8, 1, 7 if E == 1 else 6, 0]
+    cp_c, sp_c = cp.copy(), sp.copy()
+    assert oracle.commit(sp_c, cp_c, ssn, csn, E, accepted, lens, wl.slots) == 0
+    for s, (L, m) in enumerate(zip(lens, accepted)):
+        sl = wl.slots[s]
+        if 1 <= m < L and m % E == 0:
+            c_ref, s_ref = _prefix_states(wl, s, m)
+        else:
+            c_ref, s_ref = cp[sl], sp[sl]
+        assert np.array_equal(cp_c[sl], c_ref), s
+        assert np.array_equal(sp_c[sl], s_ref), s
+    for sl in set(range(wl.shape.pool_slots)) - set(int(v) for v in wl.slots):
+        assert np.array_equal(cp_c[sl], wl.conv_pool[sl]) and np.array_equal(sp_c[sl], wl.ssm_pool[sl])
