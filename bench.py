@@ -44,6 +44,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="the long prefill only (for counter runs)")
     ap.add_argument("--no-others", action="store_true", help="skip the smaller prefill workloads")
+    ap.add_argument("--no-snapshots", action="store_true", help="skip the snapshot and verify workloads")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="also run a plain device copy of this many MB (calibrates traffic counters)")
     ap.add_argument("--cpu-sample-rows", type=int, default=16384)
@@ -203,6 +204,16 @@ def main():
     # ---------------------------------------------------------------- smaller prefills
     others = None if (args.no_others or args.no_decode) else run_other_prefills(args, torch, ops, W, dev)
 
+    # ---------------------------------------------------------------- snapshots and verify
+    snaps = None
+    if not (args.no_snapshots or args.no_decode):
+        def long_snap_step(E, snaps_c, snaps_s, ws_snap):
+            ops.conv1d_snap(xa, xbc, conv_w, conv_b, conv_pool, snaps_c, E, batch, dims)
+            ops.scan_prefill_snap(y, xa, dt, a_log, dt_bias, D, ssm_pool, snaps_s, E, batch, dims, workspace=ws_snap)
+            ops.gated_rmsnorm(out, y, z, norm_w, sh.norm_groups, sh.eps)
+
+        snaps = run_snapshots(args, torch, ops, W, dev, e0, e1, long_snap_step, batch, dims, sh, ms_per_step)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -234,6 +245,7 @@ def main():
         "decode_kernels": dkern,
         "decode_roofline": dec_roof,
         "other_workloads": others,
+        "snapshots": snaps,
     }
     print(json.dumps(res))
 
@@ -298,6 +310,105 @@ def run_decode(args, torch, ops, W, dev, e0, e1):
     dec_roof["frac_hbm"] = dec_roof["achieved_GBs"] / HBM_PEAK_GBS
 
     return decode_us, dkern, dec_roof, R, dsh, dsteps
+
+
+def run_snapshots(args, torch, ops, W, dev, e0, e1, long_snap_step, long_batch, long_dims, long_sh,
+                  long_ms):
+    """State snapshots and speculative verify.  (1) The verify workload: 256 sequences of 4
+    draft rows on the decode workload's 512-slot pool, one step = conv with per-row conv
+    snapshots + the verify scan with per-row SSM snapshots + the norm, timed against the same
+    step without snapshots; then the commit of random accepted counts.  (2) The long prefill
+    with snapshots every 1024 rows against the plain prefill step."""
+    d = ops.to_device
+    vwl = W.verify_batch()
+    sh = vwl.shape
+    dims = ops.make_dims(sh.nheads, sh.headdim, sh.d_state, sh.ngroups, sh.conv_kernel, sh.chunk_size,
+                         sh.pool_slots, sh.act)
+    cw, cb, al, db, DD, nw = [d(a) for a in (vwl.conv_w, vwl.conv_b, vwl.a_log, vwl.dt_bias, vwl.D, vwl.norm_w)]
+    x, z, dt = d(vwl.xbc), d(vwl.z), d(vwl.dt)
+    pristine_c, pristine_s = d(vwl.conv_pool), d(vwl.ssm_pool)
+    cp, sp = pristine_c.clone(), pristine_s.clone()
+    b = ops.RecurrentBatch(vwl.run_lengths, vwl.slots, vwl.fresh, device=dev)
+    T, R, rows = vwl.num_rows, len(vwl.run_lengths), int(vwl.run_lengths[0])
+    n = ops.snapshot_count(b, 1)
+    csn = torch.empty((n, sh.conv_kernel - 1, sh.conv_dim), dtype=torch.bfloat16, device=dev)
+    ssn = torch.empty((n, sh.nheads, sh.headdim, sh.d_state), dtype=torch.float32, device=dev)
+    xa = torch.empty_like(x)
+    y = torch.empty((T, sh.d_inner), dtype=torch.bfloat16, device=dev)
+    out = torch.empty_like(y)
+    accepted = torch.from_numpy(np.random.default_rng(5).integers(1, rows + 1, R).astype(np.int32)).to(dev)
+
+    def step(snap):
+        if snap:
+            ops.conv1d_snap(xa, x, cw, cb, cp, csn, 1, b, dims)
+        else:
+            ops.conv1d(xa, x, cw, cb, cp, b, dims)
+        ops.scan_verify(y, xa, dt, al, db, DD, sp, ssn if snap else None, b, dims)
+        ops.gated_rmsnorm(out, y, z, nw, sh.norm_groups, sh.eps)
+
+    def timed(fn, reps=7):
+        times = []
+        for _ in range(reps):
+            cp.copy_(pristine_c)
+            sp.copy_(pristine_s)
+            torch.cuda.synchronize()
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e3)
+        return float(np.median(times[1:]))
+
+    us_snap = timed(lambda: step(True))
+    us_plain = timed(lambda: step(False))
+    step(True)
+    torch.cuda.synchronize()
+    t0 = []
+    for _ in range(7):
+        e0.record()
+        ops.commit_snapshots(sp, cp, ssn, csn, 1, accepted, b, dims)
+        e1.record()
+        torch.cuda.synchronize()
+        t0.append(e0.elapsed_time(e1) * 1e3)
+    us_commit = float(np.median(t0[1:]))
+    ops.timing_enable(64)
+    cp.copy_(pristine_c)
+    sp.copy_(pristine_s)
+    step(True)
+    ops.commit_snapshots(sp, cp, ssn, csn, 1, accepted, b, dims)
+    torch.cuda.synchronize()
+    kern = {k: round(1e3 * ms, 2) for k, ms in ops.timing_collect(64)}
+    ops.timing_enable(0)
+    H, P, N = sh.nheads, sh.headdim, sh.d_state
+    resumed = int((vwl.fresh == 0).sum())
+    vbytes = (resumed + R) * H * P * N * 4 + n * H * P * N * 4 + T * (sh.conv_dim + H + sh.d_inner) * 2
+    verify = {"workload": "verify_%dx%d" % (R, rows), "requests": R, "rows_per_request": rows,
+              "us_per_step": us_snap, "tokens_per_s": T / (us_snap * 1e-6), "us_per_step_no_snapshots": us_plain,
+              "commit_us": us_commit, "kernels_us": kern, "scan_verify_alg_bytes": vbytes,
+              "scan_verify_GBs": vbytes / (kern["scan_verify"] * 1e-6) / 1e9}
+
+    # (2) long prefill, snapshots every 1024 rows
+    E = 1024
+    nl = ops.snapshot_count(long_batch, E)
+    lc = torch.empty((nl, long_sh.conv_kernel - 1, long_sh.conv_dim), dtype=torch.bfloat16, device=dev)
+    ls = torch.empty((nl, long_sh.nheads, long_sh.headdim, long_sh.d_state), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(256, ops.scan_prefill_snap_workspace_bytes(long_batch, long_dims, E)), dtype=torch.uint8,
+                     device=dev)
+    for _ in range(5):
+        long_snap_step(E, lc, ls, ws)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        long_snap_step(E, lc, ls, ws)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    prefill = {"workload": "long_prefill_4x16384", "snap_every": E, "snapshots": nl, "ms_per_step": ms,
+               "overhead_vs_plain_step": ms / long_ms - 1.0,
+               "snapshot_bytes": nl * (long_sh.nheads * long_sh.headdim * long_sh.d_state * 4 +
+                                       (long_sh.conv_kernel - 1) * long_sh.conv_dim * 2)}
+    del lc, ls, ws
+    return {"verify": verify, "prefill": prefill}
 
 
 def run_other_prefills(args, torch, ops, W, dev):

@@ -167,6 +167,87 @@ mamba2_status mamba2_gated_rmsnorm(void* dst, const void* x, const void* z, cons
                                    int32_t act_dtype, void* stream);
 
 /*
+ * State snapshots and rollback.  "feat(mamba2): integrate model loading and
+ * recurrent inference" (InfiniLM PR #575), section "Notes for Reviewers", names
+ * prefix-state snapshots and speculative rollback as variants that adaptation
+ * leaves out; the calls below provide them.  A snapshot at boundary b of a
+ * sequence is the state that a run of only its first b rows would leave in its
+ * slots: the SSM state [H, P, N] f32 after row b, and the conv state [K-1, Dc]
+ * act (the last K-1 entries of history ++ rows[0, b)).  With a stride
+ * snap_every = E >= 1 the boundaries are E, 2E, ... strictly inside each run
+ * (b < L; the state after the whole run is in the slots).  Snapshots are packed
+ * sequence after sequence in batch order: sequence s owns floor((L_s - 1) / E)
+ * of them, boundary j E at index first(s) + j - 1, first(s) the count owned by
+ * the sequences before it.  A snapshot has the layout of one pool slot, so the
+ * snapshot buffers may be free slots of the caller's own pools (the snapshot
+ * pointers set to slot `base` of each pool): rolling a sequence back is then a
+ * change of its slot number, with no copy; mamba2_commit_snapshots is the
+ * copying alternative.
+ */
+
+/* Snapshots a batch holds at stride snap_every (host only); -1 on a null batch,
+ * a run length < 1 or snap_every < 1. */
+int64_t mamba2_snapshot_count(const mamba2_recurrent_batch* rb, int32_t snap_every);
+
+/*
+ * mamba2_conv1d plus its conv-state snapshots every snap_every rows.
+ *   conv_snaps device [count, K-1, Dc] act (written; may be NULL when count is 0)
+ * Other arguments, requirements and errors as mamba2_conv1d.
+ */
+mamba2_status mamba2_conv1d_snap(void* dst, const void* x, const float* weight, const float* bias,
+                                 void* conv_state, void* conv_snaps, int32_t snap_every,
+                                 const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream);
+
+/*
+ * mamba2_scan_prefill plus SSM-state snapshots every snap_every rows (prefix
+ * caching).  The chunked scan then cuts its segments so that every boundary
+ * starts one, and copies the states entering those segments.
+ *   ssm_snaps device [count, H, P, N] f32 (written; may be NULL when count is 0)
+ *   workspace >= mamba2_scan_prefill_snap_workspace_bytes(rb, dims, snap_every)
+ * snap_every must be a multiple of 64 on the bf16 P = 64, N = 128 path and of
+ * min(chunk_size, 64) on the other, else MAMBA2_NOT_IMPLEMENTED.  Other
+ * arguments, requirements and errors as mamba2_scan_prefill.
+ */
+mamba2_status mamba2_scan_prefill_snap(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                       const float* dt_bias, const float* d, float* ssm_state,
+                                       float* ssm_snaps, int32_t snap_every,
+                                       const mamba2_recurrent_batch* rb, const mamba2_dims* dims,
+                                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Workspace bytes mamba2_scan_prefill_snap needs (0 when S == 0 or snap_every
+ * is not supported). */
+size_t mamba2_scan_prefill_snap_workspace_bytes(const mamba2_recurrent_batch* rb,
+                                                const mamba2_dims* dims, int32_t snap_every);
+
+/*
+ * A short run per sequence, e.g. the draft tokens of speculative decoding to be
+ * verified: runs of 1..16 rows (MAMBA2_RUN_LENGTHS beyond), the recurrence applied
+ * row after row in the decode mapping (each sequence's state is read once and
+ * written once; a run of one row gives mamba2_scan_decode's results bit for bit).
+ *   ssm_snaps device [T - S, H, P, N] f32: the state after every row but the last
+ *             (snap_every = 1 snapshots), or NULL to skip them
+ * Other arguments as mamba2_scan_decode; the shapes it covers, else
+ * MAMBA2_NOT_IMPLEMENTED.
+ */
+mamba2_status mamba2_scan_verify(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                 const float* dt_bias, const float* d, float* ssm_state, float* ssm_snaps,
+                                 const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream);
+
+/*
+ * Rollback to the accepted prefix of each run: sequence s accepted its first
+ * m = accepted[s] rows; when 1 <= m < L_s and m % snap_every == 0 its slots take
+ * the snapshots at boundary m; otherwise (m == L_s: the slots already hold the
+ * whole run's state; any other value) they are left as they are.  rb and
+ * snap_every are those of the run that made the snapshots.
+ *   ssm_state, ssm_snaps:  device, as above (ssm_snaps NULL: the SSM pool is not touched)
+ *   conv_state, conv_snaps: device, as above (conv_snaps NULL: the conv pool is not touched)
+ *   accepted  device [S] int32
+ */
+mamba2_status mamba2_commit_snapshots(float* ssm_state, void* conv_state, const float* ssm_snaps,
+                                      const void* conv_snaps, int32_t snap_every, const int32_t* accepted,
+                                      const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream);
+
+/*
  * Host-only checks shared by every stateful call (no device access):
  * dims, then run lengths (each >= 1; decode != 0: each == 1; sum == num_rows),
  * then slot range, then slot sharing.  Returns the first failing status.

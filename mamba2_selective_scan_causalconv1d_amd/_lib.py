@@ -47,6 +47,12 @@ SIGNATURES = [
     ("mamba2_scan_prefill_workspace_bytes", _sz, [_pb, _pd]),
     ("mamba2_scan_decode", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pb, _pd, _vp]),
     ("mamba2_gated_rmsnorm", _i32, [_vp, _vp, _vp, _vp, _i32, _f32, _i32, _i32, _i32, _vp]),
+    ("mamba2_snapshot_count", ctypes.c_int64, [_pb, _i32]),
+    ("mamba2_conv1d_snap", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _i32, _pb, _pd, _vp]),
+    ("mamba2_scan_prefill_snap", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _pb, _pd, _vp, _sz, _vp]),
+    ("mamba2_scan_prefill_snap_workspace_bytes", _sz, [_pb, _pd, _i32]),
+    ("mamba2_scan_verify", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _pb, _pd, _vp]),
+    ("mamba2_commit_snapshots", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _pb, _pd, _vp]),
     ("mamba2_validate", _i32, [_pb, _pd, _i32]),
     ("mamba2_ssm_slot_bytes", _sz, [_pd]),
     ("mamba2_conv_slot_bytes", _sz, [_pd]),

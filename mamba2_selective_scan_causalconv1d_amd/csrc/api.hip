@@ -166,6 +166,116 @@ mamba2_status mamba2_gated_rmsnorm(void* dst, const void* x, const void* z, cons
                                        (hipStream_t)stream));
 }
 
+int64_t mamba2_snapshot_count(const mamba2_recurrent_batch* rb, int32_t snap_every) {
+  if (!rb || snap_every < 1 || rb->num_seqs < 0 || (rb->num_seqs > 0 && !rb->run_lengths)) return -1;
+  for (int s = 0; s < rb->num_seqs; ++s)
+    if (rb->run_lengths[s] < 1) return -1;
+  return snapshot_count(rb, snap_every);
+}
+
+mamba2_status mamba2_conv1d_snap(void* dst, const void* x, const float* weight, const float* bias,
+                                 void* conv_state, void* conv_snaps, int32_t snap_every,
+                                 const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream) {
+  mamba2_status st = check_dims(dims);
+  if (st != MAMBA2_OK) return st;
+  if (!rb || snap_every < 1) return MAMBA2_INVALID_ARGUMENT;
+  if (rb->num_rows > 0 && (!dst || !x || !weight || !bias || !conv_state)) return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({dst, x, weight, bias, conv_state, conv_snaps})) return MAMBA2_INVALID_ARGUMENT;
+  st = check_batch(rb, dims, false);
+  if (st != MAMBA2_OK) return st;
+  const int64_t Dc = (int64_t)dims->nheads * dims->headdim + 2 * (int64_t)dims->ngroups * dims->d_state;
+  if (dims->conv_kernel < 2 || dims->conv_kernel > 4 || Dc % act_vec(dims->act_dtype) != 0)
+    return MAMBA2_NOT_IMPLEMENTED;
+  const int64_t n = snapshot_count(rb, snap_every);
+  if (n > 0 && !conv_snaps) return MAMBA2_INVALID_ARGUMENT;
+  if (n * (dims->conv_kernel - 1) >= kMaxElems) return MAMBA2_NOT_IMPLEMENTED;
+  if (rb->num_rows == 0) return MAMBA2_OK;
+  // the snapshots read the slot rows the conv then replaces: stream order keeps them first
+  hipError_t e = launch_conv_snapshots(conv_snaps, x, conv_state, batch_dev(rb), snapshot_max_per_seq(rb, snap_every),
+                                       (int32_t)Dc, dims->conv_kernel, snap_every, dims->act_dtype,
+                                       (hipStream_t)stream);
+  if (e != hipSuccess) return MAMBA2_HIP_ERROR;
+  return from_hip(launch_conv1d(dst, x, weight, bias, conv_state, batch_dev(rb), (int32_t)Dc,
+                                dims->conv_kernel, dims->act_dtype, (hipStream_t)stream));
+}
+
+size_t mamba2_scan_prefill_snap_workspace_bytes(const mamba2_recurrent_batch* rb, const mamba2_dims* dims,
+                                                int32_t snap_every) {
+  if (check_all(rb, dims, false) != MAMBA2_OK || rb->num_rows == 0) return 0;
+  const int32_t L = scan_segment_length_snap(rb, dims, snap_every);
+  return L > 0 ? scan_layout(rb, dims, L).total : 0;
+}
+
+mamba2_status mamba2_scan_prefill_snap(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                       const float* dt_bias, const float* d, float* ssm_state,
+                                       float* ssm_snaps, int32_t snap_every,
+                                       const mamba2_recurrent_batch* rb, const mamba2_dims* dims,
+                                       void* workspace, size_t workspace_bytes, void* stream) {
+  mamba2_status st = check_dims(dims);
+  if (st != MAMBA2_OK) return st;
+  if (!rb || snap_every < 1) return MAMBA2_INVALID_ARGUMENT;
+  if (rb->num_rows > 0 && (!dst || !xbc || !dt || !a_log || !dt_bias || !d || !ssm_state))
+    return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({dst, xbc, ssm_state, ssm_snaps})) return MAMBA2_INVALID_ARGUMENT;
+  st = check_batch(rb, dims, false);
+  if (st != MAMBA2_OK) return st;
+  if (!scan_supported(dims)) return MAMBA2_NOT_IMPLEMENTED;
+  const int32_t seg_len = scan_segment_length_snap(rb, dims, snap_every);
+  if (seg_len == 0) return MAMBA2_NOT_IMPLEMENTED;
+  const int64_t n = snapshot_count(rb, snap_every);
+  if (n > 0 && !ssm_snaps) return MAMBA2_INVALID_ARGUMENT;
+  if (n >= kMaxElems) return MAMBA2_NOT_IMPLEMENTED;
+  if (rb->num_rows == 0) return MAMBA2_OK;
+  const ScanLayout lay = scan_layout(rb, dims, seg_len);
+  if (!workspace || workspace_bytes < lay.total) return MAMBA2_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & 255) != 0) return MAMBA2_INVALID_ARGUMENT;
+  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace};
+  hipError_t e = launch_scan_prefill(a, (hipStream_t)stream);
+  if (e != hipSuccess) return MAMBA2_HIP_ERROR;
+  return from_hip(launch_ssm_snapshots(a, ssm_snaps, snapshot_max_per_seq(rb, snap_every), snap_every,
+                                       (hipStream_t)stream));
+}
+
+mamba2_status mamba2_scan_verify(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                 const float* dt_bias, const float* d, float* ssm_state, float* ssm_snaps,
+                                 const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream) {
+  mamba2_status st = check_dims(dims);
+  if (st != MAMBA2_OK) return st;
+  if (!rb) return MAMBA2_INVALID_ARGUMENT;
+  if (rb->num_rows > 0 && (!dst || !xbc || !dt || !a_log || !dt_bias || !d || !ssm_state))
+    return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({dst, xbc, ssm_state, ssm_snaps})) return MAMBA2_INVALID_ARGUMENT;
+  st = check_batch(rb, dims, false);
+  if (st != MAMBA2_OK) return st;
+  int32_t max_rows = 0;
+  for (int s = 0; s < rb->num_seqs; ++s) max_rows = std::max(max_rows, rb->run_lengths[s]);
+  if (max_rows > kMaxVerifyRows) return MAMBA2_RUN_LENGTHS;
+  if (!decode_supported(*dims) || !decode_grid_fits(*dims, rb->num_seqs)) return MAMBA2_NOT_IMPLEMENTED;
+  if (verify_lds_bytes(*dims, kMaxVerifyRows) > 65536) return MAMBA2_NOT_IMPLEMENTED;
+  if (rb->num_rows == 0) return MAMBA2_OK;
+  return from_hip(launch_scan_verify(dst, xbc, dt, a_log, dt_bias, d, ssm_state, ssm_snaps, batch_dev(rb), *dims,
+                                     max_rows, (hipStream_t)stream));
+}
+
+mamba2_status mamba2_commit_snapshots(float* ssm_state, void* conv_state, const float* ssm_snaps,
+                                      const void* conv_snaps, int32_t snap_every, const int32_t* accepted,
+                                      const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream) {
+  mamba2_status st = check_dims(dims);
+  if (st != MAMBA2_OK) return st;
+  if (!rb || snap_every < 1) return MAMBA2_INVALID_ARGUMENT;
+  if (rb->num_seqs > 0 && !accepted) return MAMBA2_INVALID_ARGUMENT;
+  if ((ssm_snaps && !ssm_state) || (conv_snaps && !conv_state)) return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({ssm_state, conv_state, ssm_snaps, conv_snaps})) return MAMBA2_INVALID_ARGUMENT;
+  st = check_batch(rb, dims, false);
+  if (st != MAMBA2_OK) return st;
+  const int64_t Dc = (int64_t)dims->nheads * dims->headdim + 2 * (int64_t)dims->ngroups * dims->d_state;
+  if (dims->d_state % 4 != 0 || Dc % act_vec(dims->act_dtype) != 0 || dims->conv_kernel < 2)
+    return MAMBA2_NOT_IMPLEMENTED;
+  if (rb->num_seqs == 0 || (!ssm_snaps && !conv_snaps)) return MAMBA2_OK;
+  return from_hip(launch_commit(ssm_state, conv_state, ssm_snaps, conv_snaps, accepted, batch_dev(rb), *dims,
+                                snap_every, (hipStream_t)stream));
+}
+
 size_t mamba2_ssm_slot_bytes(const mamba2_dims* d) {
   if (check_dims(d) != MAMBA2_OK) return 0;
   return (size_t)d->nheads * d->headdim * d->d_state * sizeof(float);

@@ -87,6 +87,21 @@ __device__ __forceinline__ float softplus_f32(float v) { return v > 20.f ? v : l
 // below the bf16 / fp32 output rounding of every op that uses it.
 __device__ __forceinline__ float silu_f32(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 
+// Sum over aligned groups of q lanes (q a power of two <= 64, uniform), every lane of a
+// group receiving the group's sum.  Within rows of 16 lanes the partners come from DPP
+// (quad permutes, then the half-row and row mirrors: after each step all lanes of the
+// growing group hold the same partial sum), across rows from a swizzle (xor 16) and a
+// permute (xor 32), so most steps cost no LDS round trip.
+__device__ __forceinline__ float group_sum(float v, int q) {
+  if (q >= 2) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+  if (q >= 4) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+  if (q >= 8) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false));
+  if (q >= 16) v += __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false));
+  if (q >= 32) v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  if (q >= 64) v += __shfl_xor(v, 32, 64);
+  return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
@@ -152,6 +167,25 @@ hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st);
 hipError_t launch_scan_pass(const ScanArgs& a, hipStream_t st);
 bool decode_supported(const mamba2_dims& dm);
 bool decode_grid_fits(const mamba2_dims& dm, int32_t num_seqs);
+
+// ------------------------------------------------------- snapshots and rollback
+// Boundaries E, 2E, ... strictly inside each run; packed sequence after sequence.
+constexpr int32_t kMaxVerifyRows = 16;
+int64_t snapshot_count(const mamba2_recurrent_batch* rb, int32_t E);
+int32_t snapshot_max_per_seq(const mamba2_recurrent_batch* rb, int32_t E);
+size_t verify_lds_bytes(const mamba2_dims& dm, int32_t max_rows);
+hipError_t launch_scan_verify(void* y, const void* xbc, const void* dt, const float* a_log,
+                              const float* dt_bias, const float* D, float* pool, float* snaps,
+                              const BatchDev& bd, const mamba2_dims& dm, int32_t max_rows, hipStream_t st);
+hipError_t launch_conv_snapshots(void* snaps, const void* x, const void* conv_state, const BatchDev& bd,
+                                 int32_t maxj, int32_t Dc, int32_t K, int32_t E, int32_t act, hipStream_t st);
+hipError_t launch_ssm_snapshots(const ScanArgs& a, float* snaps, int32_t maxj, int32_t E, hipStream_t st);
+hipError_t launch_commit(float* ssm_state, void* conv_state, const float* ssm_snaps, const void* conv_snaps,
+                         const int32_t* accepted, const BatchDev& bd, const mamba2_dims& dm, int32_t E,
+                         hipStream_t st);
+// Segment length of the chunked scan when every multiple of E must start a segment
+// (0: E is not a multiple of the path's segment unit).
+int32_t scan_segment_length_snap(const mamba2_recurrent_batch* rb, const mamba2_dims* d, int32_t E);
 
 // ------------------------------------------------------------------ timing
 // When enabled, kernel launches are bracketed by event records.

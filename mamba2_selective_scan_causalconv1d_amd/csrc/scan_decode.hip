@@ -102,11 +102,7 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(
 #pragma unroll
   for (int k = 0; k < KP; ++k) __builtin_nontemporal_store(hv[k], st + k * nthr + tid);
 #pragma unroll
-  for (int k = 0; k < KP; ++k) {
-    float s = part[k];
-    for (int o = Q4 >> 1; o >= 1; o >>= 1) s += __shfl_xor(s, o, 64);
-    part[k] = s;
-  }
+  for (int k = 0; k < KP; ++k) part[k] = group_sum(part[k], Q4);
   if ((tid % Q4) == 0) {
     const float d = Dp[h];
 #pragma unroll
@@ -115,6 +111,131 @@ __global__ __launch_bounds__(256) void scan_decode_kernel(
       Act<T>::store(y + (size_t)r * Di + (size_t)h * P + p, fmaf(d, xs[k], part[k]));
     }
   }
+}
+
+// A short run per sequence (1..kMaxVerifyRows rows, e.g. a speculative draft), in the
+// decode mapping: the block's state stays in registers over the run's rows, so it is read
+// and written once whatever the run length.  The run's B, C, x (the block's rows) and
+// per-row decay scalars are first staged in LDS ([L][2N + rb] and [L][2]), then the rows
+// are applied in order with the arithmetic of the one-row kernel (a run of one row gives
+// its results bit for bit).  snaps (may be null): the state after every row but the last,
+// [T - S][H][P][N], sequence r's first at row offset cu[r] - r.
+template <typename T, int KP>
+__global__ __launch_bounds__(256) void scan_verify_kernel(
+    T* __restrict__ y, const T* __restrict__ xbc, const T* __restrict__ dt,
+    const float* __restrict__ a_log, const float* __restrict__ dt_bias,
+    const float* __restrict__ Dp, float* __restrict__ pool, float* __restrict__ snaps,
+    const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ fresh,
+    int H, int P, int N, int G, int nblk) {
+  extern __shared__ float lds[];
+  const int hb = blockIdx.x % (H * nblk);
+  const int r = blockIdx.x / (H * nblk);
+  const int h = hb / nblk;
+  const int blk = hb - h * nblk;
+  const int tid = threadIdx.x;
+  const int nthr = blockDim.x;
+  const int Q4 = N >> 2;
+  const int Di = H * P;
+  const size_t Dc = (size_t)Di + 2 * (size_t)G * N;
+  const int g = h / (H / G);
+  const int f0 = blk * KP * nthr;
+  const int row0 = cu[r];
+  const int L = cu[r + 1] - row0;
+
+  const int rb = KP * nthr / Q4;
+  const int pfirst = f0 / Q4;
+  const int W = 2 * N + rb;
+  float* sw = lds;           // [L][W]: B, C, the block's x
+  float* sdt = lds + L * W;  // [L][2]: dt', exp(-exp(A_log) dt')
+  // The state goes out first, then the staging loads (eight per thread and pass, indices
+  // clamped into the run so that every load is unconditional) and the dt values: the
+  // workgroup pays one trip to memory for all of them.
+  const int cB = Di + g * N, cC = Di + (G + g) * N, cX = h * P + pfirst;
+  const int nst = L * W;
+  auto stage_load = [&](int i0, float* v) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int i = min(i0 + u * nthr, nst - 1);
+      const int t = i / W;
+      const int c = i - t * W;
+      const int ch = c < N ? cB + c : (c < 2 * N ? cC + (c - N) : cX + (c - 2 * N));
+      v[u] = Act<T>::load(xbc + (size_t)(row0 + t) * Dc + ch);
+    }
+  };
+  auto stage_store = [&](int i0, const float* v) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (i0 + u * nthr < nst) sw[i0 + u * nthr] = v[u];
+  };
+
+  f4v* st = reinterpret_cast<f4v*>(pool + ((size_t)slots[r] * H + h) * (size_t)P * N) + f0;
+  f4v hv[KP];
+  if (fresh[r]) {
+#pragma unroll
+    for (int k = 0; k < KP; ++k) hv[k] = f4v{0.f, 0.f, 0.f, 0.f};
+  } else {
+#pragma unroll
+    for (int k = 0; k < KP; ++k) hv[k] = __builtin_nontemporal_load(st + k * nthr + tid);
+  }
+  float v0[8];
+  stage_load(tid, v0);
+  const float dtv = Act<T>::load(dt + (size_t)(row0 + min(tid, L - 1)) * H + h);
+  const float bias = dt_bias[h];
+  const float A = __expf(a_log[h]);
+
+  stage_store(tid, v0);
+  if (tid < L) {
+    const float dtp = softplus_f32(dtv + bias);
+    sdt[2 * tid] = dtp;
+    sdt[2 * tid + 1] = __expf(-A * dtp);
+  }
+  for (int i0 = tid + 8 * nthr; i0 < nst; i0 += 8 * nthr) {  // runs of 8 rows and more (W <= 2 nthr)
+    float v[8];
+    stage_load(i0, v);
+    stage_store(i0, v);
+  }
+  __syncthreads();
+
+  const int n0 = 4 * (tid % Q4);
+  const float d = Dp[h];
+  const size_t hpn = (size_t)H * P * N;
+  f4v* snap0 = snaps ? reinterpret_cast<f4v*>(snaps + (size_t)(row0 - r) * hpn + (size_t)h * P * N) + f0
+                     : nullptr;
+  for (int t = 0; t < L; ++t) {
+    const float* rw = sw + t * W;
+    const float dtp = sdt[2 * t];
+    const float dA = sdt[2 * t + 1];
+    const float Bv[4] = {rw[n0], rw[n0 + 1], rw[n0 + 2], rw[n0 + 3]};
+    const float Cv[4] = {rw[N + n0], rw[N + n0 + 1], rw[N + n0 + 2], rw[N + n0 + 3]};
+    float part[KP], xs[KP];
+#pragma unroll
+    for (int k = 0; k < KP; ++k) {
+      xs[k] = rw[2 * N + (f0 + k * nthr + tid) / Q4 - pfirst];
+      const float c = dtp * xs[k];
+      f4v s = hv[k];
+      s.x = fmaf(c, Bv[0], s.x * dA);
+      s.y = fmaf(c, Bv[1], s.y * dA);
+      s.z = fmaf(c, Bv[2], s.z * dA);
+      s.w = fmaf(c, Bv[3], s.w * dA);
+      hv[k] = s;
+      part[k] = fmaf(s.x, Cv[0], fmaf(s.y, Cv[1], fmaf(s.z, Cv[2], s.w * Cv[3])));
+    }
+    if (snap0 && t + 1 < L) {
+#pragma unroll
+      for (int k = 0; k < KP; ++k) snap0[(size_t)t * (hpn / 4) + k * nthr + tid] = hv[k];
+    }
+#pragma unroll
+    for (int k = 0; k < KP; ++k) part[k] = group_sum(part[k], Q4);
+    if ((tid % Q4) == 0) {
+#pragma unroll
+      for (int k = 0; k < KP; ++k) {
+        const int p = (f0 + k * nthr + tid) / Q4;
+        Act<T>::store(y + (size_t)(row0 + t) * Di + (size_t)h * P + p, fmaf(d, xs[k], part[k]));
+      }
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < KP; ++k) __builtin_nontemporal_store(hv[k], st + k * nthr + tid);
 }
 
 // Block shape: 512 float4s (two per thread) when the head's state is a multiple of
@@ -148,7 +269,42 @@ hipError_t launch_t(void* y, const void* xbc, const void* dt, const float* a_log
   return hipSuccess;
 }
 
+template <typename T>
+hipError_t launch_verify_t(void* y, const void* xbc, const void* dt, const float* a_log, const float* dt_bias,
+                           const float* D, float* pool, float* snaps, const BatchDev& bd, const mamba2_dims& dm,
+                           int32_t max_rows, hipStream_t st) {
+  const DecodeShape sh = decode_shape(dm);
+  const dim3 grid((unsigned)((int64_t)bd.num_seqs * dm.nheads * sh.nblk));
+  const int rb = sh.kp * sh.nthr / (dm.d_state / 4);
+  const size_t shmem = (size_t)max_rows * (2 * dm.d_state + rb + 2) * sizeof(float);
+  if (sh.kp == 2) {
+    M2_LAUNCH("scan_verify", (scan_verify_kernel<T, 2>), grid, dim3(sh.nthr), shmem, st, (T*)y, (const T*)xbc,
+              (const T*)dt, a_log, dt_bias, D, pool, snaps, bd.cu_seqlens, bd.slots, bd.fresh, dm.nheads,
+              dm.headdim, dm.d_state, dm.ngroups, sh.nblk);
+  } else {
+    M2_LAUNCH("scan_verify", (scan_verify_kernel<T, 1>), grid, dim3(sh.nthr), shmem, st, (T*)y, (const T*)xbc,
+              (const T*)dt, a_log, dt_bias, D, pool, snaps, bd.cu_seqlens, bd.slots, bd.fresh, dm.nheads,
+              dm.headdim, dm.d_state, dm.ngroups, sh.nblk);
+  }
+  return hipSuccess;
+}
+
 }  // namespace
+
+// LDS the run staging takes for runs of up to max_rows rows.
+size_t verify_lds_bytes(const mamba2_dims& dm, int32_t max_rows) {
+  const DecodeShape sh = decode_shape(dm);
+  const int rb = sh.kp * sh.nthr / (dm.d_state / 4);
+  return (size_t)max_rows * (2 * dm.d_state + rb + 2) * sizeof(float);
+}
+
+hipError_t launch_scan_verify(void* y, const void* xbc, const void* dt, const float* a_log,
+                              const float* dt_bias, const float* D, float* pool, float* snaps,
+                              const BatchDev& bd, const mamba2_dims& dm, int32_t max_rows, hipStream_t st) {
+  if (dm.act_dtype == MAMBA2_DTYPE_BF16)
+    return launch_verify_t<bf16_t>(y, xbc, dt, a_log, dt_bias, D, pool, snaps, bd, dm, max_rows, st);
+  return launch_verify_t<float>(y, xbc, dt, a_log, dt_bias, D, pool, snaps, bd, dm, max_rows, st);
+}
 
 // Shapes the decode kernel covers: N % 4 == 0 with N/4 a power of two <= 64 (a state
 // row's lanes lie in one wavefront), and P*N/4 float4s per head either a multiple of

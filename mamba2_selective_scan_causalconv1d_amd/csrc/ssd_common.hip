@@ -119,6 +119,20 @@ int32_t scan_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims*
   return scan_mfma_segment_length(rb, d);
 }
 
+// With snapshots every E rows, segments must start at every multiple of E: the longest
+// segment length that divides E, is a multiple of the path's unit (the chunk of the MFMA
+// path, the one-chunk segment of the generic path) and is at most the usual length.
+int32_t scan_segment_length_snap(const mamba2_recurrent_batch* rb, const mamba2_dims* d, int32_t E) {
+  const bool mfma = scan_uses_mfma(d);
+  const int32_t usual = scan_segment_length(rb, d, mfma);
+  const int32_t unit = mfma ? 64 : scan_segment_length(rb, d, false);
+  if (E < 1 || E % unit != 0) return 0;
+  int32_t best = unit;
+  for (int32_t k = 1; (int64_t)k * unit <= usual; ++k)
+    if ((E / unit) % k == 0) best = k * unit;
+  return best;
+}
+
 ScanLayout scan_layout(const mamba2_recurrent_batch* rb, const mamba2_dims* d, int32_t seg_len) {
   ScanLayout L{};
   L.seg_len = seg_len;

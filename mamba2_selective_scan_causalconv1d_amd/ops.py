@@ -120,6 +120,49 @@ def gated_rmsnorm(dst, x, z, weight, groups: int, eps: float, stream=None):
     _lib.check(st, "mamba2_gated_rmsnorm")
 
 
+def snapshot_count(batch: RecurrentBatch, snap_every: int) -> int:
+    return int(LIB.mamba2_snapshot_count(batch.ref(), int(snap_every)))
+
+
+def conv1d_snap(dst, x, weight, bias, conv_state, conv_snaps, snap_every: int, batch: RecurrentBatch,
+                dims: Dims, stream=None):
+    st = LIB.mamba2_conv1d_snap(_ptr(dst), _ptr(x), _ptr(weight), _ptr(bias), _ptr(conv_state), _ptr(conv_snaps),
+                                int(snap_every), batch.ref(), ctypes.byref(dims), _stream(stream))
+    _lib.check(st, "mamba2_conv1d_snap")
+
+
+def scan_prefill_snap_workspace_bytes(batch: RecurrentBatch, dims: Dims, snap_every: int) -> int:
+    return int(LIB.mamba2_scan_prefill_snap_workspace_bytes(batch.ref(), ctypes.byref(dims), int(snap_every)))
+
+
+def scan_prefill_snap(dst, xbc, dt, a_log, dt_bias, D, ssm_state, ssm_snaps, snap_every: int,
+                      batch: RecurrentBatch, dims: Dims, workspace: Optional[torch.Tensor] = None, stream=None):
+    if workspace is None:
+        nbytes = scan_prefill_snap_workspace_bytes(batch, dims, snap_every)
+        workspace = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=xbc.device)
+    st = LIB.mamba2_scan_prefill_snap(_ptr(dst), _ptr(xbc), _ptr(dt), _ptr(a_log), _ptr(dt_bias), _ptr(D),
+                                      _ptr(ssm_state), _ptr(ssm_snaps), int(snap_every), batch.ref(),
+                                      ctypes.byref(dims), _ptr(workspace),
+                                      workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check(st, "mamba2_scan_prefill_snap")
+    return workspace
+
+
+def scan_verify(dst, xbc, dt, a_log, dt_bias, D, ssm_state, ssm_snaps, batch: RecurrentBatch, dims: Dims,
+                stream=None):
+    st = LIB.mamba2_scan_verify(_ptr(dst), _ptr(xbc), _ptr(dt), _ptr(a_log), _ptr(dt_bias), _ptr(D),
+                                _ptr(ssm_state), _ptr(ssm_snaps), batch.ref(), ctypes.byref(dims), _stream(stream))
+    _lib.check(st, "mamba2_scan_verify")
+
+
+def commit_snapshots(ssm_state, conv_state, ssm_snaps, conv_snaps, snap_every: int, accepted,
+                     batch: RecurrentBatch, dims: Dims, stream=None):
+    st = LIB.mamba2_commit_snapshots(_ptr(ssm_state), _ptr(conv_state), _ptr(ssm_snaps), _ptr(conv_snaps),
+                                     int(snap_every), _ptr(accepted), batch.ref(), ctypes.byref(dims),
+                                     _stream(stream))
+    _lib.check(st, "mamba2_commit_snapshots")
+
+
 def ssm_slot_bytes(dims: Dims) -> int:
     return int(LIB.mamba2_ssm_slot_bytes(ctypes.byref(dims)))
 

@@ -134,6 +134,36 @@ def test_entry_points_reject_before_launch(ops):
     assert L.mamba2_gated_rmsnorm(p, p, p, p, 2, -1.0, 4, 64, 1, None) == _lib.INVALID_ARGUMENT
     assert L.mamba2_gated_rmsnorm(p, p, p, p, 16, 1e-5, 4, 64, 1, None) == _lib.NOT_IMPLEMENTED
     assert L.mamba2_gated_rmsnorm(p, p, p, p, 1, 1e-5, 0, 64, 1, None) == _lib.OK
+    # snapshots, verify and commit: argument checks, then the batch, then what the kernels cover
+    mf = _dims(ops, nheads=4, headdim=64, d_state=128, ngroups=1)  # the MFMA path's shape
+    assert L.mamba2_snapshot_count(b.ref(), 2) == (3 - 1) // 2 + (4 - 1) // 2
+    assert L.mamba2_snapshot_count(b.ref(), 0) == -1
+    assert L.mamba2_conv1d_snap(p, p, p, p, p, p, 0, b.ref(), ctypes.byref(d), None) == _lib.INVALID_ARGUMENT
+    assert L.mamba2_conv1d_snap(p, p, p, p, p, None, 1, b.ref(), ctypes.byref(d), None) == \
+        _lib.INVALID_ARGUMENT  # snapshots to write, no buffer
+    assert L.mamba2_conv1d_snap(p, p, p, p, p, q, 1, b.ref(), ctypes.byref(d), None) == _lib.INVALID_ARGUMENT
+    shared = ops.RecurrentBatch([3, 4], [2, 2], [0, 0], device=None)
+    assert L.mamba2_conv1d_snap(p, p, p, p, p, p, 1, shared.ref(), ctypes.byref(d), None) == _lib.SLOT_SHARED
+    assert L.mamba2_scan_prefill_snap(p, p, p, p, p, p, p, p, 96, b.ref(), ctypes.byref(mf), p, 1 << 20,
+                                      None) == _lib.NOT_IMPLEMENTED  # 96 rows: not a multiple of 64
+    c2 = _dims(ops, chunk_size=2)  # the fp32 path, segments of 2 rows
+    assert L.mamba2_scan_prefill_snap(p, p, p, p, p, p, p, None, 2, b.ref(), ctypes.byref(c2), p, 1 << 20,
+                                      None) == _lib.INVALID_ARGUMENT  # snapshots to write, no buffer
+    assert L.mamba2_scan_prefill_snap_workspace_bytes(b.ref(), ctypes.byref(mf), 96) == 0
+    assert L.mamba2_scan_prefill_snap_workspace_bytes(b.ref(), ctypes.byref(mf), 128) > 0
+    dec = _dims(ops, nheads=4, headdim=64, d_state=128, ngroups=1)
+    long_run = ops.RecurrentBatch([17, 1], [0, 1], [0, 0], device=None)
+    assert L.mamba2_scan_verify(p, p, p, p, p, p, p, None, long_run.ref(), ctypes.byref(dec), None) == \
+        _lib.RUN_LENGTHS
+    assert L.mamba2_scan_verify(p, p, p, p, p, p, p, None, b.ref(), ctypes.byref(d), None) == \
+        _lib.NOT_IMPLEMENTED  # 16 vectors per head state, as the decode scan
+    assert L.mamba2_commit_snapshots(p, p, p, p, 0, p, b.ref(), ctypes.byref(d), None) == _lib.INVALID_ARGUMENT
+    assert L.mamba2_commit_snapshots(p, p, p, p, 1, None, b.ref(), ctypes.byref(d), None) == \
+        _lib.INVALID_ARGUMENT
+    assert L.mamba2_commit_snapshots(None, p, p, p, 1, p, b.ref(), ctypes.byref(d), None) == \
+        _lib.INVALID_ARGUMENT
+    assert L.mamba2_commit_snapshots(p, p, p, p, 1, p, shared.ref(), ctypes.byref(d), None) == _lib.SLOT_SHARED
+    assert L.mamba2_commit_snapshots(p, p, None, None, 1, p, b.ref(), ctypes.byref(d), None) == _lib.OK
     assert not host.any()
 
 
