@@ -212,11 +212,11 @@ def verify_batch(requests: int = 256, rows: int = 4) -> Workload:
     """Speculative verify: `requests` sequences of `rows` draft rows each on distinct slots of
     the decode workload's 512-slot pool (same shape and distributions), 10% fresh."""
     sh = SHAPE_DECODE
-    rng = np.random.default_rng(4)
+    rng = np.random.default_rng(5)
     slots = rng.permutation(sh.pool_slots)[:requests]
     fresh = np.zeros(requests, dtype=np.uint8)
     fresh[rng.permutation(requests)[:int(round(0.1 * requests))]] = 1
-    return make_prefill("verify%d_x%d" % (requests, rows), 4, sh, [rows] * requests, slots, fresh, rng=rng)
+    return make_prefill("verify%d_x%d" % (requests, rows), 5, sh, [rows] * requests, slots, fresh, rng=rng)
 
 
 def long_prefill(batch: int = 4, length: int = 16384) -> Workload:
