@@ -290,6 +290,31 @@ def run_decode(args, torch, ops, W, dev, e0, e1):
         times.append(e0.elapsed_time(e1))
         assert float(dout.float().sum().item()) == dref
     decode_us = 1e3 * float(np.median(times)) / len(dsteps)
+
+    # the same 64 steps captured once in a HIP graph and replayed (the launch pattern of a
+    # serving loop that captures its decode step); every replay is checked against the eager
+    # run's output, with eager work and synchronisations in between
+    graph_us = None
+    g = torch.cuda.CUDAGraph()
+    cpool.copy_(pristine_conv)
+    spool.copy_(pristine_ssm)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        decode_run()
+    gtimes = []
+    for _ in range(max(1, args.decode_reps)):
+        cpool.copy_(pristine_conv)
+        spool.copy_(pristine_ssm)
+        dout.zero_()
+        torch.cuda.synchronize()
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gtimes.append(e0.elapsed_time(e1))
+        assert float(dout.float().sum().item()) == dref, "graph replay differs from the eager run"
+    graph_us = 1e3 * float(np.median(gtimes)) / len(dsteps)
+    del g
     # per-kernel durations: one more run with the library's HIP events around every launch
     cpool.copy_(pristine_conv)
     spool.copy_(pristine_ssm)
@@ -309,6 +334,7 @@ def run_decode(args, torch, ops, W, dev, e0, e1):
     dec_roof = {"kernel": "scan_decode", "achieved_GBs": dec_bytes / (dkern["scan_decode"]["avg_us"] * 1e-6) / 1e9}
     dec_roof["frac_hbm"] = dec_roof["achieved_GBs"] / HBM_PEAK_GBS
 
+    dec_roof["graph_us_per_step"] = graph_us
     return decode_us, dkern, dec_roof, R, dsh, dsteps
 
 

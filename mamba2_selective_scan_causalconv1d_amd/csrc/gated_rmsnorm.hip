@@ -8,7 +8,7 @@
 // written once: a streaming HBM-bound kernel).  Each group owns a contiguous run of
 // L = 64 / groups lanes, and its 16-byte vectors are dealt to those lanes round robin,
 // so every load instruction touches whole 128-byte lines and the group's sum of squares
-// is an xor-shuffle over L lanes.  Four rows per workgroup, rows streamed with
+// is a DPP / swizzle reduction over L lanes.  Four rows per workgroup, rows streamed with
 // non-temporal accesses; a launch of fewer than 4096 rows (a decode step) uses one-wave
 // workgroups and loads the weights before the reduction.  Shapes that do not fit (groups not dividing 64, rows
 // not a multiple of 64 vectors) use the unit kernel: one wavefront per (row, group).
@@ -165,7 +165,7 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ 
       ss = fmaf(g[k][i], g[k][i], ss);
     }
   }
-  for (int o = lanes_per_group >> 1; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, 64);
+  ss = group_sum(ss, lanes_per_group);
   const float inv = rsqrtf(ss * inv_gs + eps);
 #pragma unroll
   for (int k = 0; k < NVPL; ++k) {
