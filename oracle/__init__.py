@@ -52,6 +52,11 @@ def lib() -> ctypes.CDLL:
         L.oracle_scan_snap.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
                                        i32, i32, i32, i32, i32, i32, vp, i32]
         L.oracle_commit.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32]
+        L.oracle_padded_runs.argtypes = [vp, i32, i32, vp, vp]
+        L.oracle_pack_rows.argtypes = [vp, vp, i32, i32, vp, i32, ctypes.c_size_t]
+        L.oracle_unpack_rows.argtypes = [vp, vp, i32, i32, vp, i32, ctypes.c_size_t]
+        for f in (L.oracle_padded_runs, L.oracle_pack_rows, L.oracle_unpack_rows):
+            f.restype = ctypes.c_int
         L.oracle_snapshot_count.argtypes = [i32, vp, i32]
         L.oracle_snapshot_count.restype = ctypes.c_longlong
         L.oracle_check_batch.argtypes = [i32, i32, vp, vp, i32, i32]
@@ -146,6 +151,32 @@ def commit(ssm_state, conv_state, ssm_snaps, conv_snaps, snap_every, accepted, r
     act = F32 if conv_state.dtype == np.float32 else BF16
     return lib().oracle_commit(_p(ssm_state), _p(conv_state), _p(ssm_snaps), _p(conv_snaps), int(snap_every),
                                _p(acc), len(rl), _p(rl), _p(sl), H, P, N, Dc, K1 + 1, act)
+
+
+def padded_runs(mask):
+    """(status, run lengths [B] int32, left_padded) of a [B, Lmax] mask."""
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    B, Lmax = m.shape
+    lens = np.zeros(B, dtype=np.int32)
+    left = np.zeros(1, dtype=np.int32)
+    st = lib().oracle_padded_runs(_p(m), B, Lmax, _p(lens), _p(left))
+    return st, lens, int(left[0])
+
+
+def pack_rows(dst, src, lens, left_padded) -> int:
+    """dst [T, ...] <- the real rows of src [B, Lmax, ...] (any dtype; rows copied as bytes)."""
+    B, Lmax = src.shape[0], src.shape[1]
+    rl = np.ascontiguousarray(lens, dtype=np.int32)
+    return lib().oracle_pack_rows(_p(dst), _p(src), B, Lmax, _p(rl), int(left_padded),
+                                  src[0, 0].nbytes)
+
+
+def unpack_rows(dst, src, lens, left_padded) -> int:
+    """dst [B, Lmax, ...] <- packed rows at their padded positions, zeros on padding."""
+    B, Lmax = dst.shape[0], dst.shape[1]
+    rl = np.ascontiguousarray(lens, dtype=np.int32)
+    return lib().oracle_unpack_rows(_p(dst), _p(src), B, Lmax, _p(rl), int(left_padded),
+                                    dst[0, 0].nbytes)
 
 
 def gated_rmsnorm(dst, x, z, weight, groups, eps) -> int:

@@ -427,6 +427,75 @@ int oracle_gated_rmsnorm(void* dst, const void* x, const void* z, const float* w
   return ORC_OK;
 }
 
+/* --------------------------------------------------------- padded batches */
+
+/*
+ * Padded batches: the layer entry of "Granite Mamba2 Inference Optimization"
+ * takes hidden states [B][Lmax] with an attention mask and must match across
+ * variable-length padded batches.  Reading: mask[b][j] nonzero marks a real
+ * row; the real rows of each batch row form one run, at the end of the row for
+ * every row (left padding) or at its start for every row (right padding); the
+ * run is the sequence (padding rows are not part of it).  A row without real
+ * rows, a gap inside a run, or a mix of the two sides is rejected.
+ */
+int oracle_padded_runs(const uint8_t* mask, int B, int Lmax, int32_t* lens, int32_t* left_padded) {
+  if (B < 0 || Lmax < 1 || (B > 0 && (mask == NULL || lens == NULL))) return ORC_INVALID_ARGUMENT;
+  int left_ok = 1, right_ok = 1;
+  for (int b = 0; b < B; ++b) {
+    const uint8_t* m = mask + (size_t)b * Lmax;
+    int n = 0, first = -1, last = -1;
+    for (int j = 0; j < Lmax; ++j)
+      if (m[j]) {
+        if (first < 0) first = j;
+        last = j;
+        ++n;
+      }
+    if (n == 0 || last - first + 1 != n) return ORC_INVALID_ARGUMENT;
+    lens[b] = n;
+    if (last != Lmax - 1) left_ok = 0;
+    if (first != 0) right_ok = 0;
+  }
+  if (!left_ok && !right_ok) return ORC_INVALID_ARGUMENT;
+  if (left_padded) *left_padded = left_ok && !right_ok ? 1 : 0;
+  return ORC_OK;
+}
+
+/* First padded position of row b's run. */
+static int run_start(int left_padded, int Lmax, int L) { return left_padded ? Lmax - L : 0; }
+
+/* dst[T][row_bytes] <- the real rows of src[B][Lmax][row_bytes], batch row after batch row. */
+int oracle_pack_rows(void* dst, const void* src, int B, int Lmax, const int32_t* lens, int left_padded,
+                     size_t row_bytes) {
+  size_t t = 0;
+  for (int b = 0; b < B; ++b) {
+    if (lens[b] < 1 || lens[b] > Lmax) return ORC_INVALID_ARGUMENT;
+    const int j0 = run_start(left_padded, Lmax, lens[b]);
+    for (int i = 0; i < lens[b]; ++i, ++t)
+      memcpy((unsigned char*)dst + t * row_bytes,
+             (const unsigned char*)src + ((size_t)b * Lmax + j0 + i) * row_bytes, row_bytes);
+  }
+  return ORC_OK;
+}
+
+/* dst[B][Lmax][row_bytes] <- the packed rows at their padded positions, zero bytes on padding. */
+int oracle_unpack_rows(void* dst, const void* src, int B, int Lmax, const int32_t* lens, int left_padded,
+                       size_t row_bytes) {
+  size_t t = 0;
+  for (int b = 0; b < B; ++b) {
+    if (lens[b] < 1 || lens[b] > Lmax) return ORC_INVALID_ARGUMENT;
+    const int j0 = run_start(left_padded, Lmax, lens[b]);
+    for (int j = 0; j < Lmax; ++j) {
+      unsigned char* d = (unsigned char*)dst + ((size_t)b * Lmax + j) * row_bytes;
+      if (j >= j0 && j < j0 + lens[b])
+        memcpy(d, (const unsigned char*)src + (t + (size_t)(j - j0)) * row_bytes, row_bytes);
+      else
+        memset(d, 0, row_bytes);
+    }
+    t += (size_t)lens[b];
+  }
+  return ORC_OK;
+}
+
 int oracle_max_threads(void) {
 #ifdef _OPENMP
   return omp_get_max_threads();

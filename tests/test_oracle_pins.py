@@ -8,7 +8,9 @@ the pages state, or a brute force on tiny inputs.  Sources:
   * "feat(mamba2): integrate model loading and recurrent inference" (InfiniLM PR #575),
     sections "Motivation" and "Notes for Reviewers" (prefix-state snapshots and speculative
     rollback, which that adaptation leaves out: a snapshot at boundary b is the state a run of
-    the first b rows leaves in the slot, pinned below against such runs).
+    the first b rows leaves in the slot, pinned below against such runs);
+  * "Granite Mamba2 Inference Optimization" (variable-length padded batches through the
+    layer's attention mask).
 """
 import json
 import math
@@ -518,3 +520,54 @@ def test_commit_rolls_back_to_accepted_prefix(orc, E):
         assert np.array_equal(sp_c[sl], s_ref), s
     for sl in set(range(wl.shape.pool_slots)) - set(int(v) for v in wl.slots):
         assert np.array_equal(cp_c[sl], wl.conv_pool[sl]) and np.array_equal(sp_c[sl], wl.ssm_pool[sl])
+
+
+# ------------------------------------------------------------ padded batches
+
+
+def _mask(lens, Lmax, left):
+    m = np.zeros((len(lens), Lmax), dtype=np.uint8)
+    for b, L in enumerate(lens):
+        if left:
+            m[b, Lmax - L:] = 1
+        else:
+            m[b, :L] = 1
+    return m
+
+
+@pytest.mark.parametrize("left", [0, 1])
+def test_padded_runs_match_mask_counts(orc, left):
+    """Run lengths are the mask's row sums and the side is where the runs sit (numpy)."""
+    rng = np.random.default_rng(90)
+    lens = rng.integers(1, 30, 7)
+    Lmax = int(lens.max()) + 3
+    st, got, side = oracle.padded_runs(_mask(lens, Lmax, left))
+    assert st == 0 and np.array_equal(got, lens) and side == left
+    full = np.ones((3, 5), dtype=np.uint8)  # no padding: either side, reported as right
+    assert oracle.padded_runs(full)[0] == 0
+
+
+def test_padded_runs_reject_gaps_empty_rows_and_mixed_sides(orc):
+    gap = _mask([4, 3], 6, 1)
+    gap[0, 3] = 0
+    assert oracle.padded_runs(gap)[0] == oracle.INVALID_ARGUMENT
+    assert oracle.padded_runs(np.zeros((2, 4), np.uint8))[0] == oracle.INVALID_ARGUMENT
+    mixed = np.array([[0, 1, 1], [1, 1, 0]], np.uint8)
+    assert oracle.padded_runs(mixed)[0] == oracle.INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("left", [0, 1])
+def test_pack_unpack_round_trip(orc, left):
+    """pack gathers exactly the masked rows in batch order (checked with numpy boolean
+    indexing); unpack puts them back and zeroes the padding."""
+    rng = np.random.default_rng(91)
+    lens = np.array([5, 1, 9, 2], dtype=np.int32)
+    Lmax = 11
+    m = _mask(lens, Lmax, left).astype(bool)
+    src = rng.integers(0, 2 ** 16, (4, Lmax, 6), dtype=np.uint16)
+    packed = np.zeros((int(lens.sum()), 6), np.uint16)
+    assert oracle.pack_rows(packed, src, lens, left) == 0
+    assert np.array_equal(packed, src[m])
+    back = np.full_like(src, 7)
+    assert oracle.unpack_rows(back, packed, lens, left) == 0
+    assert np.array_equal(back, np.where(m[:, :, None], src, 0))
