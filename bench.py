@@ -213,6 +213,7 @@ def main():
             ops.gated_rmsnorm(out, y, z, norm_w, sh.norm_groups, sh.eps)
 
         snaps = run_snapshots(args, torch, ops, W, dev, e0, e1, long_snap_step, batch, dims, sh, ms_per_step)
+        snaps["padded"] = run_padded(torch, ops, W, dev, e0, e1)
 
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
@@ -435,6 +436,44 @@ def run_snapshots(args, torch, ops, W, dev, e0, e1, long_snap_step, long_batch, 
                                        (long_sh.conv_kernel - 1) * long_sh.conv_dim * 2)}
     del lc, ls, ws
     return {"verify": verify, "prefill": prefill}
+
+
+def run_padded(torch, ops, W, dev, e0, e1):
+    """The padded-batch front end on the varlen batch laid out left-padded ([8, Lmax] rows):
+    pack of the xBC, z and dt rows into the packed layout and unpack of the output."""
+    vwl = W.varlen_prefill()
+    sh = vwl.shape
+    lens = vwl.run_lengths
+    Lmax = int(lens.max())
+    b = ops.RecurrentBatch(lens, vwl.slots, vwl.fresh, device=dev)
+    T, B = vwl.num_rows, len(lens)
+    bf = torch.bfloat16
+    srcs = [torch.zeros((B, Lmax, c), dtype=bf, device=dev) for c in (sh.conv_dim, sh.d_inner, sh.nheads)]
+    dsts = [torch.empty((T, c), dtype=bf, device=dev) for c in (sh.conv_dim, sh.d_inner, sh.nheads)]
+    outp = torch.empty((B, Lmax, sh.d_inner), dtype=bf, device=dev)
+
+    def pack():
+        for dst, src in zip(dsts, srcs):
+            ops.pack_rows(dst, src, 1, b)
+
+    def unpack():
+        ops.unpack_rows(outp, dsts[1], 1, b)
+
+    res = {"workload": "varlen8_left_padded", "rows": T, "padded_rows": B * Lmax}
+    for name, fn, nbytes in (("pack", pack, 2 * T * (sh.conv_dim + sh.d_inner + sh.nheads) * 2),
+                             ("unpack", unpack, (T + B * Lmax) * sh.d_inner * 2)):
+        for _ in range(5):
+            fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 20 * 1e3
+        res[name + "_us"] = us
+        res[name + "_GBs"] = nbytes / (us * 1e-6) / 1e9
+    return res
 
 
 def run_other_prefills(args, torch, ops, W, dev):

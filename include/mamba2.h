@@ -248,6 +248,38 @@ mamba2_status mamba2_commit_snapshots(float* ssm_state, void* conv_state, const 
                                       const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream);
 
 /*
+ * Padded batches.  The layer entry of "Granite Mamba2 Inference Optimization"
+ * takes hidden states [B, Lmax] with an attention mask and must match across
+ * variable-length padded batches.  Reading: the real rows of each batch row form
+ * one run, at the end of every row (left padding) or at the start of every row
+ * (right padding); that run is the row's sequence and the padding rows are not
+ * part of it.  The caller builds a RecurrentBatch from the run lengths (its slot
+ * and fresh flag per batch row, fresh = no previous state), packs the padded
+ * inputs, runs the path and unpacks the output.
+ */
+
+/* Host only: run lengths [batch] and the padding side (1 left, 0 right; a batch
+ * without padding reports 0) of a host mask [batch, max_len] (nonzero = real).
+ * MAMBA2_INVALID_ARGUMENT for a row without real rows, a gap inside a run, or
+ * runs on both sides. */
+mamba2_status mamba2_padded_runs(const uint8_t* mask, int32_t batch, int32_t max_len, int32_t* run_lengths,
+                                 int32_t* left_padded);
+
+/*
+ * dst [T, row] <- the real rows of src [S, max_len, row], batch row after batch
+ * row (pack), or dst [S, max_len, row] <- the packed rows at their padded
+ * positions with zero bytes on the padding (unpack).  Rows are copied as
+ * row_bytes bytes (any element type).  rb: the batch built from the run
+ * lengths (its slots and fresh flags are not used here); each run length must be
+ * at most max_len, else MAMBA2_RUN_LENGTHS.  device buffers; no alignment needed
+ * (the copy unit adapts to the row size and the pointers).
+ */
+mamba2_status mamba2_pack_rows(void* dst, const void* src, int64_t row_bytes, int32_t max_len, int32_t left_padded,
+                               const mamba2_recurrent_batch* rb, void* stream);
+mamba2_status mamba2_unpack_rows(void* dst, const void* src, int64_t row_bytes, int32_t max_len,
+                                 int32_t left_padded, const mamba2_recurrent_batch* rb, void* stream);
+
+/*
  * Host-only checks shared by every stateful call (no device access):
  * dims, then run lengths (each >= 1; decode != 0: each == 1; sum == num_rows),
  * then slot range, then slot sharing.  Returns the first failing status.

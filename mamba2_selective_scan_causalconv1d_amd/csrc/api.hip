@@ -78,6 +78,24 @@ mamba2_status from_hip(hipError_t e) { return e == hipSuccess ? MAMBA2_OK : MAMB
 // Shapes the prefill scan covers (both paths need N % 4 == 0 for 16-byte state access).
 bool scan_supported(const mamba2_dims* d) { return d->d_state % 4 == 0; }
 
+mamba2_status padded_call(bool pack, void* dst, const void* src, int64_t row_bytes, int32_t max_len,
+                          int32_t left_padded, const mamba2_recurrent_batch* rb, void* stream) {
+  if (!rb || row_bytes < 1 || max_len < 1 || (left_padded != 0 && left_padded != 1)) return MAMBA2_INVALID_ARGUMENT;
+  const int S = rb->num_seqs;
+  if (S < 0 || rb->num_rows < 0) return MAMBA2_INVALID_ARGUMENT;
+  if (S > 0 && (!rb->run_lengths || !rb->dev_cu_seqlens || !dst || !src)) return MAMBA2_INVALID_ARGUMENT;
+  int64_t sum = 0;
+  for (int s = 0; s < S; ++s) {
+    if (rb->run_lengths[s] < 1 || rb->run_lengths[s] > max_len) return MAMBA2_RUN_LENGTHS;
+    sum += rb->run_lengths[s];
+  }
+  if (sum != rb->num_rows) return MAMBA2_RUN_LENGTHS;
+  if ((int64_t)S * max_len * row_bytes >= ((int64_t)1 << 46)) return MAMBA2_INVALID_ARGUMENT;
+  if (S == 0) return MAMBA2_OK;
+  return from_hip(launch_padded(pack, dst, src, batch_dev(rb), max_len, left_padded, row_bytes,
+                                (hipStream_t)stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -274,6 +292,42 @@ mamba2_status mamba2_commit_snapshots(float* ssm_state, void* conv_state, const 
   if (rb->num_seqs == 0 || (!ssm_snaps && !conv_snaps)) return MAMBA2_OK;
   return from_hip(launch_commit(ssm_state, conv_state, ssm_snaps, conv_snaps, accepted, batch_dev(rb), *dims,
                                 snap_every, (hipStream_t)stream));
+}
+
+mamba2_status mamba2_padded_runs(const uint8_t* mask, int32_t batch, int32_t max_len, int32_t* run_lengths,
+                                 int32_t* left_padded) {
+  if (batch < 0 || max_len < 1 || (batch > 0 && (!mask || !run_lengths)) || !left_padded)
+    return MAMBA2_INVALID_ARGUMENT;
+  bool left_ok = true, right_ok = true;
+  for (int b = 0; b < batch; ++b) {
+    const uint8_t* m = mask + (size_t)b * max_len;
+    int n = 0, first = -1, last = -1;
+    for (int j = 0; j < max_len; ++j) {
+      if (m[j]) {
+        if (first < 0) first = j;
+        last = j;
+        ++n;
+      }
+    }
+    if (n == 0 || last - first + 1 != n) return MAMBA2_INVALID_ARGUMENT;
+    run_lengths[b] = n;
+    left_ok = left_ok && last == max_len - 1;
+    right_ok = right_ok && first == 0;
+  }
+  if (!left_ok && !right_ok) return MAMBA2_INVALID_ARGUMENT;
+  *left_padded = left_ok && !right_ok ? 1 : 0;
+  return MAMBA2_OK;
+}
+
+
+mamba2_status mamba2_pack_rows(void* dst, const void* src, int64_t row_bytes, int32_t max_len, int32_t left_padded,
+                               const mamba2_recurrent_batch* rb, void* stream) {
+  return padded_call(true, dst, src, row_bytes, max_len, left_padded, rb, stream);
+}
+
+mamba2_status mamba2_unpack_rows(void* dst, const void* src, int64_t row_bytes, int32_t max_len,
+                                 int32_t left_padded, const mamba2_recurrent_batch* rb, void* stream) {
+  return padded_call(false, dst, src, row_bytes, max_len, left_padded, rb, stream);
 }
 
 size_t mamba2_ssm_slot_bytes(const mamba2_dims* d) {

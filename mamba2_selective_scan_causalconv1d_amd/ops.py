@@ -163,6 +163,33 @@ def commit_snapshots(ssm_state, conv_state, ssm_snaps, conv_snaps, snap_every: i
     _lib.check(st, "mamba2_commit_snapshots")
 
 
+def padded_runs(mask: np.ndarray):
+    """(run lengths [B] int32, left_padded) of a host mask [B, Lmax] (nonzero = a real row)."""
+    m = np.ascontiguousarray(mask, dtype=np.uint8)
+    B, Lmax = m.shape
+    lens = np.zeros(B, dtype=np.int32)
+    left = np.zeros(1, dtype=np.int32)
+    st = LIB.mamba2_padded_runs(m.ctypes.data, B, Lmax, lens.ctypes.data, left.ctypes.data)
+    _lib.check(st, "mamba2_padded_runs")
+    return lens, int(left[0])
+
+
+def pack_rows(dst, src, left_padded: int, batch: RecurrentBatch, stream=None):
+    """dst [T, ...] <- the real rows of src [B, Lmax, ...]."""
+    row_bytes = src[0, 0].numel() * src.element_size()
+    st = LIB.mamba2_pack_rows(_ptr(dst), _ptr(src), row_bytes, int(src.shape[1]), int(left_padded), batch.ref(),
+                              _stream(stream))
+    _lib.check(st, "mamba2_pack_rows")
+
+
+def unpack_rows(dst, src, left_padded: int, batch: RecurrentBatch, stream=None):
+    """dst [B, Lmax, ...] <- packed rows at their padded positions, zeros on padding."""
+    row_bytes = dst[0, 0].numel() * dst.element_size()
+    st = LIB.mamba2_unpack_rows(_ptr(dst), _ptr(src), row_bytes, int(dst.shape[1]), int(left_padded), batch.ref(),
+                                _stream(stream))
+    _lib.check(st, "mamba2_unpack_rows")
+
+
 def ssm_slot_bytes(dims: Dims) -> int:
     return int(LIB.mamba2_ssm_slot_bytes(ctypes.byref(dims)))
 

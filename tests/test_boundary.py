@@ -164,6 +164,10 @@ def test_entry_points_reject_before_launch(ops):
         _lib.INVALID_ARGUMENT
     assert L.mamba2_commit_snapshots(p, p, p, p, 1, p, shared.ref(), ctypes.byref(d), None) == _lib.SLOT_SHARED
     assert L.mamba2_commit_snapshots(p, p, None, None, 1, p, b.ref(), ctypes.byref(d), None) == _lib.OK
+    # padded batches: the run finder agrees with the oracle's; pack / unpack check lengths first
+    assert L.mamba2_pack_rows(p, p, 64, 3, 1, b.ref(), None) == _lib.RUN_LENGTHS  # a run of 4 > max_len 3
+    assert L.mamba2_unpack_rows(p, p, 0, 8, 1, b.ref(), None) == _lib.INVALID_ARGUMENT
+    assert L.mamba2_pack_rows(p, p, 64, 8, 2, b.ref(), None) == _lib.INVALID_ARGUMENT
     assert not host.any()
 
 
@@ -191,3 +195,30 @@ def test_workspace_size(ops):
     assert n > 0 and n % 256 == 0
     bad = ops.RecurrentBatch([30, 5], [0, 0], [1, 0], device=None)
     assert ops.scan_prefill_workspace_bytes(bad, d) == 0
+
+
+def test_padded_runs_agree_with_oracle(ops):
+    """The library's host run finder against the oracle's on random masks: left, right and
+    no padding, gaps, empty rows, mixed sides."""
+    rng = np.random.default_rng(92)
+    for trial in range(60):
+        B, Lmax = int(rng.integers(1, 6)), int(rng.integers(1, 12))
+        lens = rng.integers(1, Lmax + 1, B)
+        left = int(rng.integers(0, 2))
+        m = np.zeros((B, Lmax), np.uint8)
+        for i, L in enumerate(lens):
+            if left:
+                m[i, Lmax - L:] = 1
+            else:
+                m[i, :L] = 1
+        if trial % 5 == 1:
+            m[rng.integers(0, B), rng.integers(0, Lmax)] ^= 1  # a gap, an empty row or a longer run
+        if trial % 7 == 2 and B > 1:
+            m[0] = m[0][::-1]  # possibly the other side
+        st_o, lens_o, left_o = oracle.padded_runs(m)
+        got = np.zeros(B, np.int32)
+        side = np.zeros(1, np.int32)
+        st = ops.LIB.mamba2_padded_runs(m.ctypes.data, B, Lmax, got.ctypes.data, side.ctypes.data)
+        assert st == st_o, (trial, m)
+        if st == 0:
+            assert np.array_equal(got, lens_o) and int(side[0]) == left_o
