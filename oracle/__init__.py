@@ -52,6 +52,8 @@ def lib() -> ctypes.CDLL:
         L.oracle_scan_snap.argtypes = [vp, vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, vp,
                                        i32, i32, i32, i32, i32, i32, vp, i32]
         L.oracle_commit.argtypes = [vp, vp, vp, vp, i32, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32]
+        L.oracle_linear.argtypes = [vp, vp, vp, i32, i32, i32, i32]
+        L.oracle_linear.restype = ctypes.c_int
         L.oracle_padded_runs.argtypes = [vp, i32, i32, vp, vp]
         L.oracle_pack_rows.argtypes = [vp, vp, i32, i32, vp, i32, ctypes.c_size_t]
         L.oracle_unpack_rows.argtypes = [vp, vp, i32, i32, vp, i32, ctypes.c_size_t]
@@ -151,6 +153,13 @@ def commit(ssm_state, conv_state, ssm_snaps, conv_snaps, snap_every, accepted, r
     act = F32 if conv_state.dtype == np.float32 else BF16
     return lib().oracle_commit(_p(ssm_state), _p(conv_state), _p(ssm_snaps), _p(conv_snaps), int(snap_every),
                                _p(acc), len(rl), _p(rl), _p(sl), H, P, N, Dc, K1 + 1, act)
+
+
+def linear(dst, x, w) -> int:
+    """dst [M, N] = x [M, K] . w [N, K]^T in double, one rounding to the activation type."""
+    M, K = x.shape
+    N = w.shape[0]
+    return lib().oracle_linear(_p(dst), _p(x), _p(w), M, N, K, _act_of(x))
 
 
 def padded_runs(mask):

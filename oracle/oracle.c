@@ -427,6 +427,28 @@ int oracle_gated_rmsnorm(void* dst, const void* x, const void* z, const float* w
   return ORC_OK;
 }
 
+/* ------------------------------------------------------------ projections */
+
+/*
+ * The projections on either side of the mixer path (a linear layer, one weight
+ * row per output feature): dst[m][n] = sum_k x[m][k] * w[n][k], summed in
+ * double from the stored values and rounded once to the activation type.
+ * Layouts: x [M][K], w [N][K], dst [M][N], all act.
+ */
+int oracle_linear(void* dst, const void* x, const void* w, int M, int N, int K, int act) {
+  if (M < 0 || N < 1 || K < 1 || (act != ORC_F32 && act != ORC_BF16)) return ORC_INVALID_ARGUMENT;
+#pragma omp parallel for schedule(static)
+  for (int m = 0; m < M; ++m) {
+    for (int n = 0; n < N; ++n) {
+      double acc = 0.0;
+      for (int k = 0; k < K; ++k)
+        acc += load_act(x, (size_t)m * K + k, act) * load_act(w, (size_t)n * K + k, act);
+      store_act(dst, (size_t)m * N + n, act, acc);
+    }
+  }
+  return ORC_OK;
+}
+
 /* --------------------------------------------------------- padded batches */
 
 /*

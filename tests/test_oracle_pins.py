@@ -10,7 +10,7 @@ the pages state, or a brute force on tiny inputs.  Sources:
     rollback, which that adaptation leaves out: a snapshot at boundary b is the state a run of
     the first b rows leaves in the slot, pinned below against such runs);
   * "Granite Mamba2 Inference Optimization" (variable-length padded batches through the
-    layer's attention mask).
+    layer's attention mask; the layer's projections around the path).
 """
 import json
 import math
@@ -571,3 +571,39 @@ def test_pack_unpack_round_trip(orc, left):
     back = np.full_like(src, 7)
     assert oracle.unpack_rows(back, packed, lens, left) == 0
     assert np.array_equal(back, np.where(m[:, :, None], src, 0))
+
+
+# ------------------------------------------------------------ projections
+
+
+@pytest.mark.parametrize("act", ["f32", "bf16"])
+def test_linear_identity_and_rank_one(orc, act):
+    """An identity weight returns x exactly; a rank-one product is K a_m b_n (closed form,
+    exact in both types for small integers)."""
+    rng = np.random.default_rng(96)
+    x = W.to_act(rng.standard_normal((5, 16)).astype(np.float32), act)
+    eye = W.to_act(np.eye(16, dtype=np.float32), act)
+    out = np.zeros_like(x)
+    assert oracle.linear(out, x, eye) == 0
+    assert np.array_equal(out, x)
+    a = rng.integers(-3, 4, 6).astype(np.float32)
+    b = rng.integers(-3, 4, 9).astype(np.float32)
+    xa = W.to_act(np.repeat(a[:, None], 8, axis=1), act)
+    wb = W.to_act(np.repeat(b[:, None], 8, axis=1), act)
+    out = np.zeros((6, 9), dtype=xa.dtype)
+    assert oracle.linear(out, xa, wb) == 0
+    assert np.array_equal(W.act_to_f32(out), 8 * np.outer(a, b))
+
+
+def test_linear_matches_numpy_matmul(orc):
+    """Against numpy's float64 matmul of the same bf16 values, rounded once to bf16 (another
+    summation order: equal up to one bf16 rounding flip)."""
+    rng = np.random.default_rng(97)
+    x = W.to_act(rng.standard_normal((33, 200)).astype(np.float32), "bf16")
+    w = W.to_act(rng.standard_normal((24, 200)).astype(np.float32), "bf16")
+    out = np.zeros((33, 24), np.uint16)
+    assert oracle.linear(out, x, w) == 0
+    ref = W.act_to_f32(x).astype(np.float64) @ W.act_to_f32(w).astype(np.float64).T
+    want = W.act_to_f32(W.to_act(ref.astype(np.float32), "bf16"))
+    got = W.act_to_f32(out)
+    assert np.max(np.abs(got - want) / (1 + np.abs(want))) <= 2 ** -8
