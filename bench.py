@@ -215,6 +215,12 @@ def main():
         snaps = run_snapshots(args, torch, ops, W, dev, e0, e1, long_snap_step, batch, dims, sh, ms_per_step)
         snaps["padded"] = run_padded(torch, ops, W, dev, e0, e1)
 
+    # ---------------------------------------------------------------- the whole layer
+    layer = None
+    if not (args.no_snapshots or args.no_decode):
+        layer = run_layer(args, torch, ops, dev, e0, e1, xbc, z, dt, xa, y, out, conv_w, conv_b, a_log, dt_bias,
+                          D, norm_w, conv_pool, ssm_pool, batch, dims, sh, ws)
+
     # ---------------------------------------------------------------- CPU oracle baseline
     cpu = None
     if not args.no_cpu_baseline:
@@ -247,6 +253,7 @@ def main():
         "decode_roofline": dec_roof,
         "other_workloads": others,
         "snapshots": snaps,
+        "layer": layer,
     }
     print(json.dumps(res))
 
@@ -436,6 +443,63 @@ def run_snapshots(args, torch, ops, W, dev, e0, e1, long_snap_step, long_batch, 
                                        (long_sh.conv_kernel - 1) * long_sh.conv_dim * 2)}
     del lc, ls, ws
     return {"verify": verify, "prefill": prefill}
+
+
+def run_layer(args, torch, ops, dev, e0, e1, xbc, z, dt, xa, y, out, conv_w, conv_b, a_log, dt_bias, D, norm_w,
+              conv_pool, ssm_pool, batch, dims, sh, ws):
+    """The whole mixer layer on the long-prefill batch: in_proj (z, xBC and dt from model-width
+    hidden states, three calls on row slices of one weight) -> the path -> out_proj, model
+    width Di / 2 = 1536, random weights of that architecture (scaled by 1/sqrt(fan-in))."""
+    T, Di, Dc, H = xbc.shape[0], sh.d_inner, sh.conv_dim, sh.nheads
+    d_model = Di // 2
+    g = torch.Generator(device=dev)
+    g.manual_seed(6)
+    hid = torch.randn((T, d_model), generator=g, device=dev).to(torch.bfloat16)
+    w_in = (torch.randn((Di + Dc + H, d_model), generator=g, device=dev) * d_model ** -0.5).to(torch.bfloat16)
+    w_out = (torch.randn((d_model, Di), generator=g, device=dev) * Di ** -0.5).to(torch.bfloat16)
+    res_out = torch.empty((T, d_model), dtype=torch.bfloat16, device=dev)
+
+    def in_proj():
+        ops.linear(z, hid, w_in[:Di])
+        ops.linear(xbc, hid, w_in[Di:Di + Dc])
+        ops.linear(dt, hid, w_in[Di + Dc:])
+
+    def step():
+        in_proj()
+        ops.conv1d(xa, xbc, conv_w, conv_b, conv_pool, batch, dims)
+        ops.scan_prefill(y, xa, dt, a_log, dt_bias, D, ssm_pool, batch, dims, workspace=ws)
+        ops.gated_rmsnorm(out, y, z, norm_w, sh.norm_groups, sh.eps)
+        ops.linear(res_out, out, w_out)
+
+    for _ in range(5):
+        step()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    ops.timing_enable(64)
+    step()
+    torch.cuda.synchronize()
+    recs = ops.timing_collect(64)
+    ops.timing_enable(0)
+    lin = [1e3 * t for name, t in recs if name == "linear"]  # z, xBC, dt, out_proj
+    shapes = [(Di, d_model), (Dc, d_model), (H, d_model), (d_model, Di)]
+    gemms = []
+    for (n, k), us in zip(shapes, lin):
+        fl = 2.0 * T * n * k
+        gemms.append({"N": n, "K": k, "us": us, "TFLOPs": fl / (us * 1e-6) / 1e12,
+                      "frac_mfma": fl / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
+    tot_fl = sum(2.0 * T * n * k for n, k in shapes)
+    tot_us = sum(lin)
+    # the sums keep the work from being optimised out and show the output is finite
+    assert torch.isfinite(res_out.float()).all()
+    return {"workload": "long_prefill_4x16384_layer", "d_model": d_model, "ms_per_step": ms,
+            "tokens_per_s": T / (ms * 1e-3), "gemms": gemms, "gemm_us": tot_us,
+            "gemm_TFLOPs": tot_fl / (tot_us * 1e-6) / 1e12,
+            "gemm_frac_mfma": tot_fl / (tot_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
 
 def run_padded(torch, ops, W, dev, e0, e1):

@@ -248,6 +248,23 @@ mamba2_status mamba2_commit_snapshots(float* ssm_state, void* conv_state, const 
                                       const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream);
 
 /*
+ * The projections around the path (a linear layer; the layer of "Granite Mamba2
+ * Inference Optimization" maps its hidden states to z, xBC and dt before the
+ * conv and the norm's output back to the model width after it):
+ *   dst[m, n] = sum_k x[m, k] * weight[n, k]   (fp32 accumulation, one rounding)
+ *   dst    device [rows, out_features] act (written; must not alias x or weight)
+ *   x      device [rows, in_features] act
+ *   weight device [out_features, in_features] act, one row per output feature
+ * A row slice of a weight is itself a weight, so in_proj is one call per output
+ * part (z, xBC, dt) on the matching rows of its weight, each writing its own
+ * contiguous tensor.  Covers bf16 with out_features and in_features multiples of
+ * 8 (and rows * in_features, rows * out_features, out_features * in_features
+ * below 2^31), else MAMBA2_NOT_IMPLEMENTED.
+ */
+mamba2_status mamba2_linear(void* dst, const void* x, const void* weight, int64_t rows, int64_t out_features,
+                            int64_t in_features, int32_t act_dtype, void* stream);
+
+/*
  * Padded batches.  The layer entry of "Granite Mamba2 Inference Optimization"
  * takes hidden states [B, Lmax] with an attention mask and must match across
  * variable-length padded batches.  Reading: the real rows of each batch row form

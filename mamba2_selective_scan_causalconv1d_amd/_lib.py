@@ -53,6 +53,7 @@ SIGNATURES = [
     ("mamba2_scan_prefill_snap_workspace_bytes", _sz, [_pb, _pd, _i32]),
     ("mamba2_scan_verify", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _pb, _pd, _vp]),
     ("mamba2_commit_snapshots", _i32, [_vp, _vp, _vp, _vp, _i32, _vp, _pb, _pd, _vp]),
+    ("mamba2_linear", _i32, [_vp, _vp, _vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, _i32, _vp]),
     ("mamba2_padded_runs", _i32, [_vp, _i32, _i32, _vp, _vp]),
     ("mamba2_pack_rows", _i32, [_vp, _vp, ctypes.c_int64, _i32, _i32, _pb, _vp]),
     ("mamba2_unpack_rows", _i32, [_vp, _vp, ctypes.c_int64, _i32, _i32, _pb, _vp]),

@@ -330,6 +330,17 @@ mamba2_status mamba2_unpack_rows(void* dst, const void* src, int64_t row_bytes, 
   return padded_call(false, dst, src, row_bytes, max_len, left_padded, rb, stream);
 }
 
+mamba2_status mamba2_linear(void* dst, const void* x, const void* weight, int64_t rows, int64_t out_features,
+                            int64_t in_features, int32_t act_dtype, void* stream) {
+  if (rows < 0 || out_features < 1 || in_features < 1) return MAMBA2_INVALID_ARGUMENT;
+  if (act_dtype != MAMBA2_DTYPE_F32 && act_dtype != MAMBA2_DTYPE_BF16) return MAMBA2_INVALID_ARGUMENT;
+  if (rows > 0 && (!dst || !x || !weight)) return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({dst, x, weight})) return MAMBA2_INVALID_ARGUMENT;
+  if (rows == 0) return MAMBA2_OK;
+  if (!linear_supported(rows, out_features, in_features, act_dtype)) return MAMBA2_NOT_IMPLEMENTED;
+  return from_hip(launch_linear(dst, x, weight, rows, out_features, in_features, (hipStream_t)stream));
+}
+
 size_t mamba2_ssm_slot_bytes(const mamba2_dims* d) {
   if (check_dims(d) != MAMBA2_OK) return 0;
   return (size_t)d->nheads * d->headdim * d->d_state * sizeof(float);

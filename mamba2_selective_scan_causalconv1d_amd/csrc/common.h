@@ -186,6 +186,10 @@ hipError_t launch_commit(float* ssm_state, void* conv_state, const float* ssm_sn
 // (0: E is not a multiple of the path's segment unit).
 int32_t scan_segment_length_snap(const mamba2_recurrent_batch* rb, const mamba2_dims* d, int32_t E);
 
+// ------------------------------------------------------------------ projections
+bool linear_supported(int64_t M, int64_t N, int64_t K, int32_t act);
+hipError_t launch_linear(void* dst, const void* x, const void* w, int64_t M, int64_t N, int64_t K, hipStream_t st);
+
 // ------------------------------------------------------------------ padded batches
 // pack: dst[T][row] <- real rows of src[B][Lmax][row]; unpack: the reverse, zeros on padding.
 hipError_t launch_padded(bool pack, void* dst, const void* src, const BatchDev& bd, int32_t Lmax, int32_t left,

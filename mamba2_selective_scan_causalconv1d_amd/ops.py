@@ -163,6 +163,15 @@ def commit_snapshots(ssm_state, conv_state, ssm_snaps, conv_snaps, snap_every: i
     _lib.check(st, "mamba2_commit_snapshots")
 
 
+def linear(dst, x, weight, stream=None):
+    """dst [rows, out] = x [rows, in] . weight [out, in]^T (weight may be a row slice)."""
+    rows, k = x.shape
+    n = weight.shape[0]
+    st = LIB.mamba2_linear(_ptr(dst), _ptr(x), _ptr(weight), int(rows), int(n), int(k), act_dtype_code(x),
+                           _stream(stream))
+    _lib.check(st, "mamba2_linear")
+
+
 def padded_runs(mask: np.ndarray):
     """(run lengths [B] int32, left_padded) of a host mask [B, Lmax] (nonzero = a real row)."""
     m = np.ascontiguousarray(mask, dtype=np.uint8)

@@ -164,6 +164,12 @@ def test_entry_points_reject_before_launch(ops):
         _lib.INVALID_ARGUMENT
     assert L.mamba2_commit_snapshots(p, p, p, p, 1, p, shared.ref(), ctypes.byref(d), None) == _lib.SLOT_SHARED
     assert L.mamba2_commit_snapshots(p, p, None, None, 1, p, b.ref(), ctypes.byref(d), None) == _lib.OK
+    # projections: sizes, dtype, alignment, then what the kernel covers
+    assert L.mamba2_linear(p, p, p, 4, 0, 8, 1, None) == _lib.INVALID_ARGUMENT
+    assert L.mamba2_linear(p, p, q, 4, 8, 8, 1, None) == _lib.INVALID_ARGUMENT
+    assert L.mamba2_linear(p, p, p, 4, 12, 8, 1, None) == _lib.NOT_IMPLEMENTED  # out_features % 8
+    assert L.mamba2_linear(p, p, p, 4, 8, 8, 0, None) == _lib.NOT_IMPLEMENTED  # fp32
+    assert L.mamba2_linear(p, p, p, 0, 8, 8, 1, None) == _lib.OK
     # padded batches: the run finder agrees with the oracle's; pack / unpack check lengths first
     assert L.mamba2_pack_rows(p, p, 64, 3, 1, b.ref(), None) == _lib.RUN_LENGTHS  # a run of 4 > max_len 3
     assert L.mamba2_unpack_rows(p, p, 0, 8, 1, b.ref(), None) == _lib.INVALID_ARGUMENT
