@@ -5,12 +5,14 @@
 //
 // MFMA tiling: a 256-thread workgroup computes a 128 x 128 block of dst, each wavefront a
 // 64 x 64 quarter as 4 x 4 tiles of v_mfma_f32_16x16x32_bf16.  K advances 64 at a time:
-// the x and w rows of the step (16 KiB each) are loaded into registers one step ahead,
-// written to a double-buffered LDS tile (rows padded to 144 bytes, so the 16 rows a
-// fragment read touches fall in distinct bank groups) and read back as MFMA fragments
+// the x and w rows of the step (16 KiB each) are loaded into registers two steps ahead
+// (two register sets, 64 KiB in flight per workgroup), written to a double-buffered LDS
+// tile (rows padded to 144 bytes, so the 16 rows a fragment read touches fall in distinct
+// bank groups) and read back as MFMA fragments
 // (lane l: row l % 16, k 8 (l / 16) .. +7), one barrier per step.  The product is formed
 // as (w x^T)^T: a lane then holds 4 consecutive output columns of one row, stored as 8
-// bytes.  Rows and k past the matrix edges are loaded from a clamped address and zeroed.
+// bytes.  Rows and k past the matrix edges are loaded from a clamped address and zeroed
+// when written to LDS.
 //
 // Workgroup -> tile: consecutive workgroups go to different XCDs (each with its own L2),
 // so the tiles are dealt XCD by XCD in row-block order: the workgroups resident on one XCD
@@ -51,31 +53,36 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(bf16_t* __restrict_
   const int m0 = (t / tiles_n) * BM;
   const int n0 = (t % tiles_n) * BN;
 
-  // global -> register staging: unit i = tid + 256 j is row i / 8, k 8 (i % 8) of the step
-  u32x4 ra[4], rb[4];
-  auto gload = [&](int k0) {
+  // global -> register staging: unit i = tid + 256 j is row i / 8, k 8 (i % 8) of the step.
+  // Steps past the end load the last step again (clamped, unconditional, so every step issues
+  // the same loads and the compiler's waits stay exact) and are never stored.
+  const int nk = (K + BK - 1) / BK;
+  // loads from clamped (always valid) addresses; the units past the edges are zeroed where
+  // the registers are written to LDS, so no load result is needed before then
+  auto gload = [&](u32x4* ra, u32x4* rb, int kt) {
+    const int k0 = min(kt, nk - 1) * BK;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = tid + 256 * j;
       const int row = i >> 3;
-      const int k = k0 + 8 * (i & 7);
-      const bool kin = k < K;
-      const int kc = kin ? k : K - 8;
-      const int ma = min(m0 + row, M - 1), nb = min(n0 + row, N - 1);
-      const u32x4 va = *reinterpret_cast<const u32x4*>(x + (size_t)ma * K + kc);
-      const u32x4 vb = *reinterpret_cast<const u32x4*>(w + (size_t)nb * K + kc);
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      ra[j] = (kin && m0 + row < M) ? va : z;
-      rb[j] = (kin && n0 + row < N) ? vb : z;
+      const int kc = min(k0 + 8 * (i & 7), K - 8);
+      // 32-bit element offsets (M K, N K < 2^31): a uniform base plus a 32-bit lane offset
+      const uint32_t oa = (uint32_t)min(m0 + row, M - 1) * (uint32_t)K + (uint32_t)kc;
+      const uint32_t ob = (uint32_t)min(n0 + row, N - 1) * (uint32_t)K + (uint32_t)kc;
+      ra[j] = *reinterpret_cast<const u32x4*>(x + oa);
+      rb[j] = *reinterpret_cast<const u32x4*>(w + ob);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](const u32x4* ra, const u32x4* rb, int kt, int buf) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = tid + 256 * j;
-      const int off = (i >> 3) * LDR + 8 * (i & 7);
-      *reinterpret_cast<u32x4*>(&sA[buf][off]) = ra[j];
-      *reinterpret_cast<u32x4*>(&sB[buf][off]) = rb[j];
+      const int row = i >> 3;
+      const bool kin = kt * BK + 8 * (i & 7) < K;
+      const int off = row * LDR + 8 * (i & 7);
+      *reinterpret_cast<u32x4*>(&sA[buf][off]) = (kin && m0 + row < M) ? ra[j] : z;
+      *reinterpret_cast<u32x4*>(&sB[buf][off]) = (kin && n0 + row < N) ? rb[j] : z;
     }
   };
 
@@ -85,14 +92,8 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(bf16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = (K + BK - 1) / BK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
   const int frow = lane & 15, fk = 8 * (lane >> 4);
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       u32x4 af[4], bf[4];
@@ -107,7 +108,23 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(bf16_t* __restrict_
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = mfma(bf[j], af[i], acc[i][j]);
     }
-    if (kt + 1 < nk) lstore(buf ^ 1);
+  };
+
+  // Two steps of loads in flight: registers 0 and 1 alternate, each filled two steps ahead.
+  u32x4 ra0[4], rb0[4], ra1[4], rb1[4];
+  gload(ra0, rb0, 0);
+  gload(ra1, rb1, 1);
+  lstore(ra0, rb0, 0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; kt += 2) {
+    gload(ra0, rb0, kt + 2);
+    compute(0);
+    if (kt + 1 < nk) lstore(ra1, rb1, kt + 1, 1);
+    __syncthreads();
+    if (kt + 1 >= nk) break;
+    gload(ra1, rb1, kt + 3);
+    compute(1);
+    if (kt + 2 < nk) lstore(ra0, rb0, kt + 2, 0);
     __syncthreads();
   }
 
