@@ -225,6 +225,20 @@ def long_prefill(batch: int = 4, length: int = 16384) -> Workload:
                         list(range(batch)), [1] * batch)
 
 
+def decay_span_prefill(batch: int = 4, length: int = 16384) -> Workload:
+    """Long-prefill shapes with A = exp(A_log) log-spaced over [1e-3, 30] across the heads and
+    every other sequence resuming from its slot: per 64-row chunk the log-decay sum runs from
+    about -0.05 (state carried over whole runs) through a few units (the state entering a chunk
+    scaled down by many orders over a few chunks) to hundreds (the carried state far below fp32
+    resolution of the chunk's own contribution)."""
+    sh = SHAPE_LONG
+    rng = np.random.default_rng(6)
+    wl = make_prefill("decay_span_%dx%d" % (batch, length), 6, sh, [length] * batch, list(range(batch)),
+                      [(i + 1) % 2 for i in range(batch)], rng=rng)
+    wl.a_log = np.log(np.geomspace(1e-3, 30.0, sh.nheads)).astype(np.float32)
+    return wl
+
+
 def by_index(i: int) -> Workload:
     return [tiny_fp32, layer_130m_prefill, varlen_prefill, decode_batch, long_prefill][i]()
 

@@ -121,6 +121,52 @@ def test_long_prefill_sampled(gpu):
     say("  norm out: %.3g of bar" % assert_close(gpu.f32(out_g), gpu.f32(out_o), BF16_BAR, "norm out"))
 
 
+def _chunk_log_decays(wl, h):
+    """Host-side sums of the log-decays -exp(A_log) softplus(dt + dt_bias) of head h over the
+    64-row chunks of each run (in double, from the workload's bf16 dt)."""
+    dt = (wl.dt[:, h].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    v = dt + float(wl.dt_bias[h])
+    dtp = np.where(v > 20.0, v, np.log1p(np.exp(np.minimum(v, 20.0))))
+    a = -np.exp(float(wl.a_log[h])) * dtp
+    sums, r0 = [], 0
+    for L in wl.run_lengths:
+        for c in range(0, int(L), 64):
+            sums.append(a[r0 + c:r0 + min(c + 64, int(L))].sum())
+        r0 += int(L)
+    return np.array(sums)
+
+
+def test_decay_regimes_long(gpu):
+    """4 x 16384 rows with A log-spaced over [1e-3, 30] across the 48 heads, two sequences
+    resuming: chunks whose log-decay sum is near zero (state carried across the whole run), a few
+    units (the carried state shrinks by 2^-20 over several chunks), tens (every chunk) and
+    hundreds (the carried state negligible).  The scan on eight heads spanning the range against
+    the oracle, all rows and final states."""
+    wl = W.decay_span_prefill()
+    sh = wl.shape
+    heads = [0, 7, 14, 20, 26, 33, 40, 47]
+    classes = np.zeros(4, dtype=np.int64)
+    for h in heads:
+        c = -_chunk_log_decays(wl, h)
+        classes += [np.sum(c < 1.0), np.sum((c >= 1.0) & (c < 13.8)), np.sum((c >= 13.8) & (c <= 60.0)),
+                    np.sum(c > 60.0)]
+    say("[%s] chunks by -log-decay: <1 %d, 1..13.8 %d, 13.8..60 %d, >60 %d" % ((wl.name,) + tuple(classes)))
+    assert np.all(classes >= 100), classes
+    b = gpu.batch_of(wl)
+    p = gpu.Params(wl)
+    xa_g, _ = gpu.gpu_conv(wl, wl.xbc, wl.conv_pool, b, p)
+    mask = np.zeros(sh.nheads, dtype=np.uint8)
+    mask[heads] = 1
+    y_o, sp_o = oracle_scan(wl, xa_g, head_mask=mask)
+    y_g, sp_g = gpu.gpu_scan(wl, xa_g, wl.dt, wl.ssm_pool, b, p)
+    P = sh.headdim
+    for h in heads:
+        cols = slice(h * P, (h + 1) * P)
+        f = assert_close(gpu.f32(y_g[:, cols]), gpu.f32(y_o[:, cols]), BF16_BAR, "y head %d" % h)
+        g = max(assert_close(sp_g[s, h], sp_o[s, h], F32_BAR, "state slot %d head %d" % (s, h)) for s in wl.slots)
+        say("  head %d (A %.3g): y %.3g of bar, states %.3g" % (h, np.exp(wl.a_log[h]), f, g))
+
+
 def test_decode_64_steps(gpu):
     """256 one-row requests on 512 slots, 10% fresh over dirty slots, 64 successive steps.
     Each step: conv on the step's rows (both sides), the decode scan on the GPU's conv output,
