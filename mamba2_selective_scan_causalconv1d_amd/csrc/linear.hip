@@ -3,7 +3,10 @@
 // feature), one rounding to bf16.  in_proj produces the z, xBC and dt columns (three calls
 // on row slices of one weight), out_proj maps the norm's output back to the model width.
 //
-// MFMA tiling: a 256-thread workgroup computes a 128 x 128 block of dst, each wavefront a
+// Two kernels: 256 x 256 tiles with direct-to-LDS copies (below) where M, N >= 256 and K is
+// a multiple of 64 (the layer's shapes), and 128 x 128 tiles for every other shape.
+//
+// 128 x 128 tiling: a 256-thread workgroup computes a 128 x 128 block of dst, each wavefront a
 // 64 x 64 quarter as 4 x 4 tiles of v_mfma_f32_16x16x32_bf16.  K advances 64 at a time:
 // the x and w rows of the step (16 KiB each) are loaded into registers two steps ahead
 // (two register sets, 64 KiB in flight per workgroup), written to a double-buffered LDS
@@ -146,35 +149,47 @@ __global__ __launch_bounds__(256, 2) void linear_bf16_kernel(bf16_t* __restrict_
 
 // ---------------------------------------------------------------- large tiles
 //
-// For M, N >= 256: a 512-thread workgroup computes a 256 x 256 block of dst, wavefront (wm, wn)
-// a 128 x 64 part of it (8 x 4 MFMA tiles, 128 accumulators per lane).  K advances 32 at a
-// time through four LDS stages of 32 KiB (the step's 256 x rows and 256 w rows, 64 bytes each):
-// the copies of step k + 3 are issued as step k is contracted, one barrier per step.  The
-// copies are buffer loads that write LDS directly (no registers, no LDS stores): each
-// instruction fills 1 KiB (16 rows x 4 units of 16 bytes) and each lane fetches the global unit
-// that lands in its slot.  Units are stored XOR-swizzled: unit u of tile row r sits in slot
-// u ^ ((r / 4) % 4), so the 16 rows a fragment read touches fall in distinct bank groups.
-// Rows past M or N and k past K read as zero (out-of-range buffer offsets).
+// For M, N >= 256 and K a multiple of 64: a 512-thread workgroup computes a 256 x 256 block of
+// dst, wavefront (wm, wn) a 128 x 64 part of it (8 x 4 MFMA tiles, 128 accumulators per lane).
+// K advances 64 at a time through two LDS stages of 64 KiB (the step's 256 x rows and 256 w
+// rows, 128 bytes each): the copies of step k + 1 are issued when step k starts, one barrier
+// per step.  The copies are buffer loads that write LDS directly (no registers, no LDS
+// stores): each instruction fills 1 KiB, 8 rows of 8 units of 16 bytes, so every lane group
+// fetches a whole 128-byte line, and each lane fetches the global unit that lands in its slot.
+// Unit u of tile row r sits in slot u ^ s(r % 16), s chosen so that the 16 rows a fragment
+// read touches fall in distinct bank groups.  Rows past M or N read as zero (out-of-range
+// buffer offsets).  The result leaves through LDS: each wavefront writes its bf16 values into
+// the tile, then every row is stored as full 512-byte runs, 16 bytes per lane (8-byte stores
+// straight from the accumulators, a quarter line each, were measured 5-20 % slower).
 
-constexpr int LBM = 256, LBN = 256, LBK = 32, LNS = 4;
+constexpr int LBM = 256, LBN = 256, LBK = 64, LNS = 2;
 
 #define M2_LDS_AS __attribute__((address_space(3)))
 typedef uint32_t u32x4r __attribute__((ext_vector_type(4)));
+
+// Buffer resource over `bytes` bytes from `base`.
+__device__ __forceinline__ u32x4r buf_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  return u32x4r{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+}
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is set here and used by nothing else
-// 16 bytes per lane from base + voff into LDS at lds + 16 lane (lds wave-uniform); offsets at or
-// past `bytes` write zeros.  The compiler does not see these LDS writes: they are waited for with
-// explicit vmcnt waits before the barrier that publishes them.
-__device__ __forceinline__ void dma16(const void* base, uint32_t bytes, const bf16_t* lds, uint32_t voff) {
-  const uint64_t a = (uint64_t)base;
-  const u32x4r rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes, 0x00020000u};
+// 16 bytes per lane from the resource at voff + soff into LDS at lds + 16 lane (lds
+// wave-uniform).  The range check sees voff only: lanes with voff at or past the resource's size
+// write zeros; the uniform soff moves the address.  The compiler does not see these LDS writes:
+// they are waited for with explicit vmcnt waits before the barrier that publishes them.
+__device__ __forceinline__ void dma16(const u32x4r& rsrc, const bf16_t* lds, uint32_t voff, uint32_t soff) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(const M2_LDS_AS void*)lds;
-  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
-               : "s"(m0), "v"(voff), "s"(rsrc)
+               : "s"(m0), "v"(voff), "s"(rsrc), "s"(soff)
                : "m0");
 }
 #pragma clang diagnostic pop
+
+// Slot of unit 0 of tile row r (r % 16) in 128-byte rows: the 16 rows of a fragment read of
+// one unit touch distinct bank groups in every 8-lane and every 16-lane pass.
+__device__ __forceinline__ int lswz(int r) { return (r & 6) | ((r ^ (r >> 3)) & 1); }
 
 // s_waitcnt with vmcnt <= n (n < 64) and no wait on the other counters
 template <int n>
@@ -186,8 +201,10 @@ __device__ __forceinline__ void wait_vm() {
 __global__ __launch_bounds__(512, 1) void linear_bf16_256_kernel(bf16_t* __restrict__ dst, const bf16_t* __restrict__ x,
                                                                  const bf16_t* __restrict__ w, int M, int N, int K,
                                                                  int tiles_n, int remap) {
-  __shared__ __attribute__((aligned(1024))) bf16_t sA[LNS][LBM * LBK];
-  __shared__ __attribute__((aligned(1024))) bf16_t sB[LNS][LBN * LBK];
+  // the operand stages, then (after the K loop) the 256 x 256 bf16 output tile
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * LNS * LBM * LBK];
+  auto SA = [&](int buf) { return smem + buf * (LBM * LBK); };
+  auto SB = [&](int buf) { return smem + (LNS + buf) * (LBM * LBK); };
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const int wm = wave >> 2, wn = wave & 3;
@@ -199,27 +216,30 @@ __global__ __launch_bounds__(512, 1) void linear_bf16_256_kernel(bf16_t* __restr
   }
   const int m0 = (t / tiles_n) * LBM;
   const int n0 = (t % tiles_n) * LBN;
-  const int nk = (K + LBK - 1) / LBK;
+  const int nk = K / LBK;
 
-  // copy instructions of this wave: tile rows 16 j .. 16 j + 15, j = wave and wave + 8, of x and w
+  // copy instruction a (0..3) of this wave fills tile rows 8 (wave + 8 a) .. +7; lane i: row
+  // + i / 8, slot i % 8.  The per-lane offsets are fixed; a step moves the uniform offset, and
+  // steps past the end use an empty resource (zeros, no memory access).
   const uint32_t bytes_x = (uint32_t)M * (uint32_t)K * 2u, bytes_w = (uint32_t)N * (uint32_t)K * 2u;
-  const int crow = lane >> 2;                      // row within the instruction's 16
-  const int cunit = (lane & 3) ^ (lane >> 4);      // global unit fetched into slot lane % 4
-  const int rx0 = m0 + 16 * wave + crow, rx1 = rx0 + 128;
-  const int rw0 = n0 + 16 * wave + crow, rw1 = rw0 + 128;
+  const u32x4r rsx = buf_rsrc(x, bytes_x), rsw = buf_rsrc(w, bytes_w), rs0 = buf_rsrc(x, 0u);
+  uint32_t vx[4], vw[4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int rr = 8 * (wave + 8 * a) + (lane >> 3);
+    const int u = (lane & 7) ^ lswz(rr & 15);
+    vx[a] = m0 + rr < M ? 2u * (uint32_t)(m0 + rr) * (uint32_t)K + 16u * (uint32_t)u : bytes_x;
+    vw[a] = n0 + rr < N ? 2u * (uint32_t)(n0 + rr) * (uint32_t)K + 16u * (uint32_t)u : bytes_w;
+  }
   auto issue = [&](int kt) {
     const int buf = kt & (LNS - 1);
-    const int k = kt * LBK + 8 * cunit;
-    const bool kin = kt < nk && k < K;
-    const uint32_t ko = 2u * (uint32_t)k;
-    const uint32_t ox0 = (kin && rx0 < M) ? 2u * (uint32_t)rx0 * (uint32_t)K + ko : bytes_x;
-    const uint32_t ox1 = (kin && rx1 < M) ? 2u * (uint32_t)rx1 * (uint32_t)K + ko : bytes_x;
-    const uint32_t ow0 = (kin && rw0 < N) ? 2u * (uint32_t)rw0 * (uint32_t)K + ko : bytes_w;
-    const uint32_t ow1 = (kin && rw1 < N) ? 2u * (uint32_t)rw1 * (uint32_t)K + ko : bytes_w;
-    dma16(x, bytes_x, &sA[buf][(16 * wave) * LBK], ox0);
-    dma16(x, bytes_x, &sA[buf][(16 * wave + 128) * LBK], ox1);
-    dma16(w, bytes_w, &sB[buf][(16 * wave) * LBK], ow0);
-    dma16(w, bytes_w, &sB[buf][(16 * wave + 128) * LBK], ow1);
+    const bool in = kt < nk;
+    const uint32_t so = in ? 128u * (uint32_t)kt : 0u;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      dma16(in ? rsx : rs0, &SA(buf)[(8 * (wave + 8 * a)) * LBK], vx[a], so);
+      dma16(in ? rsw : rs0, &SB(buf)[(8 * (wave + 8 * a)) * LBK], vw[a], so);
+    }
   };
 
   f32x4 acc[8][4];
@@ -228,45 +248,57 @@ __global__ __launch_bounds__(512, 1) void linear_bf16_256_kernel(bf16_t* __restr
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // fragment reads: lane l reads row l % 16 of a 16-row tile, unit l / 16, from slot
-  // (l / 16) ^ ((l % 16) / 4)
-  const int frag = (lane & 15) * LBK + 8 * ((lane >> 4) ^ ((lane & 15) >> 2));
-  const int fa = (wm * 128) * LBK + frag, fb = (wn * 64) * LBK + frag;
+  // fragment reads: lane l reads row l % 16 of a 16-row tile, unit 4 kk + l / 16
+  const int sw = lswz(lane & 15), kq = lane >> 4;
+  const int fa = (wm * 128 + (lane & 15)) * LBK, fb = (wn * 64 + (lane & 15)) * LBK;
+  auto rd = [&](u32x4 (&af)[8], u32x4 (&bf)[4], int kt, int kk) {
+    const int buf = kt & (LNS - 1);
+    const int so = 8 * ((4 * kk + kq) ^ sw);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const u32x4*>(&SA(buf)[fa + 16 * i * LBK + so]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(&SB(buf)[fb + 16 * j * LBK + so]);
+  };
 
   issue(0);
-  issue(1);
-  issue(2);
   for (int kt = 0; kt < nk; ++kt) {
-    wait_vm<8>();  // this wave's copies of step kt have landed (steps kt + 1, kt + 2 may be in flight)
-    __syncthreads();  // everyone's have; step kt - 1's stage is no longer read
-    issue(kt + 3);
-    const int buf = kt & (LNS - 1);
-    u32x4 af[8], bf[4];
+    wait_vm<0>();
+    __syncthreads();  // stage kt visible; stage kt - 1's buffer no longer read
+    issue(kt + 1);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) af[i] = *reinterpret_cast<const u32x4*>(&sA[buf][fa + 16 * i * LBK]);
+    for (int kk = 0; kk < 2; ++kk) {
+      u32x4 af[8], bf[4];
+      rd(af, bf, kt, kk);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) bf[j] = *reinterpret_cast<const u32x4*>(&sB[buf][fb + 16 * j * LBK]);
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i][j] = mfma(bf[j], af[i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma(bf[j], af[i], acc[i][j]);
+    }
   }
-  wait_vm<0>();  // the copies issued past the last step (zero fills) land before the workgroup ends
+  wait_vm<0>();  // the zero fill issued in the last step has landed
 
-  // lane l holds dst[row l % 16 of tile i][columns 4 (l / 16) .. +3 of tile j]
-  const int frow = lane & 15;
+  // lane l holds dst[row l % 16 of tile i][columns 4 (l / 16) .. +3 of tile j]; the tile row r
+  // keeps its 16-byte unit u at unit u ^ (r % 16) of its 512 bytes
+  __syncthreads();  // every wave is done reading the operand stages
+  char* const tile = reinterpret_cast<char*>(smem);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int m = m0 + wm * 128 + 16 * i + frow;
-    if (m >= M) continue;
+    const int r = wm * 128 + 16 * i + (lane & 15);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int n = n0 + wn * 64 + 16 * j + 4 * (lane >> 4);
-      if (n < N) {
-        const f32x4 o = acc[i][j];
-        *reinterpret_cast<uint2*>(dst + (size_t)m * N + n) = make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
-      }
+      const int c = wn * 64 + 16 * j + 4 * (lane >> 4);
+      const f32x4 o = acc[i][j];
+      *reinterpret_cast<uint2*>(tile + r * 512 + 16 * ((c >> 3) ^ (r & 15)) + 2 * (c & 7)) =
+          make_uint2(pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3]));
     }
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int q = 0; q < 16; ++q) {
+    const int r = wave * 32 + 2 * q + (lane >> 5), u = lane & 31;
+    const int m = m0 + r, n = n0 + 8 * u;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(tile + r * 512 + 16 * (u ^ (r & 15)));
+    if (m < M && n < N) *reinterpret_cast<u32x4*>(dst + (size_t)m * N + n) = v;
   }
 }
 
@@ -280,7 +312,7 @@ bool linear_supported(int64_t M, int64_t N, int64_t K, int32_t act) {
 }
 
 hipError_t launch_linear(void* dst, const void* x, const void* w, int64_t M, int64_t N, int64_t K, hipStream_t st) {
-  if (M >= LBM && N >= LBN) {
+  if (M >= LBM && N >= LBN && K % LBK == 0) {
     const int tm = (int)((M + LBM - 1) / LBM), tn = (int)((N + LBN - 1) / LBN);
     const int64_t nwg = (int64_t)tm * tn;
     const int remap = nwg % kXcds == 0 ? 1 : 0;
