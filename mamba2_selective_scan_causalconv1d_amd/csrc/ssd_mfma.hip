@@ -31,8 +31,10 @@
 // transposed operands (x^T, B^T) come from the gfx950 transposing LDS read.  Contractions
 // use permuted k orders that match the accumulator layout (lane group g holds rows 4 g..4 g+3
 // of a 16 x 16 tile): over chunk rows j, slot s of group g in k block m is
-// j = 32 m + 16 (s / 4) + 4 g + s % 4 (two stacked tiles); over state columns n in S C^T,
-// block kk pairs state tiles kk and kk + 4: n = 16 kk + 64 (s / 4) + 4 g + s % 4.
+// j = 32 m + 16 (s / 4) + 4 g + s % 4 (two stacked tiles).  State tile nb holds the columns
+// n = 32 (nb / 2) + 8 (R / 4) + 4 (nb % 2) + R % 4 in its rows R (the transposing reads of B
+// pick them), so that in S C^T block kk pairs tiles 2 kk and 2 kk + 1 and slot s of group g is
+// n = 32 kk + 8 g + s: a lane's C operand is one 16-byte read.
 #include "common.h"
 
 #include <type_traits>
@@ -162,8 +164,6 @@ __device__ __forceinline__ int swz_x(int row) {
 
 template <typename T>
 __device__ __forceinline__ u32x4 lds16(const T* p) { return *reinterpret_cast<const u32x4*>(p); }
-template <typename T>
-__device__ __forceinline__ u32x2 lds8(const T* p) { return *reinterpret_cast<const u32x2*>(p); }
 
 // Transposing read: within each 16-lane group, lane c receives column c of the four rows
 // whose 8-byte pieces the group's lanes address (lane l: row (l % 16) / 4, columns 4 (l % 4)).
@@ -176,8 +176,8 @@ __device__ __forceinline__ u32x2 tr8(const bf16_t* p) {
 // Lane (c, g) = (lane % 16, lane / 16); q = (lane % 16) / 4, b = (lane % 4) / 2.
 struct Lofs {
   int gt[2];  // B / C row 16 jb + c, elements 32 kk + 8 g..: + 16 jb*128, [kk%2], ^ 64 (kk/2)
-  int cf[4];  // C row 16 ib + c, elements 16 kk + 4 g.. (and ^ 64): + 16 ib*128, [kk]
-  int bt[4];  // B^T transposing read for column block nb: + row0*128, [nb%4], ^ 64 (nb/4)
+  int cf[4];  // C row 16 ib + c, elements 32 kk + 8 g .. +7: + 16 ib*128, [kk]
+  int bt;     // B^T transposing read of state tile nb: ^ 32 (nb / 2), + 4 (nb % 2)
   int xt[2];  // x^T transposing read for p block 32 ph + 16 t: + row0*64, [t]
 };
 __device__ __forceinline__ Lofs lane_offsets(int lane, int ph) {
@@ -187,9 +187,8 @@ __device__ __forceinline__ Lofs lane_offsets(int lane, int ph) {
 #pragma unroll
   for (int a = 0; a < 2; ++a) o.gt[a] = c * kN + (((4 * a + g) ^ sc) << 3);
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) o.cf[kk] = c * kN + (((2 * kk + (g >> 1)) ^ sc) << 3) + 4 * (g & 1);
-#pragma unroll
-  for (int nb = 0; nb < 4; ++nb) o.bt[nb] = (4 * g + q) * kN + (((2 * nb + b) ^ sq) << 3) + e;
+  for (int kk = 0; kk < 4; ++kk) o.cf[kk] = c * kN + (((4 * kk + g) ^ sc) << 3);
+  o.bt = (4 * g + q) * kN + (((lane & 3) ^ sq) << 3);
 #pragma unroll
   for (int t = 0; t < 2; ++t) o.xt[t] = (4 * g + q) * kP + (((4 * ph + 2 * t + b) ^ sx) << 3) + e;
   return o;
@@ -365,7 +364,7 @@ __device__ __forceinline__ void su_mfma(f32x4 (&S)[2][8], const u32x4 (&wh)[2][2
   for (int nb = 0; nb < 8; ++nb) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
-      const u32x4 bt = tr_frag<kN>(sB + (lo.bt[nb & 3] ^ (64 * (nb >> 2))), m);
+      const u32x4 bt = tr_frag<kN>(sB + ((lo.bt ^ (32 * (nb >> 1))) + 4 * (nb & 1)), m);
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
         S[t][nb] = mfma(bt, wh[t][m], (kFresh && m == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : S[t][nb]);
@@ -397,10 +396,11 @@ __device__ __forceinline__ void state_update(f32x4 (&S)[2][8], const u32x4 (&xt)
   }
 }
 
-// State tile (nb, t) of wave half ph: S[p][n..n+3], p = 32 ph + 16 t + c, n = 16 nb + 4 g.
+// State tile (nb, t) of wave half ph: S[p][n..n+3], p = 32 ph + 16 t + c,
+// n = 32 (nb / 2) + 8 g + 4 (nb % 2).
 __device__ __forceinline__ size_t state_elem(int ph, int t, int nb, int lane) {
   const int g = lane >> 4, c = lane & 15;
-  return (size_t)(32 * ph + 16 * t + c) * kN + 16 * nb + 4 * g;
+  return (size_t)(32 * ph + 16 * t + c) * kN + 32 * (nb >> 1) + 8 * g + 4 * (nb & 1);
 }
 
 // ---------------------------------------------------------------- segment states
@@ -658,16 +658,14 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
       u32x4 sh[2], sl[2];
 #pragma unroll
       for (int t = 0; t < 2; ++t) {
-        const f32x4 a = S[t][kk], b = S[t][kk + 4];
+        const f32x4 a = S[t][2 * kk], b = S[t][2 * kk + 1];
         const u32x4 sa = split4(a[0], a[1], a[2], a[3]), sb = split4(b[0], b[1], b[2], b[3]);
         sh[t] = u32x4{sa[0], sa[1], sb[0], sb[1]};
         sl[t] = u32x4{sa[2], sa[3], sb[2], sb[3]};
       }
 #pragma unroll
       for (int ib = 0; ib < 4; ++ib) {
-        const u32x2 c0 = lds8(sC + 16 * ib * kN + lo.cf[kk]);
-        const u32x2 c1 = lds8(sC + 16 * ib * kN + (lo.cf[kk] ^ 64));
-        const u32x4 cf = u32x4{c0.x, c0.y, c1.x, c1.y};
+        const u32x4 cf = lds16(sC + 16 * ib * kN + lo.cf[kk]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           Y[t][ib] = mfma(sh[t], cf, Y[t][ib]);
