@@ -7,29 +7,69 @@
 // [B][Lmax][row] tensor into [T][row]; unpack scatters [T][row] back to [B][Lmax][row] and
 // writes zeros on the padding.
 //
-// Both are byte copies: one thread per unit (16, 8, 4, 2 or 1 bytes, the largest that divides
-// the row and the pointers) of one row; grid (units of a row, padded position, batch row),
-// each dimension looping past the grid.  The packed row of padded position j of batch row b
-// is cu[b] + j - start(b), start(b) = Lmax - L(b) with left padding, else 0.
+// Both are byte copies.  The real rows of a batch row are contiguous in the padded layout as
+// well as in the packed one: packed unit e of batch row b (cu[b] units <= e < cu[b + 1] units,
+// counting row by row) is padded unit e + delta(b), delta(b) = (b Lmax + start(b) - cu[b]) units,
+// start(b) = Lmax - L(b) with left padding, else 0.  pack walks the packed units, unpack the
+// padded ones (zero outside [start(b), start(b) + L(b))), both flat over the whole tensor so the
+// work is spread evenly whatever the run lengths.  Units are 16, 8, 4, 2 or 1 bytes (the largest
+// that divides the row and the pointers), four per thread and step so that four loads are in
+// flight.
 #include "common.h"
 
 namespace m2 {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kPer = 4;  // units per thread and step
+
+// Batch row holding packed unit e, from a lower bound b (cu ascending).
+__device__ __forceinline__ int row_of(const int32_t* __restrict__ cu, int b, int64_t e, int64_t units) {
+  while ((int64_t)cu[b + 1] * units <= e) ++b;
+  return b;
+}
+// First batch row whose packed units reach past e (binary search, uniform over the workgroup).
+__device__ __forceinline__ int first_row(const int32_t* __restrict__ cu, int B, int64_t e, int64_t units) {
+  int lo = 0, hi = B - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if ((int64_t)cu[mid + 1] * units <= e) lo = mid + 1;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// Offset from packed unit e to its padded unit in batch row b.
+__device__ __forceinline__ int64_t pack_delta(const int32_t* __restrict__ cu, int b, int Lmax, int left,
+                                              int64_t units) {
+  const int L = cu[b + 1] - cu[b];
+  return ((int64_t)b * Lmax + (left ? Lmax - L : 0) - cu[b]) * units;
+}
 
 template <typename U>
 __global__ __launch_bounds__(kThreads) void pack_kernel(U* __restrict__ dst, const U* __restrict__ src,
                                                        const int32_t* __restrict__ cu, int B, int Lmax,
-                                                       int left, int units) {
-  for (int b = blockIdx.z; b < B; b += gridDim.z) {
-    const int row0 = cu[b];
-    const int L = cu[b + 1] - row0;
-    const int j0 = left ? Lmax - L : 0;
-    for (int i = blockIdx.y; i < L; i += gridDim.y) {
-      const U* s = src + ((size_t)b * Lmax + j0 + i) * units;
-      U* d = dst + (size_t)(row0 + i) * units;
-      for (int u = blockIdx.x * kThreads + threadIdx.x; u < units; u += gridDim.x * kThreads) d[u] = s[u];
+                                                       int left, int64_t units) {
+  const int64_t n = (int64_t)cu[B] * units;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * kPer;
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * kPer; c0 < n; c0 += stride) {
+    // the batch row at the chunk's start (uniform); units past its end look theirs up
+    const int b0 = first_row(cu, B, c0, units);
+    const int64_t end0 = (int64_t)cu[b0 + 1] * units, d0 = pack_delta(cu, b0, Lmax, left, units);
+    U v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t e = c0 + threadIdx.x + (int64_t)k * kThreads;
+      if (e < n) {
+        int64_t d = d0;
+        if (e >= end0) d = pack_delta(cu, row_of(cu, b0 + 1, e, units), Lmax, left, units);
+        v[k] = src[e + d];
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t e = c0 + threadIdx.x + (int64_t)k * kThreads;
+      if (e < n) dst[e] = v[k];
     }
   }
 }
@@ -37,19 +77,41 @@ __global__ __launch_bounds__(kThreads) void pack_kernel(U* __restrict__ dst, con
 template <typename U>
 __global__ __launch_bounds__(kThreads) void unpack_kernel(U* __restrict__ dst, const U* __restrict__ src,
                                                          const int32_t* __restrict__ cu, int B, int Lmax,
-                                                         int left, int units) {
-  for (int b = blockIdx.z; b < B; b += gridDim.z) {
-    const int row0 = cu[b];
-    const int L = cu[b + 1] - row0;
-    const int j0 = left ? Lmax - L : 0;
-    for (int j = blockIdx.y; j < Lmax; j += gridDim.y) {
-      U* d = dst + ((size_t)b * Lmax + j) * units;
-      if (j >= j0 && j < j0 + L) {  // uniform over the workgroup; padding rows read nothing
-        const U* s = src + (size_t)(row0 + (j - j0)) * units;
-        for (int u = blockIdx.x * kThreads + threadIdx.x; u < units; u += gridDim.x * kThreads) d[u] = s[u];
-      } else {
-        for (int u = blockIdx.x * kThreads + threadIdx.x; u < units; u += gridDim.x * kThreads) d[u] = U{};
+                                                         int left, int64_t units) {
+  const int64_t per_row = (int64_t)Lmax * units;
+  const int64_t n = (int64_t)B * per_row;
+  const int64_t stride = (int64_t)gridDim.x * kThreads * kPer;
+  // real units of batch row b: [first, first + L units), read from packed unit e - first + cu[b] units
+  auto span = [&](int b, int64_t& first, int64_t& last, int64_t& off) {
+    const int L = cu[b + 1] - cu[b];
+    first = ((int64_t)b * Lmax + (left ? Lmax - L : 0)) * units;
+    last = first + (int64_t)L * units;
+    off = (int64_t)cu[b] * units - first;
+  };
+  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * kPer; c0 < n; c0 += stride) {
+    const int b0 = (int)(c0 / per_row);
+    const int64_t end0 = (int64_t)(b0 + 1) * per_row;
+    int64_t f0, l0, o0;
+    span(b0, f0, l0, o0);
+    U v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t e = c0 + threadIdx.x + (int64_t)k * kThreads;
+      v[k] = U{};
+      if (e < n) {
+        int64_t f = f0, l = l0, o = o0;
+        if (e >= end0) {
+          int b = b0 + 1;
+          while ((int64_t)(b + 1) * per_row <= e) ++b;
+          span(b, f, l, o);
+        }
+        if (e >= f && e < l) v[k] = src[e + o];
       }
+    }
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int64_t e = c0 + threadIdx.x + (int64_t)k * kThreads;
+      if (e < n) dst[e] = v[k];
     }
   }
 }
@@ -59,9 +121,9 @@ unsigned clamp_grid(int64_t n, int64_t cap) { return (unsigned)(n < 1 ? 1 : (n >
 template <typename U>
 hipError_t launch_u(bool pack, void* dst, const void* src, const BatchDev& bd, int32_t Lmax, int32_t left,
                     int64_t row_bytes, hipStream_t st) {
-  const int units = (int)(row_bytes / (int64_t)sizeof(U));
-  const dim3 grid(clamp_grid((units + kThreads - 1) / kThreads, 64), clamp_grid(Lmax, 65535),
-                  clamp_grid(bd.num_seqs, 65535));
+  const int64_t units = row_bytes / (int64_t)sizeof(U);
+  const int64_t n = pack ? (int64_t)bd.num_rows * units : (int64_t)bd.num_seqs * Lmax * units;
+  const dim3 grid(clamp_grid((n + kThreads * kPer - 1) / (kThreads * kPer), 4096));
   if (pack) {
     M2_LAUNCH("pack_rows", pack_kernel<U>, grid, dim3(kThreads), 0, st, (U*)dst, (const U*)src, bd.cu_seqlens,
               bd.num_seqs, Lmax, left, units);
