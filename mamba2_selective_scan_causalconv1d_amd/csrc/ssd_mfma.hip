@@ -24,11 +24,13 @@
 // one group with 2 HB waves; wave (head hh, half ph) owns state rows p in [32 ph, 32 ph + 32)
 // of its head (all n) and the matching 32 columns of y.  The state lives in MFMA accumulators
 // as S^T tiles (n x p) whose lane layout is the A-operand layout of S C^T, so the state never
-// goes through LDS.  G^T = B C^T is computed once per chunk for all HB heads (one 16 x 16 tile
-// per wave, plus the last two tiles per head), scaled per head into M^T and shared through
-// LDS in operand order.  Chunk rows of B, C and x are copied global -> LDS by buffer loads
-// that write LDS directly (B and C double-buffered), XOR-swizzled in 16-byte units; the
-// transposed operands (x^T, B^T) come from the gfx950 transposing LDS read.  Contractions
+// goes through LDS.  G^T = B C^T is computed once per chunk for all HB heads (its first eight
+// 16 x 16 tiles dealt over the waves, the last two per head by that head's waves), scaled per
+// head into M^T and shared through LDS in operand order.  Chunk rows of B, C and x are copied
+// global -> LDS by buffer loads that write LDS directly, XOR-swizzled in 16-byte units, into
+// single tiles: the next chunk's copies are issued once the current tiles are no longer read
+// and land during the output phase, while the CU's other workgroup computes.  The transposed
+// operands (x^T, B^T) come from the gfx950 transposing LDS read.  Contractions
 // use permuted k orders that match the accumulator layout (lane group g holds rows 4 g..4 g+3
 // of a 16 x 16 tile): over chunk rows j, slot s of group g in k block m is
 // j = 32 m + 16 (s / 4) + 4 g + s % 4 (two stacked tiles).  State tile nb holds the columns
