@@ -101,15 +101,34 @@ __global__ __launch_bounds__(kThreads) void ssm_snap_kernel(float4* __restrict__
   }
 }
 
-// grid (x: 16-byte units of one sequence's SSM state then of its conv state, z: sequence).
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// dst[0, n) = src[0, n) in 16-byte units over the grid's x dimension, four units per thread and
+// step (four loads in flight), streaming (each unit is touched once).
+__device__ __forceinline__ void copy16(void* dst_, const void* src_, int n) {
+  u32x4v* __restrict__ dst = static_cast<u32x4v*>(dst_);
+  const u32x4v* __restrict__ src = static_cast<const u32x4v*>(src_);
+  constexpr int kPer = 4;
+  const int stride = gridDim.x * kThreads * kPer;
+  for (int u0 = blockIdx.x * kThreads * kPer + threadIdx.x; u0 < n; u0 += stride) {
+    u32x4v v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (u0 + k * kThreads < n) v[k] = __builtin_nontemporal_load(src + u0 + k * kThreads);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (u0 + k * kThreads < n) __builtin_nontemporal_store(v[k], dst + u0 + k * kThreads);
+  }
+}
+
+// grid (x: chunks of one sequence's SSM state and of its conv state, z: sequence).
 template <typename T>
 __global__ __launch_bounds__(kThreads) void commit_kernel(
-    float4* __restrict__ ssm_pool, T* __restrict__ conv_pool, const float4* __restrict__ ssm_snaps,
+    uint4* __restrict__ ssm_pool, T* __restrict__ conv_pool, const uint4* __restrict__ ssm_snaps,
     const T* __restrict__ conv_snaps, const int32_t* __restrict__ accepted, const int32_t* __restrict__ cu,
     const int32_t* __restrict__ slots, int S, int ssm_units, int Dc, int K1, int E) {
   constexpr int V = 16 / sizeof(T);
-  const int conv_units = conv_snaps ? K1 * Dc / V : 0;
-  const int su = ssm_snaps ? ssm_units : 0;
+  const int conv_units = K1 * Dc / V;
   for (int s = blockIdx.z; s < S; s += gridDim.z) {
     const int first = snap_first(cu, s, E);
     const int L = cu[s + 1] - cu[s];
@@ -117,15 +136,9 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
     if (m < 1 || m >= L || m % E != 0) continue;  // uniform over the workgroup
     const size_t idx = (size_t)first + m / E - 1;
     const size_t slot = (size_t)slots[s];
-    for (int u = blockIdx.x * kThreads + threadIdx.x; u < su + conv_units; u += gridDim.x * kThreads) {
-      if (u < su) {
-        ssm_pool[slot * ssm_units + u] = ssm_snaps[idx * ssm_units + u];
-      } else {
-        const size_t c = (size_t)(u - su) * V;
-        *reinterpret_cast<uint4*>(conv_pool + slot * K1 * Dc + c) =
-            *reinterpret_cast<const uint4*>(conv_snaps + idx * K1 * Dc + c);
-      }
-    }
+    if (ssm_snaps) copy16(ssm_pool + slot * ssm_units, ssm_snaps + idx * ssm_units, ssm_units);
+    if (conv_snaps)
+      copy16(conv_pool + slot * K1 * Dc, conv_snaps + idx * K1 * Dc, conv_units);
   }
 }
 
@@ -184,14 +197,14 @@ hipError_t launch_commit(float* ssm_state, void* conv_state, const float* ssm_sn
   const int V = dm.act_dtype == MAMBA2_DTYPE_BF16 ? 8 : 4;
   const int64_t ssm_units = (int64_t)dm.nheads * dm.headdim * dm.d_state / 4;
   const int64_t units = (ssm_snaps ? ssm_units : 0) + (conv_snaps ? (int64_t)K1 * Dc / V : 0);
-  const dim3 grid(clamp_grid((units + kThreads - 1) / kThreads, 1024), 1, clamp_grid(bd.num_seqs, 65535));
+  const dim3 grid(clamp_grid((units + 4 * kThreads - 1) / (4 * kThreads), 1024), 1, clamp_grid(bd.num_seqs, 65535));
   if (dm.act_dtype == MAMBA2_DTYPE_BF16) {
-    M2_LAUNCH("commit_snapshots", commit_kernel<bf16_t>, grid, dim3(kThreads), 0, st, (float4*)ssm_state,
-              (bf16_t*)conv_state, (const float4*)ssm_snaps, (const bf16_t*)conv_snaps, accepted, bd.cu_seqlens,
+    M2_LAUNCH("commit_snapshots", commit_kernel<bf16_t>, grid, dim3(kThreads), 0, st, (uint4*)ssm_state,
+              (bf16_t*)conv_state, (const uint4*)ssm_snaps, (const bf16_t*)conv_snaps, accepted, bd.cu_seqlens,
               bd.slots, bd.num_seqs, (int)ssm_units, Dc, K1, E);
   } else {
-    M2_LAUNCH("commit_snapshots", commit_kernel<float>, grid, dim3(kThreads), 0, st, (float4*)ssm_state,
-              (float*)conv_state, (const float4*)ssm_snaps, (const float*)conv_snaps, accepted, bd.cu_seqlens,
+    M2_LAUNCH("commit_snapshots", commit_kernel<float>, grid, dim3(kThreads), 0, st, (uint4*)ssm_state,
+              (float*)conv_state, (const uint4*)ssm_snaps, (const float*)conv_snaps, accepted, bd.cu_seqlens,
               bd.slots, bd.num_seqs, (int)ssm_units, Dc, K1, E);
   }
   return hipSuccess;
