@@ -48,6 +48,28 @@ __device__ int snap_first(const int32_t* __restrict__ cu, int s, int E) {
   return block_sum(v);
 }
 
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+
+// dst[0, n) = src[0, n) in 16-byte units over the grid's x dimension, four units per thread and
+// step (four loads in flight).  Stores stream (the copies are not read back soon); loads stream
+// too unless kKeepSrc (a source that later kernels read again).
+template <bool kKeepSrc>
+__device__ __forceinline__ void copy16(void* dst_, const void* src_, int n) {
+  u32x4v* __restrict__ dst = static_cast<u32x4v*>(dst_);
+  const u32x4v* __restrict__ src = static_cast<const u32x4v*>(src_);
+  constexpr int kPer = 4;
+  const int stride = gridDim.x * kThreads * kPer;
+  for (int u0 = blockIdx.x * kThreads * kPer + threadIdx.x; u0 < n; u0 += stride) {
+    u32x4v v[kPer];
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (u0 + k * kThreads < n) v[k] = kKeepSrc ? src[u0 + k * kThreads] : __builtin_nontemporal_load(src + u0 + k * kThreads);
+#pragma unroll
+    for (int k = 0; k < kPer; ++k)
+      if (u0 + k * kThreads < n) __builtin_nontemporal_store(v[k], dst + u0 + k * kThreads);
+  }
+}
+
 // grid (x: 16-byte units of a snapshot, y: boundary index j - 1, z: sequence), each
 // dimension looping when the batch is larger than the grid.
 template <typename T>
@@ -81,7 +103,7 @@ __global__ __launch_bounds__(kThreads) void conv_snap_kernel(
   }
 }
 
-// grid (x: float4 blocks of all heads' states, y: boundary index j - 1, z: sequence).  The
+// grid (x: chunks of all heads' states, y: boundary index j - 1, z: sequence).  The
 // boundary jE starts segment jE / seg_len of the sequence; its entering state is the
 // snapshot.
 __global__ __launch_bounds__(kThreads) void ssm_snap_kernel(float4* __restrict__ snaps,
@@ -94,30 +116,9 @@ __global__ __launch_bounds__(kThreads) void ssm_snap_kernel(float4* __restrict__
     const int L = cu[s + 1] - cu[s];
     const int seg0 = seq_info[s].x;
     for (int j = blockIdx.y + 1; (int64_t)j * E < L; j += gridDim.y) {
-      const float4* src = seg_state + (size_t)(seg0 + (int64_t)j * E / seg_len) * units;
-      float4* dst = snaps + (size_t)(first + j - 1) * units;
-      for (int u = blockIdx.x * kThreads + threadIdx.x; u < units; u += gridDim.x * kThreads) dst[u] = src[u];
+      copy16<true>(snaps + (size_t)(first + j - 1) * units, seg_state + (size_t)(seg0 + (int64_t)j * E / seg_len) * units,
+             units);
     }
-  }
-}
-
-typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
-
-// dst[0, n) = src[0, n) in 16-byte units over the grid's x dimension, four units per thread and
-// step (four loads in flight), streaming (each unit is touched once).
-__device__ __forceinline__ void copy16(void* dst_, const void* src_, int n) {
-  u32x4v* __restrict__ dst = static_cast<u32x4v*>(dst_);
-  const u32x4v* __restrict__ src = static_cast<const u32x4v*>(src_);
-  constexpr int kPer = 4;
-  const int stride = gridDim.x * kThreads * kPer;
-  for (int u0 = blockIdx.x * kThreads * kPer + threadIdx.x; u0 < n; u0 += stride) {
-    u32x4v v[kPer];
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      if (u0 + k * kThreads < n) v[k] = __builtin_nontemporal_load(src + u0 + k * kThreads);
-#pragma unroll
-    for (int k = 0; k < kPer; ++k)
-      if (u0 + k * kThreads < n) __builtin_nontemporal_store(v[k], dst + u0 + k * kThreads);
   }
 }
 
@@ -136,9 +137,9 @@ __global__ __launch_bounds__(kThreads) void commit_kernel(
     if (m < 1 || m >= L || m % E != 0) continue;  // uniform over the workgroup
     const size_t idx = (size_t)first + m / E - 1;
     const size_t slot = (size_t)slots[s];
-    if (ssm_snaps) copy16(ssm_pool + slot * ssm_units, ssm_snaps + idx * ssm_units, ssm_units);
+    if (ssm_snaps) copy16<false>(ssm_pool + slot * ssm_units, ssm_snaps + idx * ssm_units, ssm_units);
     if (conv_snaps)
-      copy16(conv_pool + slot * K1 * Dc, conv_snaps + idx * K1 * Dc, conv_units);
+      copy16<false>(conv_pool + slot * K1 * Dc, conv_snaps + idx * K1 * Dc, conv_units);
   }
 }
 
@@ -180,7 +181,7 @@ hipError_t launch_conv_snapshots(void* snaps, const void* x, const void* conv_st
 hipError_t launch_ssm_snapshots(const ScanArgs& a, float* snaps, int32_t maxj, int32_t E, hipStream_t st) {
   if (maxj == 0 || a.bd.num_seqs == 0) return hipSuccess;
   const int64_t units = (int64_t)a.dims.nheads * a.dims.headdim * a.dims.d_state / 4;
-  const dim3 grid(clamp_grid((units + kThreads - 1) / kThreads, 1024), clamp_grid(maxj, 65535),
+  const dim3 grid(clamp_grid((units + 4 * kThreads - 1) / (4 * kThreads), 1024), clamp_grid(maxj, 65535),
                   clamp_grid(a.bd.num_seqs, 65535));
   M2_LAUNCH("ssm_snapshots", ssm_snap_kernel, grid, dim3(kThreads), 0, st, (float4*)snaps,
             (const float4*)(a.ws + a.lay.off_seg_state), (const int2*)(a.ws + a.lay.off_seq_info),
