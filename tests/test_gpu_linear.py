@@ -46,6 +46,25 @@ def test_linear_ragged_shapes(gpu, M, N, K):
     assert_close(gpu.f32(ops.to_host(out)), gpu.f32(want), BF16_BAR, "linear %dx%dx%d" % (M, N, K))
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_linear_random_shapes(gpu, seed):
+    """Seeded random shapes across both tilings: M in [1, 700], N in [8, 800] and K in [8, 640]
+    (multiples of 8), every third case with K a multiple of 64 and M, N >= 256."""
+    ops = gpu.ops
+    rng = np.random.default_rng(500 + seed)
+    if seed % 3 == 0:
+        M, N, K = int(rng.integers(256, 701)), 8 * int(rng.integers(32, 101)), 64 * int(rng.integers(1, 11))
+    else:
+        M, N, K = int(rng.integers(1, 701)), 8 * int(rng.integers(1, 101)), 8 * int(rng.integers(1, 81))
+    x, w = _bf16(rng, (M, K)), _bf16(rng, (N, K), K ** -0.5)
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ops.linear(out, ops.to_device(x), ops.to_device(w))
+    torch.cuda.synchronize()
+    want = np.zeros((M, N), np.uint16)
+    assert oracle.linear(want, x, w) == 0
+    assert_close(gpu.f32(ops.to_host(out)), gpu.f32(want), BF16_BAR, "linear %dx%dx%d" % (M, N, K))
+
+
 @pytest.mark.parametrize("N,K", [(3328, 1536), (3072, 1536), (48, 1536), (1536, 3072)])
 def test_linear_layer_shapes_sampled(gpu, N, K):
     """65536 rows (the long-prefill batch); 96 rows sampled, incl. the first and last."""

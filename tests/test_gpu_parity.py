@@ -167,6 +167,21 @@ def test_decay_regimes_long(gpu):
         say("  head %d (A %.3g): y %.3g of bar, states %.3g" % (h, np.exp(wl.a_log[h]), f, g))
 
 
+@pytest.mark.parametrize("seed", range(3))
+def test_random_ragged_batches(gpu, seed):
+    """Seeded random batches on the MFMA path's shapes (8 heads x 64, d_state 128): 1 to 9
+    sequences of 1 to 700 rows, random fresh flags and distinct slots of a 12-slot pool; every
+    op against the oracle."""
+    rng = np.random.default_rng(900 + seed)
+    S = int(rng.integers(1, 10))
+    lens = [int(v) for v in rng.integers(1, 701, S)]
+    sh = W.Shape(nheads=8, headdim=64, d_state=128, ngroups=1, conv_kernel=4, chunk_size=256, norm_groups=2,
+                 pool_slots=12, act="bf16")
+    wl = W.random_prefill(910 + seed, sh, lens, fresh=[int(v) for v in rng.integers(0, 2, S)],
+                          slots=[int(v) for v in rng.permutation(12)[:S]])
+    _prefill_parity(gpu, wl)
+
+
 def test_decode_64_steps(gpu):
     """256 one-row requests on 512 slots, 10% fresh over dirty slots, 64 successive steps.
     Each step: conv on the step's rows (both sides), the decode scan on the GPU's conv output,
