@@ -257,8 +257,9 @@ mamba2_status mamba2_commit_snapshots(float* ssm_state, void* conv_state, const 
  *   weight device [out_features, in_features] act, one row per output feature
  * A row slice of a weight is itself a weight, so in_proj is one call per output
  * part (z, xBC, dt) on the matching rows of its weight, each writing its own
- * contiguous tensor.  Covers bf16 with out_features and in_features multiples of
- * 8 (and rows * in_features, rows * out_features, out_features * in_features
+ * contiguous tensor.  dst, x and weight 16-byte aligned, else
+ * MAMBA2_INVALID_ARGUMENT.  Covers bf16 with out_features and in_features multiples
+ * of 8 (and rows * in_features, rows * out_features, out_features * in_features
  * below 2^31), else MAMBA2_NOT_IMPLEMENTED.
  */
 mamba2_status mamba2_linear(void* dst, const void* x, const void* weight, int64_t rows, int64_t out_features,
