@@ -39,8 +39,11 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--decode-reps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=400.0,
+                    help="GPU time spent on untimed steps before the warm-up, so the clocks settle")
+    ap.add_argument("--reps", type=int, default=20, help="individually timed and digested prefill steps")
+    ap.add_argument("--decode-reps", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="the long prefill only (for counter runs)")
     ap.add_argument("--no-others", action="store_true", help="skip the smaller prefill workloads")
@@ -60,15 +63,52 @@ def kernel_bytes_flops(name, wl, nrows):
     resumed = int((wl.fresh == 0).sum())
     if name == "conv1d_silu":
         return 2 * T * Dc * a + (S + resumed) * (sh.conv_kernel - 1) * Dc * a, 0
-    if name in ("ssd_scan", "ssd_generic_scan"):
-        q = 64
-        flops = T * H * (N * (q + 1) / (H // G) + P * (q + 1) + 4 * N * P)
-        return T * (Dc + H + Di) * a + (S + resumed) * H * P * N * 4, flops
+    if name in ("ssd_scan", "ssd_generic_scan", "scan_op"):
+        return T * (Dc + H + Di) * a + (S + resumed) * H * P * N * 4, scan_flops(wl, T)[0]
     if name in ("gated_rmsnorm", "gated_rmsnorm_unit", "gated_rmsnorm_wide"):
         return 3 * T * Di * a + Di * 4, 0
     if name == "scan_decode":
         return (T * (Dc + H + Di) * a + (S + resumed) * H * P * N * 4), 6 * T * H * P * N
     return None, None
+
+
+def scan_flops(wl, T):
+    """Algorithmic and dense-tile flops of the chunked scan over T rows at the workload's chunk
+    length Q.  Per row and head: C B^T over the causal triangle N (Q + 1) / (H / G) (shared by
+    the heads of a group), the masked product with x P (Q + 1), the chunk state 2 N P and the
+    state's output term 2 N P.  Dense tiles (the upper triangle not skipped) double the two
+    triangular terms' Q / 2 to Q."""
+    sh = wl.shape
+    H, P, N, G, Q = sh.nheads, sh.headdim, sh.d_state, sh.ngroups, sh.chunk_size
+    alg = T * H * (N * (Q + 1) / (H // G) + P * (Q + 1) + 4 * N * P)
+    dense = T * H * (2 * N * Q / (H // G) + 2 * P * Q + 4 * N * P)
+    return alg, dense
+
+
+SCAN_KERNELS = ("scan_setup", "ssd_state", "scan_pass", "ssd_scan", "ssd_generic_state", "ssd_generic_scan",
+                "scan_prep", "ssd_chain")
+
+
+def digest(torch, tensors):
+    """64-bit digest of the exact bits of device tensors: per tensor, two int64 sums of its
+    32-bit words (plain, and weighted by a position pattern), combined on the host."""
+    h = hashlib.sha1()
+    for t in tensors:
+        flat = t.contiguous().view(-1)
+        if flat.element_size() == 2 and flat.numel() % 2:
+            h.update(("tail:%d;" % int(flat[-1:].view(torch.int16).item())).encode())
+            flat = flat[:-1]
+        w = flat.view(torch.int32)
+        n = w.numel()
+        s1 = s2 = 0
+        step = 1 << 24
+        pat = (torch.arange(step, device=w.device, dtype=torch.int64) % 1021) + 1
+        for i in range(0, n, step):
+            c = w[i:i + step].to(torch.int64)
+            s1 += int(c.sum().item())
+            s2 += int((c * pat[: c.numel()]).sum().item())
+        h.update(("%d:%d:%d;" % (n, s1, s2)).encode())
+    return h.hexdigest()[:16]
 
 
 def sources_sha1(names):
@@ -133,24 +173,57 @@ def main():
         ops.scan_prefill(y, xa, dt, a_log, dt_bias, D, ssm_pool, batch, dims, workspace=ws)
         ops.gated_rmsnorm(out, y, z, norm_w, sh.norm_groups, sh.eps)
 
-    # parity digest of the timed output (all-fresh batch: every step recomputes the same result)
+    slots = torch.from_numpy(wl.slots.astype(np.int64)).to(dev)
+
+    def step_digest():
+        # every output of a step and the states it leaves in its slots (all-fresh batch: every
+        # step recomputes the same bits)
+        return digest(torch, [xa, y, out, conv_pool.index_select(0, slots), ssm_pool.index_select(0, slots)])
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    # the digest of a first (untimed) run: every timed step must reproduce it
     step()
     torch.cuda.synchronize()
-    ref_digest = (float(out.float().sum().item()), float(y.float().abs().sum().item()))
+    ref_digest = step_digest()
 
-    # warm-up long enough for the clocks to settle (~40 ms of steps), then the timed steps
+    # clock settling: untimed steps worth settle_ms of GPU time, reported on their own
+    e0.record()
+    step()
+    e1.record()
+    torch.cuda.synchronize()
+    n_settle = max(1, int(args.settle_ms / max(e0.elapsed_time(e1), 1e-3)))
+    e0.record()
+    for _ in range(n_settle):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    settle = {"steps": n_settle + 1, "ms": e0.elapsed_time(e1)}
+
+    # the contract's timed region: W warm-up steps, then exactly K steps back to back
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()
     for _ in range(args.steps):
         step()
     e1.record()
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
-    digest = (float(out.float().sum().item()), float(y.float().abs().sum().item()))
-    assert digest == ref_digest, "timed output differs from the parity run: %s vs %s" % (digest, ref_digest)
+    assert step_digest() == ref_digest, "timed output differs from the parity run"
+
+    # repetitions: each step timed on its own with HIP events on the launch stream, then its
+    # outputs and states digested (outside the timed span) and compared with the first run's
+    rep_ms = []
+    for _ in range(max(1, args.reps)):
+        e0.record()
+        step()
+        e1.record()
+        torch.cuda.synchronize()
+        rep_ms.append(e0.elapsed_time(e1))
+        assert step_digest() == ref_digest, "a repetition's outputs or states differ from the parity run"
+    reps = {"n": len(rep_ms), "median_ms": float(np.median(rep_ms)), "min_ms": float(np.min(rep_ms)),
+            "max_ms": float(np.max(rep_ms)), "median_tokens_per_s": T / (float(np.median(rep_ms)) * 1e-3),
+            "digest": ref_digest, "digests_matched": len(rep_ms) + 1}
 
     # per-kernel durations: the same K steps again, with the library's HIP events recorded on
     # the launch stream around every kernel (they add a few us per launch, hence a pass of
@@ -182,9 +255,24 @@ def main():
         rooflines[k] = r
     dom = max(kernels, key=lambda k: kernels[k]["avg_us"] * kernels[k]["launches_per_step"])
     dr = rooflines.get(dom, {})
+    traffic = measured_traffic(dom)
     roofline = {"kernel": dom, "bound": "hbm", "achieved": dr.get("achieved_GBs"), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": dr.get("frac_hbm"), "traffic": measured_traffic(dom),
-                "avg_us": kernels[dom]["avg_us"]}
+                "unit": "GB/s", "frac": dr.get("frac_hbm"), "traffic": traffic,
+                "traffic_source": None if traffic is None else
+                "rocprofv3 FETCH_SIZE and WRITE_SIZE per launch, scaled by a plain copy's counts "
+                "(profiles/traffic_long_prefill_4x16384.txt, taken on these kernel sources)",
+                "avg_us": kernels[dom]["avg_us"],
+                "alg_bytes_scope": "the whole scan op's algorithmic bytes (x, B, C, dt read; y written; states)"}
+    # the scan op as a whole: every launch it makes, against its algorithmic bytes and flops
+    scan_us = sum(v["avg_us"] * v["launches_per_step"] for k, v in kernels.items() if k in SCAN_KERNELS)
+    sb, _ = kernel_bytes_flops("scan_op", wl, T)
+    sf, sfd = scan_flops(wl, T)
+    scan_op = {"kernels": [k for k in kernels if k in SCAN_KERNELS], "us_per_step": scan_us,
+               "alg_bytes": sb, "achieved_GBs": sb / (scan_us * 1e-6) / 1e9,
+               "frac_hbm": sb / (scan_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+               "alg_flops": sf, "dense_flops": sfd, "chunk_for_flops": sh.chunk_size,
+               "achieved_TFLOPs": sf / (scan_us * 1e-6) / 1e12,
+               "frac_mfma": sf / (scan_us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS}
 
     if args.copy_calibration_mb:
         # a plain copy of known size: its FETCH_SIZE / WRITE_SIZE give the counters' scale
@@ -197,9 +285,9 @@ def main():
         del src, dst
 
     # ---------------------------------------------------------------- decode
-    decode_us, dkern, dec_roof, R, dsh, dsteps = None, None, None, None, None, []
+    decode_us, dkern, dec_roof, R, dsh, dsteps, drep = None, None, None, None, None, [], None
     if not args.no_decode:
-        decode_us, dkern, dec_roof, R, dsh, dsteps = run_decode(args, torch, ops, W, dev, e0, e1)
+        decode_us, dkern, dec_roof, R, dsh, dsteps, drep = run_decode(args, torch, ops, W, dev, e0, e1)
 
     # ---------------------------------------------------------------- smaller prefills
     others = None if (args.no_others or args.no_decode) else run_other_prefills(args, torch, ops, W, dev)
@@ -233,7 +321,9 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": settle,
         "ms_per_step": ms_per_step,
+        "repetitions": reps,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -245,7 +335,9 @@ def main():
         "decode_us_per_step": decode_us,
         "decode_config": None if args.no_decode else
         {"workload": "decode_256x64", "requests": R, "pool_slots": dsh.pool_slots, "steps": len(dsteps)},
+        "decode_repetitions": drep,
         "roofline": roofline,
+        "scan_op": scan_op,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "rooflines": rooflines,
@@ -259,6 +351,10 @@ def main():
 
 
 def run_decode(args, torch, ops, W, dev, e0, e1):
+    """64 successive decode steps of 256 requests (conv step, decode scan, norm per step), timed
+    as one span per repetition; the pools are restored from pristine copies outside the span.
+    Each step writes its own output buffers, so after every repetition the outputs of all 64
+    steps and the final pools are digested and compared with the first run's."""
     d = ops.to_device
     dwl = W.decode_batch()
     dsh = dwl.shape
@@ -271,48 +367,54 @@ def run_decode(args, torch, ops, W, dev, e0, e1):
     b0 = ops.RecurrentBatch(dwl.run_lengths, dwl.slots, dwl.fresh, device=dev)
     b1 = ops.RecurrentBatch(dwl.run_lengths, dwl.slots, np.zeros_like(dwl.fresh), device=dev)
     R = len(dwl.run_lengths)
-    dxa = torch.empty((R, dsh.conv_dim), dtype=torch.bfloat16, device=dev)
-    dy = torch.empty((R, dsh.d_inner), dtype=torch.bfloat16, device=dev)
+    nS = len(dsteps)
+    dxa = torch.empty((nS, R, dsh.conv_dim), dtype=torch.bfloat16, device=dev)
+    dy = torch.empty((nS, R, dsh.d_inner), dtype=torch.bfloat16, device=dev)
     dout = torch.empty_like(dy)
 
     def decode_run():
         cw, cb, al, db, DD, nw = dparams
         for i, (x, zz, dd) in enumerate(dsteps):
             b = b0 if i == 0 else b1
-            ops.conv1d(dxa, x, cw, cb, cpool, b, ddims)
-            ops.scan_decode(dy, dxa, dd, al, db, DD, spool, b, ddims)
-            ops.gated_rmsnorm(dout, dy, zz, nw, dsh.norm_groups, dsh.eps)
+            ops.conv1d(dxa[i], x, cw, cb, cpool, b, ddims)
+            ops.scan_decode(dy[i], dxa[i], dd, al, db, DD, spool, b, ddims)
+            ops.gated_rmsnorm(dout[i], dy[i], zz, nw, dsh.norm_groups, dsh.eps)
 
-    decode_run()  # warm-up on a scratch copy of the pools
-    torch.cuda.synchronize()
-    dref = float(dout.float().sum().item())
-    times = []
-    for _ in range(max(1, args.decode_reps)):
+    def run_digest():
+        return digest(torch, [dxa, dy, dout, cpool, spool])
+
+    def restore():
         cpool.copy_(pristine_conv)
         spool.copy_(pristine_ssm)
         torch.cuda.synchronize()
+
+    restore()
+    decode_run()  # warm-up, and the reference digest
+    torch.cuda.synchronize()
+    dref = run_digest()
+    times = []
+    for _ in range(max(1, args.decode_reps)):
+        restore()
         e0.record()
         decode_run()
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
-        assert float(dout.float().sum().item()) == dref
-    decode_us = 1e3 * float(np.median(times)) / len(dsteps)
+        assert run_digest() == dref, "a decode repetition differs from the first run"
+    decode_us = 1e3 * float(np.median(times)) / nS
+    drep = {"n": len(times), "median_us_per_step": decode_us, "min_us_per_step": 1e3 * float(np.min(times)) / nS,
+            "max_us_per_step": 1e3 * float(np.max(times)) / nS, "digest": dref, "digests_matched": len(times) + 1}
 
     # the same 64 steps captured once in a HIP graph and replayed (the launch pattern of a
     # serving loop that captures its decode step); every replay is checked against the eager
-    # run's output, with eager work and synchronisations in between
-    graph_us = None
+    # run's digest, with eager work and synchronisations in between
     g = torch.cuda.CUDAGraph()
-    cpool.copy_(pristine_conv)
-    spool.copy_(pristine_ssm)
-    torch.cuda.synchronize()
+    restore()
     with torch.cuda.graph(g):
         decode_run()
     gtimes = []
     for _ in range(max(1, args.decode_reps)):
-        cpool.copy_(pristine_conv)
-        spool.copy_(pristine_ssm)
+        restore()
         dout.zero_()
         torch.cuda.synchronize()
         e0.record()
@@ -320,12 +422,11 @@ def run_decode(args, torch, ops, W, dev, e0, e1):
         e1.record()
         torch.cuda.synchronize()
         gtimes.append(e0.elapsed_time(e1))
-        assert float(dout.float().sum().item()) == dref, "graph replay differs from the eager run"
-    graph_us = 1e3 * float(np.median(gtimes)) / len(dsteps)
+        assert run_digest() == dref, "graph replay differs from the eager run"
+    graph_us = 1e3 * float(np.median(gtimes)) / nS
     del g
     # per-kernel durations: one more run with the library's HIP events around every launch
-    cpool.copy_(pristine_conv)
-    spool.copy_(pristine_ssm)
+    restore()
     ops.timing_enable(4096)
     decode_run()
     torch.cuda.synchronize()
@@ -334,16 +435,23 @@ def run_decode(args, torch, ops, W, dev, e0, e1):
     dper = {}
     for name, ms in drecs:
         dper.setdefault(name, []).append(ms)
-    dkern = {k: {"avg_us": 1e3 * float(np.mean(v)), "launches_per_step": len(v) / len(dsteps)}
+    dkern = {k: {"avg_us": 1e3 * float(np.mean(v)), "launches_per_step": len(v) / nS}
              for k, v in dper.items()}
-    dec_bytes, _ = kernel_bytes_flops("scan_decode", dwl, R)
     # steps 1..63 read every slot (none fresh): algorithmic bytes of a resumed step
     dec_bytes = R * (dsh.conv_dim + dsh.nheads + dsh.d_inner) * 2 + 2 * R * dsh.nheads * dsh.headdim * dsh.d_state * 4
-    dec_roof = {"kernel": "scan_decode", "achieved_GBs": dec_bytes / (dkern["scan_decode"]["avg_us"] * 1e-6) / 1e9}
-    dec_roof["frac_hbm"] = dec_roof["achieved_GBs"] / HBM_PEAK_GBS
-
+    # the whole step, fused-mixer count (inputs xBC, dt, z read, the output written, both states
+    # read and written once): 3,204,704 bytes per request at this shape
+    step_bytes = R * (2 * dsh.nheads * dsh.headdim * dsh.d_state * 4 + 2 * (dsh.conv_kernel - 1) * dsh.conv_dim * 2 +
+                      (dsh.conv_dim + dsh.nheads + 2 * dsh.d_inner) * 2)
+    skern = [k for k in dkern if k.startswith("scan_decode")]
+    dec_roof = {"kernel": skern[0] if skern else None,
+                "achieved_GBs": dec_bytes / (dkern[skern[0]]["avg_us"] * 1e-6) / 1e9 if skern else None,
+                "step_alg_bytes": step_bytes, "step_GBs": step_bytes / (decode_us * 1e-6) / 1e9,
+                "step_frac_hbm": step_bytes / (decode_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+    if skern:
+        dec_roof["frac_hbm"] = dec_roof["achieved_GBs"] / HBM_PEAK_GBS
     dec_roof["graph_us_per_step"] = graph_us
-    return decode_us, dkern, dec_roof, R, dsh, dsteps
+    return decode_us, dkern, dec_roof, R, dsh, dsteps, drep
 
 
 def run_snapshots(args, torch, ops, W, dev, e0, e1, long_snap_step, long_batch, long_dims, long_sh,
@@ -596,33 +704,80 @@ def run_other_prefills(args, torch, ops, W, dev):
     return res
 
 
+def _oracle_prefill(oracle, wl, sub_rows=None):
+    """conv -> scan -> norm of the oracle on a workload (or on the first sub_rows rows of every
+    sequence); returns (rows, seconds)."""
+    sh = wl.shape
+    if sub_rows is not None:
+        L = min(sub_rows, int(wl.run_lengths.min()))
+        cu = np.concatenate([[0], np.cumsum(wl.run_lengths)])
+        rows = np.concatenate([np.arange(cu[s], cu[s] + L) for s in range(len(wl.run_lengths))])
+        lens = np.full(len(wl.run_lengths), L, np.int32)
+        xbc, z, dt = (np.ascontiguousarray(a[rows]) for a in (wl.xbc, wl.z, wl.dt))
+    else:
+        lens, xbc, z, dt = wl.run_lengths, wl.xbc, wl.z, wl.dt
+    T = int(lens.sum())
+    t0 = time.perf_counter()
+    oa = np.zeros_like(xbc)
+    cp = wl.conv_pool.copy()
+    assert oracle.conv1d(oa, xbc, wl.conv_w, wl.conv_b, cp, lens, wl.slots, wl.fresh) == 0
+    oy = np.zeros((T, sh.d_inner), dtype=xbc.dtype)
+    sp = wl.ssm_pool.copy()
+    assert oracle.scan(oy, oa, dt, wl.a_log, wl.dt_bias, wl.D, sp, lens, wl.slots, wl.fresh, sh.ngroups) == 0
+    oo = np.zeros_like(oy)
+    assert oracle.gated_rmsnorm(oo, oy, z, wl.norm_w, sh.norm_groups, sh.eps) == 0
+    return T, time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(args, W, wl, sh):
-    """The oracle (as it stands) on the first cpu_sample_rows rows of every sequence of the
-    long-prefill batch (the whole batch by default): conv, scan and gated norm."""
+    """The oracle (as it stands) timed on the host cores, after the GPU work: the long-prefill
+    batch (first cpu_sample_rows rows of every sequence; the whole batch by default) on all the
+    threads the process may use, the tiny fp32 and 130m-shaped prefills on one thread as well,
+    and a few decode steps of the 256-request batch."""
     import oracle
 
-    L = min(args.cpu_sample_rows, int(wl.run_lengths.min()))
-    S = len(wl.run_lengths)
-    cu = np.concatenate([[0], np.cumsum(wl.run_lengths)])
-    rows = np.concatenate([np.arange(cu[s], cu[s] + L) for s in range(S)])
-    sub = W.Workload(wl.name, wl.seed, sh, np.full(S, L, np.int32), wl.slots.copy(), wl.fresh.copy(), wl.conv_w,
-                     wl.conv_b, wl.dt_bias, wl.a_log, wl.D, wl.norm_w, wl.conv_pool.copy(), wl.ssm_pool.copy(),
-                     np.ascontiguousarray(wl.xbc[rows]), np.ascontiguousarray(wl.z[rows]),
-                     np.ascontiguousarray(wl.dt[rows]))
-    t0 = time.perf_counter()
-    oa = np.zeros_like(sub.xbc)
-    cp = sub.conv_pool.copy()
-    assert oracle.conv1d(oa, sub.xbc, sub.conv_w, sub.conv_b, cp, sub.run_lengths, sub.slots, sub.fresh) == 0
-    oy = np.zeros((S * L, sh.d_inner), dtype=sub.xbc.dtype)
-    sp = sub.ssm_pool.copy()
-    assert oracle.scan(oy, oa, sub.dt, sub.a_log, sub.dt_bias, sub.D, sp, sub.run_lengths, sub.slots,
-                       sub.fresh, sh.ngroups) == 0
-    oo = np.zeros_like(oy)
-    assert oracle.gated_rmsnorm(oo, oy, sub.z, sub.norm_w, sh.norm_groups, sh.eps) == 0
-    dt_cpu = time.perf_counter() - t0
-    cpu = {"value": S * L / dt_cpu, "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+    ncpu = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    threads = oracle.max_threads()
+    T, sec = _oracle_prefill(oracle, wl, args.cpu_sample_rows)
+    cpu = {"value": T / sec, "unit": "tokens/s", "cores": threads, "kind": "oracle",
            "sample": "%d sequences x first %d rows of the long-prefill batch (48 heads, conv+scan+norm), "
-                     "%.1f s wall" % (S, L, dt_cpu)}
+                     "%.1f s wall on %d threads" % (len(wl.run_lengths), T // len(wl.run_lengths), sec, threads),
+           "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": ncpu}
+    small = {}
+    for name, w in (("tiny_fp32", W.tiny_fp32()), ("m130_prefill", W.layer_130m_prefill())):
+        for nt in (1, threads):
+            oracle.set_threads(nt)
+            t, sc = _oracle_prefill(oracle, w)
+            small["%s_%dthr" % (name, nt)] = {"tokens_per_s": t / sc, "seconds": sc, "threads": nt}
+    oracle.set_threads(threads)
+    cpu["small_prefills"] = small
+    # decode: the first few of the 64 steps (conv, scan, norm per step), on all threads
+    dwl = W.decode_batch()
+    dsh = dwl.shape
+    cp, sp = dwl.conv_pool.copy(), dwl.ssm_pool.copy()
+    nsteps = 4
+    t0 = time.perf_counter()
+    for i, (x, z, dt) in enumerate(dwl.steps[:nsteps]):
+        fresh = dwl.fresh if i == 0 else np.zeros_like(dwl.fresh)
+        oa = np.zeros_like(x)
+        assert oracle.conv1d(oa, x, dwl.conv_w, dwl.conv_b, cp, dwl.run_lengths, dwl.slots, fresh) == 0
+        oy = np.zeros((x.shape[0], dsh.d_inner), dtype=x.dtype)
+        assert oracle.scan(oy, oa, dt, dwl.a_log, dwl.dt_bias, dwl.D, sp, dwl.run_lengths, dwl.slots, fresh,
+                           dsh.ngroups, decode=True) == 0
+        oo = np.zeros_like(oy)
+        assert oracle.gated_rmsnorm(oo, oy, z, dwl.norm_w, dsh.norm_groups, dsh.eps) == 0
+    cpu["decode_us_per_step"] = 1e6 * (time.perf_counter() - t0) / nsteps
+    cpu["decode_sample"] = "first %d of the 64 steps of 256 requests, %d threads" % (nsteps, threads)
     return cpu
 
 

@@ -113,9 +113,12 @@ __device__ __forceinline__ float wave_sum(float v) {
 // sequence's first row).  Layout (each section 256-byte aligned):
 //   seq_info  int2  [S]        (first segment index, number of segments)
 //   seg_info  int4  [nseg]     (sequence, first row, rows, index within sequence)
-//   seg_decay f32   [nseg][H]  exp(sum of log-decays over the segment)
-//   seg_state f32   [nseg][H][P][N]  local end state, then the state entering
-//                                    the segment
+//   seg_decay f32   [nseg][H]  exp(sum of log-decays over the segment), 0 when that sum is
+//                              below -60 (the carried state is dropped)
+//   seg_state f32   [nseg][H][P][N]  at the index of segment k + 1: the local end state
+//                                    of segment k, then the state entering segment k + 1;
+//                                    at a sequence's first index, a copy of its slot
+//                                    (resumed sequences of several segments only)
 struct ScanLayout {
   int64_t nseg;
   int32_t seg_len;

@@ -9,10 +9,16 @@
 //   S_in(0)   = 0 when fresh, else the slot,
 //   S_in(k+1) = exp(sum_{t in k} a_t) * S_in(k) + S_loc(k),
 //   S_loc(k)  = sum_{j in k} exp(sum_{t in k, t > j} a_t) * dt'_j * x_j (x) B_j.
-// Three launches: segment states S_loc for every segment but a sequence's last
-// (scan kernels), this pass (turns them into S_in, serially over a sequence's
-// segments), and the output kernels that walk each segment from S_in, write y and,
-// for a sequence's last segment, the final state into the slot.
+// Three launches: segment states S_loc(k) for every segment but a sequence's last
+// (scan kernels; stored at the index of segment k + 1, with the segment's decay factor),
+// this pass (turns them into S_in, serially over a sequence's segments), and the output
+// kernels that walk each segment from S_in, write y and, for a sequence's last segment,
+// the final state into the slot.
+//
+// A carried state whose decay to the point of use is below e^-60 is dropped: its share is
+// below fp32 resolution next to the terms that are kept.  A segment whose whole decay is
+// that small has decay factor 0 and S_in(k+1) = S_loc(k): the pass leaves its slot as the
+// scan kernel wrote it and, where every segment decays that much, moves no state at all.
 #include "common.h"
 
 namespace m2 {
@@ -57,10 +63,16 @@ __global__ __launch_bounds__(kSetupThreads) void scan_setup_kernel(const int32_t
   }
 }
 
-// One thread per float4 of a head's state, walking one sequence's segments in order.  The
-// segments' local states and decays are loaded kBatch at a time before the chain runs
-// through them in registers, so a long chain waits on one round of loads per batch rather
-// than one per segment.
+// One thread per float4 of a head's state, walking one sequence's segments in order
+// (sequences strided over grid z).  Index k > 0 of a sequence's state array holds S_loc(k - 1)
+// as the scan kernels left it; where segment k - 1 has a nonzero decay factor the pass
+// replaces it with S_in(k) = dec(k - 1) S_in(k - 1) + S_loc(k - 1).  S_in(k - 1) is in the
+// registers when the previous step computed it, else it is read back from index k - 1 (a
+// dropped predecessor: S_loc(k - 2)).  A resumed sequence of several segments has its slot
+// copied to index 0, since the launch that reads S_in(0) also writes the final state into
+// that slot.  The decays and the local states of kBatch segments are loaded before the chain
+// runs through them, so a long chain waits on one round of loads per batch rather than one
+// per segment.
 constexpr int kBatch = 8;
 
 __global__ __launch_bounds__(256) void scan_pass_kernel(const int2* __restrict__ seq_info,
@@ -69,34 +81,43 @@ __global__ __launch_bounds__(256) void scan_pass_kernel(const int2* __restrict__
                                                         const float4* __restrict__ pool,
                                                         const int32_t* __restrict__ slots,
                                                         const uint8_t* __restrict__ fresh, int H,
-                                                        int f4) {
+                                                        int f4, int S) {
   const int f = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
-  const int s = blockIdx.z;
   if (f >= f4) return;
-  const int2 si = seq_info[s];
-  float4 S = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (!fresh[s]) S = pool[((size_t)slots[s] * H + h) * f4 + f];
-  for (int k0 = 0; k0 < si.y; k0 += kBatch) {
-    // S_loc(k) and the decays of segments k0.. (the sequence's last segment has no S_loc)
-    float4 loc[kBatch];
-    float dec[kBatch];
-#pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int k = k0 + i;
-      const int64_t seg = si.x + k;
-      loc[i] = k + 1 < si.y ? seg_state[((size_t)seg * H + h) * f4 + f] : make_float4(0.f, 0.f, 0.f, 0.f);
-      dec[i] = k + 1 < si.y ? seg_decay[seg * H + h] : 0.f;
+  for (int s = blockIdx.z; s < S; s += gridDim.z) {
+    const int2 si = seq_info[s];
+    if (si.y < 2) continue;
+    auto at = [&](int k) -> float4& { return seg_state[((size_t)(si.x + k) * H + h) * f4 + f]; };
+    float4 Sr = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (!fresh[s]) {
+      Sr = pool[((size_t)slots[s] * H + h) * f4 + f];
+      at(0) = Sr;
     }
+    bool valid = true;  // Sr holds S_in(k) of the step below
+    for (int k0 = 0; k0 + 1 < si.y; k0 += kBatch) {
+      float4 loc[kBatch];
+      float dec[kBatch];
 #pragma unroll
-    for (int i = 0; i < kBatch; ++i) {
-      const int k = k0 + i;
-      if (k < si.y) {
-        seg_state[((size_t)(si.x + k) * H + h) * f4 + f] = S;  // S_in(k)
-        S.x = fmaf(dec[i], S.x, loc[i].x);
-        S.y = fmaf(dec[i], S.y, loc[i].y);
-        S.z = fmaf(dec[i], S.z, loc[i].z);
-        S.w = fmaf(dec[i], S.w, loc[i].w);
+      for (int i = 0; i < kBatch; ++i) {
+        const int k = k0 + i;
+        dec[i] = k + 1 < si.y ? seg_decay[(int64_t)(si.x + k) * H + h] : 0.f;
+        loc[i] = dec[i] != 0.f ? at(k + 1) : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < kBatch; ++i) {
+        const int k = k0 + i;
+        if (k + 1 < si.y && dec[i] != 0.f) {
+          if (!valid) Sr = at(k);
+          Sr.x = fmaf(dec[i], Sr.x, loc[i].x);
+          Sr.y = fmaf(dec[i], Sr.y, loc[i].y);
+          Sr.z = fmaf(dec[i], Sr.z, loc[i].z);
+          Sr.w = fmaf(dec[i], Sr.w, loc[i].w);
+          at(k + 1) = Sr;  // S_in(k + 1)
+          valid = true;
+        } else {
+          valid = false;
+        }
       }
     }
   }
@@ -164,11 +185,12 @@ hipError_t launch_scan_setup(const ScanArgs& a, hipStream_t st) {
 
 hipError_t launch_scan_pass(const ScanArgs& a, hipStream_t st) {
   const int f4 = a.dims.headdim * a.dims.d_state / 4;
-  const dim3 grid((unsigned)((f4 + 255) / 256), (unsigned)a.dims.nheads, (unsigned)a.bd.num_seqs);
+  const int S = a.bd.num_seqs;
+  const dim3 grid((unsigned)((f4 + 255) / 256), (unsigned)a.dims.nheads, (unsigned)(S < 65535 ? S : 65535));
   M2_LAUNCH("scan_pass", scan_pass_kernel, grid, dim3(256), 0, st,
             (const int2*)(a.ws + a.lay.off_seq_info), (const float*)(a.ws + a.lay.off_seg_decay),
             (float4*)(a.ws + a.lay.off_seg_state), (const float4*)a.ssm_state, a.bd.slots,
-            a.bd.fresh, a.dims.nheads, f4);
+            a.bd.fresh, a.dims.nheads, f4, S);
   return hipSuccess;
 }
 

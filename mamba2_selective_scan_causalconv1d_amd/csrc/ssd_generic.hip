@@ -49,7 +49,8 @@ __device__ void chunk_prologue(const T* __restrict__ dt, const float* __restrict
   __syncthreads();
 }
 
-// Local end state of every segment except a sequence's last.
+// Local end state of every segment except a sequence's last, stored at the index of the
+// next segment (the state that segment starts from, once the pass has run).
 template <typename T>
 __global__ __launch_bounds__(256) void ssd_generic_state_kernel(
     const T* __restrict__ xbc, const T* __restrict__ dt, const float* __restrict__ a_log,
@@ -65,7 +66,7 @@ __global__ __launch_bounds__(256) void ssd_generic_state_kernel(
   const int Di = H * P;
   const size_t Dc = (size_t)Di + 2 * (size_t)G * N;
   const int g = h / (H / G);
-  float* out = sp.seg_state + ((size_t)seg * H + h) * (size_t)P * N;
+  float* out = sp.seg_state + ((size_t)(seg + 1) * H + h) * (size_t)P * N;
   for (int e = threadIdx.x; e < P * N; e += blockDim.x) {
     const int p = e / N, n = e % N;
     float acc = 0.f;
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void ssd_generic_scan_kernel(
     T* __restrict__ y, const T* __restrict__ xbc, const T* __restrict__ dt,
     const float* __restrict__ a_log, const float* __restrict__ dt_bias,
     const float* __restrict__ Dp, float* __restrict__ pool, const int32_t* __restrict__ slots,
-    ScanPtrs sp, int H, int P, int N, int G) {
+    const uint8_t* __restrict__ fresh, ScanPtrs sp, int H, int P, int N, int G) {
   const int seg = blockIdx.x;
   const int h = blockIdx.y;
   const int4 si = sp.seg_info[seg];
@@ -108,7 +109,12 @@ __global__ __launch_bounds__(256) void ssd_generic_scan_kernel(
     CB[i * kQ + j] = acc;
   }
   __syncthreads();
-  const float* Sin = sp.seg_state + ((size_t)seg * H + h) * (size_t)P * N;
+  // the state entering the segment: zero for a fresh sequence's first segment; the slot
+  // itself for a resumed sequence of one segment (this workgroup alone reads and then
+  // writes it); else what the pass left at this segment's index
+  const float* Sin = (si.w == 0 && fresh[si.x]) ? nullptr
+                     : (si.w == 0 && last) ? pool + ((size_t)slots[si.x] * H + h) * (size_t)P * N
+                                           : sp.seg_state + ((size_t)seg * H + h) * (size_t)P * N;
   const float Dh = Dp[h];
   for (int e = threadIdx.x; e < rows * P; e += blockDim.x) {
     const int i = e / P, p = e % P;
@@ -118,17 +124,19 @@ __global__ __launch_bounds__(256) void ssd_generic_scan_kernel(
                  Act<T>::load(xbc + (size_t)(row0 + j) * Dc + (size_t)h * P + p), acc);
     const T* ci = xbc + (size_t)(row0 + i) * Dc + coff;
     float off = 0.f;
-    for (int n = 0; n < N; ++n) off = fmaf(Act<T>::load(ci + n), Sin[(size_t)p * N + n], off);
+    if (Sin)
+      for (int n = 0; n < N; ++n) off = fmaf(Act<T>::load(ci + n), Sin[(size_t)p * N + n], off);
     const float xi = Act<T>::load(xbc + (size_t)(row0 + i) * Dc + (size_t)h * P + p);
     Act<T>::store(y + (size_t)(row0 + i) * Di + (size_t)h * P + p,
                   acc + __expf(cs[i]) * off + Dh * xi);
   }
+  __syncthreads();  // every read of Sin (possibly the slot itself) done before the slot is written
   if (last) {
     const float dlast = __expf(cs[rows - 1]);
     float* dstate = pool + ((size_t)slots[si.x] * H + h) * (size_t)P * N;
     for (int e = threadIdx.x; e < P * N; e += blockDim.x) {
       const int p = e / N, n = e % N;
-      float acc = dlast * Sin[e];
+      float acc = Sin ? dlast * Sin[e] : 0.f;
       for (int j = 0; j < rows; ++j) {
         const T* r = xbc + (size_t)(row0 + j) * Dc;
         acc = fmaf(W[j] * Act<T>::load(r + (size_t)h * P + p), Act<T>::load(r + boff + n), acc);
@@ -150,7 +158,7 @@ hipError_t launch_t(const ScanArgs& a, hipStream_t st) {
   hipError_t e = launch_scan_pass(a, st);
   if (e != hipSuccess) return e;
   M2_LAUNCH("ssd_generic_scan", ssd_generic_scan_kernel<T>, grid, dim3(256), 0, st, (T*)a.y,
-            (const T*)a.xbc, (const T*)a.dt, a.a_log, a.dt_bias, a.D, a.ssm_state, a.bd.slots, sp,
+            (const T*)a.xbc, (const T*)a.dt, a.a_log, a.dt_bias, a.D, a.ssm_state, a.bd.slots, a.bd.fresh, sp,
             d.nheads, d.headdim, d.d_state, d.ngroups);
   return hipSuccess;
 }

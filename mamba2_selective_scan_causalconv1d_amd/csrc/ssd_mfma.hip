@@ -407,17 +407,51 @@ __device__ __forceinline__ size_t state_elem(int ph, int t, int nb, int lane) {
 
 // ---------------------------------------------------------------- segment states
 
+// Log-decay sums of head h over the chunks of a segment [r0, r0 + nrows): lane q (< 64)
+// receives the sum of a_t = -A softplus(dt_t + bias) over chunk q.  dt is loaded eight
+// chunks at a time before it is used.
+__device__ __forceinline__ float chunk_log_decays(const bf16_t* dt, int r0, int nrows, int H, int h, float A,
+                                                  float bias, int lane) {
+  const int nch = (nrows + kQ - 1) / kQ;
+  float mine = 0.f;
+  for (int q0 = 0; q0 < nch; q0 += 8) {
+    uint32_t b[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = q0 + i;
+      b[i] = q < nch ? dt_bits(dt, r0 + q * kQ, min(kQ, nrows - q * kQ), H, h, lane) : 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int q = q0 + i;
+      if (q < nch) {
+        const int nr = min(kQ, nrows - q * kQ);
+        const float a = lane < nr ? -A * softplus_f32(bf16_to_f32(b[i]) + bias) : 0.f;
+        const float sum = lane_value(wave_scan_incl(a), 63);
+        if (lane == q) mine = sum;
+      }
+    }
+  }
+  return mine;
+}
+
 // Single-buffered tiles: with two heads per workgroup three workgroups fit a CU (LDS and
 // registers), and each one's copies are covered by the other two's work.
-template <int HB>
-__global__ __launch_bounds__(128 * HB, HB == 2 ? 3 : 1) void ssd_state_kernel(const bf16_t* __restrict__ xbc,
-                                                                             const bf16_t* __restrict__ dt,
-                                                                             const float* __restrict__ a_log,
-                                                                             const float* __restrict__ dt_bias,
-                                                                             SegPtrs sp, int H, int G, int nitems) {
+//
+// The walk starts at the last chunk q0 whose rows all decay by more than e^-60 before the
+// segment's end (none of the chunks before q0 can change the end state in fp32; chunk q0
+// itself is kept), so where the decay is fast only the segment's last chunk or two are
+// walked.  The segment's total log-decay gives its decay factor for the pass (0 below -60).
+__global__ __launch_bounds__(256, 3) void ssd_state_kernel(const bf16_t* __restrict__ xbc,
+                                                          const bf16_t* __restrict__ dt,
+                                                          const float* __restrict__ a_log,
+                                                          const float* __restrict__ dt_bias,
+                                                          SegPtrs sp, int H, int G, int nitems) {
+  constexpr int HB = 2;
   __shared__ __attribute__((aligned(16))) bf16_t sB[kQ * kN];
   __shared__ __attribute__((aligned(16))) bf16_t sX[HB][kQ * kP];
   __shared__ __attribute__((aligned(16))) Decay sD[2][HB];
+  __shared__ int sStart[HB];
 
   const int nhg = H / HB;
   const int item = work_item(blockIdx.x, nitems);
@@ -438,6 +472,21 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 3 : 1) void ssd_state_kernel(co
   const Lofs lo = lane_offsets(lane, ph);
   const DmaOfs dof = dma_offsets(lane, w, ld);
 
+  // the segment's chunk decays: E_q = log-decay from the start of chunk q to the segment's end
+  {
+    const float c = chunk_log_decays(dt, si.y, si.z, H, h, A, bias, lane);
+    const float incl = wave_scan_incl(c);
+    const float total = lane_value(incl, 63);
+    const float E = total - incl + c;
+    const uint64_t drop = __ballot(lane >= 1 && lane < nchunks && E < -kDropSpan);
+    if (ph == 0 && lane == 0) {
+      sStart[hh] = drop ? 63 - __builtin_clzll(drop) : 0;
+      sp.seg_decay[(size_t)seg * H + h] = total < -kDropSpan ? 0.f : __expf(total);
+    }
+  }
+  __syncthreads();
+  const int q0 = uniform(min(sStart[0], sStart[1]));
+
   auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
   auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
   auto dt_of = [&](int q) { return dt_bits(dt, si.y + q * kQ, nr_of(q), H, h, lane); };
@@ -455,11 +504,11 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 3 : 1) void ssd_state_kernel(co
     for (int nb = 0; nb < 8; ++nb) S[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   float lam = 1.f, lsum = 0.f;
-  load(0);
-  chunk_decay_update(sD[0][hh], bf16_to_f32(dt_of(0)), A, bias, nr_of(0), lane, ph, lam, lsum);
-  uint32_t dtn = nchunks > 1 ? dt_of(1) : 0u;
+  load(q0);
+  chunk_decay_update(sD[q0 & 1][hh], bf16_to_f32(dt_of(q0)), A, bias, nr_of(q0), lane, ph, lam, lsum);
+  uint32_t dtn = q0 + 1 < nchunks ? dt_of(q0 + 1) : 0u;
 
-  for (int q = 0; q < nchunks; ++q) {
+  for (int q = q0; q < nchunks; ++q) {
     const int st = q & 1;
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();  // chunk q rows and decay visible
@@ -482,15 +531,15 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 3 : 1) void ssd_state_kernel(co
     dtn = dtn2;
   }
 
+  // S_loc of this segment, at the index of the next segment of the sequence
   const float lam_end = uniformf(sD[(nchunks - 1) & 1][hh].lam_next);
-  float* out = sp.seg_state + ((size_t)seg * H + h) * (size_t)(kP * kN);
+  float* out = sp.seg_state + ((size_t)(seg + 1) * H + h) * (size_t)(kP * kN);
   const int lane_st = opaque(lane);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
       *reinterpret_cast<f32x4*>(out + state_elem(ph, t, nb, lane_st)) = S[t][nb] * lam_end;
-  if (ph == 0 && lane == 0) sp.seg_decay[(size_t)seg * H + h] = __expf(lsum);
 }
 
 // ---------------------------------------------------------------- outputs
@@ -498,11 +547,12 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 3 : 1) void ssd_state_kernel(co
 // Per chunk: (1) tiles and decay visible -> phase 1: x^T operands, G^T tiles and M^T of the
 // workgroup's heads, Y = S C^T, the state update; (2) M^T visible, tiles free -> copies of
 // the next chunk, phase 2: Y += x^T M^T, row scales, store, next chunk's decay.
-template <int HB>
-__global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
+__global__ __launch_bounds__(256, 2) void ssd_scan_kernel(
     bf16_t* __restrict__ y, const bf16_t* __restrict__ xbc, const bf16_t* __restrict__ dt,
     const float* __restrict__ a_log, const float* __restrict__ dt_bias, const float* __restrict__ Dp,
-    float* __restrict__ pool, const int32_t* __restrict__ slots, SegPtrs sp, int H, int G, int nitems) {
+    float* __restrict__ pool, const int32_t* __restrict__ slots, const uint8_t* __restrict__ fresh, SegPtrs sp,
+    int H, int G, int nitems) {
+  constexpr int HB = 2;
   __shared__ __attribute__((aligned(16))) bf16_t sB[kQ * kN];
   __shared__ __attribute__((aligned(16))) bf16_t sC[kQ * kN];
   __shared__ __attribute__((aligned(16))) bf16_t sX[HB][kQ * kP];
@@ -543,10 +593,20 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
     load_x<HB>(rows_of(q), nrb, 2u * ld, colX, sX, dof, w);
   };
 
-  // the state entering the segment (written by the pass kernel), frame scale 1
+  // the state entering the segment, frame scale 1: zero for a fresh sequence's first
+  // segment; the slot itself for a resumed sequence of one segment (each lane reads here
+  // and writes at the end the same elements); else what the pass left at this segment's
+  // index (for a first segment, the pass's copy of the slot, which the sequence's last
+  // segment overwrites during this launch)
   f32x4 S[2][8];
-  {
-    const float* in = sp.seg_state + ((size_t)seg * H + h) * (size_t)(kP * kN);
+  if (si.w == 0 && fresh[si.x]) {
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) S[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else {
+    const float* in = (si.w == 0 && last) ? pool + ((size_t)slots[si.x] * H + h) * (size_t)(kP * kN)
+                                          : sp.seg_state + ((size_t)seg * H + h) * (size_t)(kP * kN);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -740,12 +800,12 @@ __global__ __launch_bounds__(128 * HB, HB == 2 ? 2 : 1) void ssd_scan_kernel(
   }
 }
 
-int heads_per_block(const mamba2_dims& d) { (void)d; return 2; }
+constexpr int kHeadsPerBlock = 2;
 
 }  // namespace
 
 // Shapes the MFMA path covers: bf16, P = 64, N = 128, an even number of heads per group
-// (a workgroup takes 2 or 4 heads of one group), and chunk-row offsets within 32 bits.
+// (a workgroup takes 2 heads of one group), and chunk-row offsets within 32 bits.
 bool scan_mfma_supported(const mamba2_dims* d) {
   const int64_t Dc = (int64_t)d->nheads * d->headdim + 2 * (int64_t)d->ngroups * d->d_state;
   return d->act_dtype == MAMBA2_DTYPE_BF16 && d->headdim == kP && d->d_state == kN &&
@@ -755,7 +815,7 @@ bool scan_mfma_supported(const mamba2_dims* d) {
 // Segment length for the MFMA path: aim at three rounds of workgroups (two resident per CU
 // on each of 256 CUs), 64..4096 rows per segment.
 int32_t scan_mfma_segment_length(const mamba2_recurrent_batch* rb, const mamba2_dims* d) {
-  const int64_t groups = d->nheads / heads_per_block(*d);
+  const int64_t groups = d->nheads / kHeadsPerBlock;
   const int64_t target = 3 * 512;
   int64_t L = ((int64_t)rb->num_rows * groups + target - 1) / target;
   L = (L + kQ - 1) / kQ * kQ;
@@ -768,27 +828,15 @@ hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t st) {
   const SegPtrs sp{(const int2*)(a.ws + a.lay.off_seq_info), (const int4*)(a.ws + a.lay.off_seg_info),
                    (float*)(a.ws + a.lay.off_seg_decay), (float*)(a.ws + a.lay.off_seg_state)};
   const mamba2_dims& d = a.dims;
-  const int HB = heads_per_block(d);
-  const int nitems = (int)(a.lay.nseg * (d.nheads / HB));
+  const int nitems = (int)(a.lay.nseg * (d.nheads / kHeadsPerBlock));
   if (nitems == 0) return hipSuccess;
-  if (HB == 4) {
-    M2_LAUNCH("ssd_state", ssd_state_kernel<4>, dim3((unsigned)nitems), dim3(512), 0, st, (const bf16_t*)a.xbc,
-              (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, d.ngroups, nitems);
-  } else {
-    M2_LAUNCH("ssd_state", ssd_state_kernel<2>, dim3((unsigned)nitems), dim3(256), 0, st, (const bf16_t*)a.xbc,
-              (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, d.ngroups, nitems);
-  }
+  M2_LAUNCH("ssd_state", ssd_state_kernel, dim3((unsigned)nitems), dim3(256), 0, st, (const bf16_t*)a.xbc,
+            (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, d.ngroups, nitems);
   hipError_t e = launch_scan_pass(a, st);
   if (e != hipSuccess) return e;
-  if (HB == 4) {
-    M2_LAUNCH("ssd_scan", ssd_scan_kernel<4>, dim3((unsigned)nitems), dim3(512), 0, st, (bf16_t*)a.y,
-              (const bf16_t*)a.xbc, (const bf16_t*)a.dt, a.a_log, a.dt_bias, a.D, a.ssm_state, a.bd.slots, sp,
-              d.nheads, d.ngroups, nitems);
-  } else {
-    M2_LAUNCH("ssd_scan", ssd_scan_kernel<2>, dim3((unsigned)nitems), dim3(256), 0, st, (bf16_t*)a.y,
-              (const bf16_t*)a.xbc, (const bf16_t*)a.dt, a.a_log, a.dt_bias, a.D, a.ssm_state, a.bd.slots, sp,
-              d.nheads, d.ngroups, nitems);
-  }
+  M2_LAUNCH("ssd_scan", ssd_scan_kernel, dim3((unsigned)nitems), dim3(256), 0, st, (bf16_t*)a.y,
+            (const bf16_t*)a.xbc, (const bf16_t*)a.dt, a.a_log, a.dt_bias, a.D, a.ssm_state, a.bd.slots,
+            a.bd.fresh, sp, d.nheads, d.ngroups, nitems);
   return hipSuccess;
 }
 

@@ -26,9 +26,14 @@ def test_algorithmic_bytes_long_prefill():
     scan_bytes, scan_flops = bench.kernel_bytes_flops("ssd_scan", wl, T)
     assert scan_bytes == T * (3328 + 48 + 3072) * 2 + 4 * 48 * 64 * 128 * 4
     assert abs(scan_bytes / 1e6 - 851.44) < 0.01
-    # flops per row and head: G^T over N (shared by the 48 heads of the group), M^T x over P,
-    # S C^T and the state update over N P (two each: multiply and add)
-    assert scan_flops == T * 48 * (128 * 65 / 48 + 64 * 65 + 4 * 128 * 64)
+    # flops per row and head at the workload's chunk Q = 256: C B^T over the causal triangle
+    # (shared by the 48 heads of the group), the masked product with x, the chunk state and the
+    # state's output term (two flops per multiply-add each): 49,901 per row and head, 157.0 GFLOP
+    assert scan_flops == T * 48 * (128 * 257 / 48 + 64 * 257 + 4 * 128 * 64)
+    assert abs(scan_flops / 1e9 - 157.0) < 0.05
+    alg, dense = bench.scan_flops(wl, T)
+    assert alg == scan_flops
+    assert abs(dense / (T * 48) - 66901.33) < 0.01
     # conv: rows in and out, plus the slot rows written (fresh: none read)
     conv_bytes, _ = bench.kernel_bytes_flops("conv1d_silu", wl, T)
     assert conv_bytes == 2 * T * 3328 * 2 + 4 * 3 * 3328 * 2
@@ -44,3 +49,22 @@ def test_algorithmic_bytes_decode_step():
     b, _ = bench.kernel_bytes_flops("scan_decode", wl, 256)
     assert b == 256 * (3328 + 48 + 3072) * 2 + 2 * 256 * 48 * 64 * 128 * 4
     assert abs(b / 1e6 - 808.6) < 0.1
+
+
+def test_digest_sees_every_bit():
+    """The digest the bench compares across timed calls changes when any one bit changes, and
+    depends on the position of a value, not only on the multiset of values."""
+    import numpy as np
+    import torch
+
+    t = torch.from_numpy(np.random.default_rng(1).standard_normal(100003).astype(np.float32))
+    d0 = bench.digest(torch, [t])
+    for i in (0, 5, 100002):
+        u = t.clone()
+        u.view(torch.int32)[i] ^= 1
+        assert bench.digest(torch, [u]) != d0
+    s = t.clone()
+    s[[3, 4]] = s[[4, 3]]
+    assert bench.digest(torch, [s]) != d0
+    b = t.to(torch.bfloat16)
+    assert bench.digest(torch, [b]) == bench.digest(torch, [b.clone()])

@@ -45,11 +45,25 @@ def _check_pools(wl, named, ssm_got, ssm_ref, conv_got=None, conv_ref=None):
                 assert conv_got[s].tobytes() == wl.conv_pool[s].tobytes(), "untouched conv slot %d" % s
 
 
+def _chained(wl, xa_o, y_g, out_g, bar, what):
+    """Print (never assert) how far the GPU's own end-to-end chain sits from the oracle's own
+    chain (each side feeding its own rounded intermediates forward).  The per-op checks are the
+    parity test; this figure only keeps regressions of the chain visible."""
+    y_oo, _ = oracle_scan(wl, xa_o)
+    out_oo = oracle_norm(wl, y_oo)
+    import _util
+
+    say("  chained (each side's own pipeline, not asserted): y %.3g, out %.3g of bar" % (
+        _util.max_bar_fraction(W.act_to_f32(y_g), W.act_to_f32(y_oo), bar),
+        _util.max_bar_fraction(W.act_to_f32(out_g), W.act_to_f32(out_oo), bar)))
+
+
 def _prefill_parity(gpu, wl):
     """Each op of the GPU chain against the oracle run on the same inputs: the conv on the
     workload's rows, the scan on the GPU's conv output, the norm on the GPU's y.  (Comparing
     the two chains end to end would compare each side's own rounding of the intermediates,
-    which the scan amplifies: one-ulp bf16 changes in its inputs move y by several bars.)"""
+    which the scan amplifies: one-ulp bf16 changes in its inputs move y by several bars; that
+    figure is printed, not asserted.)"""
     sh = wl.shape
     bar = bar_for(sh.act)
     b = gpu.batch_of(wl)
@@ -69,6 +83,7 @@ def _prefill_parity(gpu, wl):
     out_g = gpu.gpu_norm(wl, y_g, wl.z)
     f = assert_close(gpu.f32(out_g), gpu.f32(out_o), bar, "norm out")
     say("  norm out: %.3g of bar" % f)
+    _chained(wl, xa_o, y_g, out_g, bar, wl.name)
 
 
 def test_tiny_fp32(gpu):
@@ -88,37 +103,27 @@ def test_varlen_slow_decay(gpu):
     _prefill_parity(gpu, W.varlen_slow_decay())
 
 
-def test_long_prefill_sampled(gpu):
-    """4 x 16384 rows, 48 heads, norm over 8 groups: conv and norm compared in full, the scan
-    on four heads (all rows and final states) -- heads are independent, so the oracle computes
-    the sampled heads exactly as a full run would."""
+def test_long_prefill(gpu):
+    """4 x 16384 rows, 48 heads, norm over 8 groups, the launch configuration the bench times:
+    every op against the oracle in full (all 48 heads, all rows, every slot)."""
     wl = W.long_prefill()
-    sh = wl.shape
     b = gpu.batch_of(wl)
     p = gpu.Params(wl)
     say("[%s] conv" % wl.name)
     xa_o, cp_o = oracle_conv(wl)
     xa_g, cp_g = gpu.gpu_conv(wl, wl.xbc, wl.conv_pool, b, p)
     say("  conv out: %.3g of bar" % assert_close(gpu.f32(xa_g), gpu.f32(xa_o), BF16_BAR, "conv out"))
-    assert np.array_equal(cp_g, cp_o)
-    del xa_o
-    heads = [0, 17, 30, 47]
-    mask = np.zeros(sh.nheads, dtype=np.uint8)
-    mask[heads] = 1
-    say("  scan (oracle on heads %s)" % heads)
-    y_o, sp_o = oracle_scan(wl, xa_g, head_mask=mask)
+    say("  scan (oracle on all heads)")
+    y_o, sp_o = oracle_scan(wl, xa_g)
     y_g, sp_g = gpu.gpu_scan(wl, xa_g, wl.dt, wl.ssm_pool, b, p)
-    P = sh.headdim
-    for h in heads:
-        cols = slice(h * P, (h + 1) * P)
-        f = assert_close(gpu.f32(y_g[:, cols]), gpu.f32(y_o[:, cols]), BF16_BAR, "y head %d" % h)
-        for s in wl.slots:
-            assert_close(sp_g[s, h], sp_o[s, h], F32_BAR, "state slot %d head %d" % (s, h))
-    say("  scan y (sampled heads) ok, last %.3g of bar" % f)
-    say("  norm")
-    out_o = oracle_norm(wl, y_g)  # the norm on the GPU's own y (full rows needed)
+    say("  scan y: %.3g of bar" % assert_close(gpu.f32(y_g), gpu.f32(y_o), BF16_BAR, "scan y"))
+    _check_pools(wl, wl.slots, sp_g, sp_o, cp_g, cp_o)
+    del y_o
+    out_o = oracle_norm(wl, y_g)  # the norm on the GPU's own y
     out_g = gpu.gpu_norm(wl, y_g, wl.z)
     say("  norm out: %.3g of bar" % assert_close(gpu.f32(out_g), gpu.f32(out_o), BF16_BAR, "norm out"))
+    del out_o
+    _chained(wl, xa_o, y_g, out_g, BF16_BAR, wl.name)
 
 
 def _chunk_log_decays(wl, h):
@@ -140,8 +145,9 @@ def test_decay_regimes_long(gpu):
     """4 x 16384 rows with A log-spaced over [1e-3, 30] across the 48 heads, two sequences
     resuming: chunks whose log-decay sum is near zero (state carried across the whole run), a few
     units (the carried state shrinks by 2^-20 over several chunks), tens (every chunk) and
-    hundreds (the carried state negligible).  The scan on eight heads spanning the range against
-    the oracle, all rows and final states."""
+    hundreds (the carried state negligible).  The scan on all 48 heads against the oracle, all
+    rows, final states and untouched slots (eight heads spanning the range are counted and
+    printed)."""
     wl = W.decay_span_prefill()
     sh = wl.shape
     heads = [0, 7, 14, 20, 26, 33, 40, 47]
@@ -155,16 +161,16 @@ def test_decay_regimes_long(gpu):
     b = gpu.batch_of(wl)
     p = gpu.Params(wl)
     xa_g, _ = gpu.gpu_conv(wl, wl.xbc, wl.conv_pool, b, p)
-    mask = np.zeros(sh.nheads, dtype=np.uint8)
-    mask[heads] = 1
-    y_o, sp_o = oracle_scan(wl, xa_g, head_mask=mask)
+    y_o, sp_o = oracle_scan(wl, xa_g)
     y_g, sp_g = gpu.gpu_scan(wl, xa_g, wl.dt, wl.ssm_pool, b, p)
     P = sh.headdim
-    for h in heads:
+    for h in range(sh.nheads):
         cols = slice(h * P, (h + 1) * P)
         f = assert_close(gpu.f32(y_g[:, cols]), gpu.f32(y_o[:, cols]), BF16_BAR, "y head %d" % h)
         g = max(assert_close(sp_g[s, h], sp_o[s, h], F32_BAR, "state slot %d head %d" % (s, h)) for s in wl.slots)
-        say("  head %d (A %.3g): y %.3g of bar, states %.3g" % (h, np.exp(wl.a_log[h]), f, g))
+        if h in heads:
+            say("  head %d (A %.3g): y %.3g of bar, states %.3g" % (h, np.exp(wl.a_log[h]), f, g))
+    _check_pools(wl, wl.slots, sp_g, sp_o)
 
 
 @pytest.mark.parametrize("seed", range(3))
@@ -430,15 +436,17 @@ def test_empty_batch_is_a_noop(gpu):
     assert np.array_equal(ops.to_host(cp), wl.conv_pool) and np.array_equal(ops.to_host(sp), wl.ssm_pool)
 
 
-@pytest.mark.parametrize("groups,act", [(1, "bf16"), (8, "bf16"), (2, "f32"), (48, "bf16")])
-def test_norm_group_widths(gpu, groups, act):
-    """Norm groups of 3072, 384, 1536 (fp32) and 64 columns, weight ~ N(1, 0.1)."""
+@pytest.mark.parametrize("groups,act,Di", [(1, "bf16", 3072), (8, "bf16", 3072), (2, "f32", 3072), (48, "bf16", 3072),
+                                           (1, "bf16", 8192), (3, "f32", 12288)])
+def test_norm_group_widths(gpu, groups, act, Di):
+    """Norm groups of 3072, 384, 1536 (fp32) and 64 columns (the row kernel and, for 48 groups,
+    the per-group kernel), and groups wider than the per-group kernel holds in registers (one
+    bf16 group of 8192 columns, three fp32 groups of 4096: the two-pass kernel); weight ~ N(1, 0.1)."""
     rng = np.random.default_rng(57)
-    Di = 3072
     y = W.to_act(rng.standard_normal((33, Di), dtype=np.float32), act)
     z = W.to_act(rng.standard_normal((33, Di), dtype=np.float32), act)
     w = rng.normal(1, 0.1, Di).astype(np.float32)
-    sh = W.Shape(48, 64, 128, 1, 4, 256, groups, 1, act)
+    sh = W.Shape(Di // 64, 64, 128, 1, 4, 256, groups, 1, act)
     wl = W.Workload("norm", 57, sh, np.array([33], np.int32), np.array([0], np.int32), np.array([1], np.uint8),
                     None, None, None, None, None, w, None, None, z=z)
     out_o = oracle_norm(wl, y, z=z, weight=w, groups=groups)

@@ -66,7 +66,8 @@ def test_conv_worked_example(orc, act):
 
 
 def test_scan_worked_example(orc):
-    """gllm PR #85 'Testing': softplus(dt) = 1 gives y = 7 and then 2/e + 2.5."""
+    """gllm PR #85 'Testing': with dt such that softplus(dt) = 1, the two outputs are 7 and
+    2/e + 2.5 (inputs reconstructed in the golden file)."""
     g = _golden("scan_worked_example.json")
     dt = np.full((2, 1), math.log(math.e - 1.0), dtype=np.float32)
     xbc = np.array([[g["x"][0], g["B"][0], g["C"][0]], [g["x"][1], g["B"][1], g["C"][1]]],
@@ -87,8 +88,9 @@ def test_scan_worked_example(orc):
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_split_vs_whole_exact(orc, act):
-    """gllm PR #85 'CPU reference'/'Testing': a run split across calls is bit-identical to the
-    same run in one call, including a one-token step shorter than the conv history."""
+    """gllm PR #85 'CPU reference'/'Testing': cutting one run into several calls changes no bit
+    of the outputs or the states, also when a call holds a single row (fewer rows than the
+    conv keeps as history)."""
     L = 40
     wl = _small(11, [L], fresh=[1], slots=[2], act=act)
     xa_w, cpool_w = oracle_conv(wl)
@@ -114,7 +116,8 @@ def test_split_vs_whole_exact(orc, act):
 
 
 def test_resume_from_saved_state_exact(orc):
-    """gllm PR #85 'Testing': resuming from a saved mid-sequence state reproduces the rest."""
+    """gllm PR #85 'Testing': a scan restarted from the state saved part-way through a run
+    gives the remaining outputs and the final state exactly."""
     L, t0 = 48, 21
     wl = _small(12, [L], fresh=[1], slots=[0])
     xa, _ = oracle_conv(wl)
@@ -133,8 +136,8 @@ def test_resume_from_saved_state_exact(orc):
 
 
 def test_swapped_slots_match_solo_runs(orc):
-    """gllm PR #85 'Testing': two sequences batched on swapped slots, one fresh and one
-    resuming, match their solo runs."""
+    """gllm PR #85 'Testing': a fresh and a resuming sequence in one batch, on slots (a, b) and
+    then (b, a), give what each gives when run alone."""
     la, lb = 13, 22
     wl = _small(13, [la, lb], fresh=[1, 0], slots=[1, 3])
     sigma_ssm = wl.ssm_pool[3].copy()
@@ -168,8 +171,8 @@ def test_swapped_slots_match_solo_runs(orc):
 
 @pytest.mark.parametrize("act", ["f32", "bf16"])
 def test_fresh_ignores_dirty_slot(orc, act):
-    """gllm PR #85 'Ops'/'Testing': a fresh sequence starts from zero and never reads its slot
-    (NaN in the slot would show if it were read)."""
+    """gllm PR #85 'Ops'/'Testing': a fresh run starts from zero state and leaves its slot
+    unread, so NaN planted in that slot must not reach any output."""
     wl = _small(14, [9, 17], fresh=[1, 1], slots=[0, 5], act=act)
     nan_c = wl.conv_pool.copy()
     nan_c[[0, 5]] = W.to_act(np.full(nan_c[[0, 5]].shape, np.nan, np.float32), act)
@@ -190,8 +193,9 @@ def test_fresh_ignores_dirty_slot(orc, act):
 
 
 def test_head_to_group_mapping(orc):
-    """gllm PR #85 'Testing': zeroing group 1's B and C leaves heads 2 and 3 with only D*x, and
-    heads 0 and 1 untouched (4 heads, 2 groups: head h reads group h / (heads/groups))."""
+    """gllm PR #85 'Testing' (head-to-group mapping): with 4 heads in 2 groups, B and C of group 1
+    set to zero reduce heads 2 and 3 to y = D*x while heads 0 and 1 keep their outputs (head h
+    reads group h / (heads/groups))."""
     wl = _small(15, [30], fresh=[1], slots=[2])
     sh = wl.shape
     xa, _ = oracle_conv(wl)
@@ -229,8 +233,8 @@ def _malformed_cases(M):
 
 
 def test_malformed_batches_rejected_without_writes(orc):
-    """gllm PR #85 'Ops'/'Testing': a slot out of range, a shared slot and run lengths that do
-    not cover the rows are rejected, and nothing is written."""
+    """gllm PR #85 'Ops'/'Testing': batches with a slot outside the pool, two sequences on one
+    slot, or run lengths whose sum differs from the rows are refused with no write."""
     wl = _small(16, [3, 4], fresh=[0, 0], slots=[0, 1])
     M = wl.shape.pool_slots
     for name, lens, slots, code, T in _malformed_cases(M):
@@ -607,3 +611,30 @@ def test_linear_matches_numpy_matmul(orc):
     want = W.act_to_f32(W.to_act(ref.astype(np.float32), "bf16"))
     got = W.act_to_f32(out)
     assert np.max(np.abs(got - want) / (1 + np.abs(want))) <= 2 ** -8
+
+
+# ------------------------------------------------------------ conditioning of the chain
+
+
+def test_scan_output_moves_by_bars_under_one_ulp_input_changes(orc):
+    """Why parity is judged op by op on shared inputs.  y sums terms that cancel, so the scan
+    amplifies the last-bit differences that two correct implementations of the conv may leave
+    in its input.  Here the oracle alone, on the packed variable-length batch: flipping the
+    lowest bf16 bit of 5 % of the conv output's elements (a change of one unit in the last
+    place, the size of one rounding difference) moves the oracle's own y, and the norm after
+    it, by more than the 2e-2 (1 + |ref|) output bar.  An end-to-end comparison of two chains
+    can therefore fail although each op of each chain is within its bar."""
+    from _util import BF16_BAR, max_bar_fraction
+
+    wl = W.varlen_prefill()
+    xa, _ = oracle_conv(wl)
+    y0, _ = oracle_scan(wl, xa)
+    rng = np.random.default_rng(28)
+    flip = rng.random(xa.shape) < 0.05
+    xf = xa ^ (flip.astype(np.uint16))
+    y1, _ = oracle_scan(wl, xf)
+    fy = max_bar_fraction(W.act_to_f32(y1), W.act_to_f32(y0), BF16_BAR)
+    o0, o1 = oracle_norm(wl, y0), oracle_norm(wl, y1)
+    fo = max_bar_fraction(W.act_to_f32(o1), W.act_to_f32(o0), BF16_BAR)
+    print("one-ulp changes in 5%% of the scan input: y moves %.3g bars, the norm output %.3g" % (fy, fo))
+    assert fy > 1.0 and fo > 1.0
