@@ -141,6 +141,23 @@ size_t mamba2_scan_prefill_workspace_bytes(const mamba2_recurrent_batch* rb,
                                            const mamba2_dims* dims);
 
 /*
+ * mamba2_scan_prefill for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the same scan,
+ * with no workspace argument.  Its workspace is a fixed 32 MiB array of the library's
+ * own, one per GPU, held until the process ends (looked up on the first call on each
+ * device); the call allocates nothing.  When the usual segment length's workspace does
+ * not fit, longer segments are used (bf16 P = 64, N = 128 path: up to 4096 rows), which
+ * can change results within rounding; a batch whose workspace does not fit even then
+ * is rejected with MAMBA2_WORKSPACE_TOO_SMALL before any launch (e.g. 48 heads x 64 x 128
+ * fits up to ~20 segments of 4096 rows).  Every call on a GPU shares that GPU's array:
+ * calls that overlap in time on one GPU (two streams, two threads) race.  Arguments,
+ * requirements and other errors as mamba2_scan_prefill.
+ */
+mamba2_status mamba2_scan_prefill_static(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                         const float* dt_bias, const float* d, float* ssm_state,
+                                         const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream);
+
+/*
  * One-row decode step of the same recurrence (every run length must be 1):
  * each sequence's fp32 state is read once from its slot (not at all when fresh)
  * and written back once.  Arguments as mamba2_scan_prefill, no workspace.

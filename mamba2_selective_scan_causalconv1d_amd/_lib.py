@@ -45,6 +45,7 @@ SIGNATURES = [
     ("mamba2_conv1d", _i32, [_vp, _vp, _vp, _vp, _vp, _pb, _pd, _vp]),
     ("mamba2_scan_prefill", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pb, _pd, _vp, _sz, _vp]),
     ("mamba2_scan_prefill_workspace_bytes", _sz, [_pb, _pd]),
+    ("mamba2_scan_prefill_static", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pb, _pd, _vp]),
     ("mamba2_scan_decode", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pb, _pd, _vp]),
     ("mamba2_gated_rmsnorm", _i32, [_vp, _vp, _vp, _vp, _i32, _f32, _i32, _i32, _i32, _vp]),
     ("mamba2_snapshot_count", ctypes.c_int64, [_pb, _i32]),

@@ -5,11 +5,19 @@
 // synchronises the host with the stream.
 #include <algorithm>
 #include <initializer_list>
+#include <mutex>
 #include <vector>
 
 #include "common.h"
 
 using namespace m2;
+
+// Scratch of mamba2_scan_prefill_static: the chunked scan's workspace for callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy until the process ends.  In host
+// code this name stands for the array, not for its device address: the address comes from
+// hipGetSymbolAddress, per device (static_scratch below).
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) char scratch[kStaticScratchBytes];
 
 namespace {
 
@@ -74,6 +82,25 @@ BatchDev batch_dev(const mamba2_recurrent_batch* rb) {
 }
 
 mamba2_status from_hip(hipError_t e) { return e == hipSuccess ? MAMBA2_OK : MAMBA2_HIP_ERROR; }
+
+// Device address of the current device's scratch array, looked up once per device with that
+// device current; null if the lookup fails.
+char* static_scratch() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static char* ptr[kMaxDevices] = {};
+  static bool done[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!done[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) p = nullptr;
+    ptr[dev] = (char*)p;
+    done[dev] = p != nullptr;
+  }
+  return ptr[dev];
+}
 
 // Shapes the prefill scan covers (both paths need N % 4 == 0 for 16-byte state access).
 bool scan_supported(const mamba2_dims* d) { return d->d_state % 4 == 0; }
@@ -148,6 +175,35 @@ mamba2_status mamba2_scan_prefill(void* dst, const void* xbc, const void* dt, co
   if (!workspace || workspace_bytes < lay.total) return MAMBA2_WORKSPACE_TOO_SMALL;
   if (((uintptr_t)workspace & 255) != 0) return MAMBA2_INVALID_ARGUMENT;
   ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace};
+  return from_hip(launch_scan_prefill(a, (hipStream_t)stream));
+}
+
+mamba2_status mamba2_scan_prefill_static(void* dst, const void* xbc, const void* dt, const float* a_log,
+                                         const float* dt_bias, const float* d, float* ssm_state,
+                                         const mamba2_recurrent_batch* rb, const mamba2_dims* dims, void* stream) {
+  mamba2_status st = check_dims(dims);
+  if (st != MAMBA2_OK) return st;
+  if (!rb) return MAMBA2_INVALID_ARGUMENT;
+  if (rb->num_rows > 0 && (!dst || !xbc || !dt || !a_log || !dt_bias || !d || !ssm_state))
+    return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16({dst, xbc, ssm_state})) return MAMBA2_INVALID_ARGUMENT;
+  st = check_batch(rb, dims, false);
+  if (st != MAMBA2_OK) return st;
+  if (!scan_supported(dims)) return MAMBA2_NOT_IMPLEMENTED;
+  if (rb->num_rows == 0) return MAMBA2_OK;
+  // the usual segment length if its workspace fits the scratch, else longer segments (fewer
+  // segment states) on the MFMA path, up to its longest
+  const bool mfma = scan_uses_mfma(dims);
+  int32_t L = scan_segment_length(rb, dims, mfma);
+  ScanLayout lay = scan_layout(rb, dims, L);
+  while (lay.total > kStaticScratchBytes && mfma && L < 4096) {
+    L = std::min<int32_t>(4096, 2 * L);
+    lay = scan_layout(rb, dims, L);
+  }
+  if (lay.total > kStaticScratchBytes) return MAMBA2_WORKSPACE_TOO_SMALL;
+  char* ws = static_scratch();
+  if (!ws) return MAMBA2_HIP_ERROR;
+  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, ws};
   return from_hip(launch_scan_prefill(a, (hipStream_t)stream));
 }
 

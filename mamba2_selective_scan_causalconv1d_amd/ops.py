@@ -106,6 +106,14 @@ def scan_prefill(dst, xbc, dt, a_log, dt_bias, D, ssm_state, batch: RecurrentBat
     return workspace
 
 
+def scan_prefill_static(dst, xbc, dt, a_log, dt_bias, D, ssm_state, batch: RecurrentBatch, dims: Dims,
+                        stream=None):
+    """scan_prefill with the library's own fixed scratch: no workspace, no allocation."""
+    st = LIB.mamba2_scan_prefill_static(_ptr(dst), _ptr(xbc), _ptr(dt), _ptr(a_log), _ptr(dt_bias), _ptr(D),
+                                        _ptr(ssm_state), batch.ref(), ctypes.byref(dims), _stream(stream))
+    _lib.check(st, "mamba2_scan_prefill_static")
+
+
 def scan_decode(dst, xbc, dt, a_log, dt_bias, D, ssm_state, batch: RecurrentBatch, dims: Dims,
                 stream=None):
     st = LIB.mamba2_scan_decode(_ptr(dst), _ptr(xbc), _ptr(dt), _ptr(a_log), _ptr(dt_bias), _ptr(D),
