@@ -254,3 +254,64 @@ def random_prefill(seed: int, sh: Shape, run_lengths, fresh=None, slots=None,
         fresh = rng.integers(0, 2, S)
     return make_prefill("random_s%d" % seed, seed, sh, run_lengths, slots, fresh, a_log_range,
                         rng=rng)
+
+
+# ------------------------------------------------------------ Mamba-3 SISO varlen forward
+
+
+@dataclass
+class Mamba3Workload:
+    """Inputs of the Mamba-3 SISO forward over packed sequences.  bf16 tensors as raw bits
+    (uint16): q, k [T, DK]; v, z [T, H, DV]; trap [T, H]; angles [T, NA].  fp32: adt, dt
+    [T, H]; q_bias, k_bias [H, DK]; d [H]."""
+    name: str
+    seed: int
+    run_lengths: np.ndarray  # int32 [S]
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    adt: np.ndarray
+    dt: np.ndarray
+    trap: np.ndarray
+    q_bias: np.ndarray
+    k_bias: np.ndarray
+    angles: np.ndarray
+    d: np.ndarray
+    z: np.ndarray
+
+    @property
+    def num_rows(self) -> int:
+        return int(self.run_lengths.sum())
+
+    @property
+    def nheads(self) -> int:
+        return int(self.v.shape[1])
+
+
+def mamba3_varlen(seed: int = 7, lengths=None, H: int = 32, DK: int = 128, DV: int = 64, NA: int = 32,
+                  decay_range=(0.05, 8.0), name=None) -> Mamba3Workload:
+    """Packed Mamba-3 SISO batch: three to five sequences of 3..15 chunks of 64 rows, never a
+    multiple of 64 rows (unless `lengths` is given).  Per head a decay rate A drawn log-uniform
+    over decay_range; per token dt = softplus(N(0,1) - 1) and adt = -A dt (the log of the
+    token's decay); q, k, v, z, trap, angles ~ N(0,1); q_bias, k_bias ~ N(0, 0.1); d ~ N(0,1)."""
+    rng = np.random.default_rng(seed)
+    if lengths is None:
+        S = int(rng.integers(3, 6))
+        lengths = [64 * (int(rng.integers(3, 16)) - 1) + int(rng.integers(1, 64)) for _ in range(S)]
+    rl = np.asarray(lengths, dtype=np.int32)
+    T = int(rl.sum())
+    A = np.exp(rng.uniform(np.log(decay_range[0]), np.log(decay_range[1]), H)).astype(np.float32)
+    q_bias = _normal(rng, (H, DK), 0.1)
+    k_bias = _normal(rng, (H, DK), 0.1)
+    d = _normal(rng, (H,), 1.0)
+    q = to_act(_normal(rng, (T, DK)), "bf16")
+    k = to_act(_normal(rng, (T, DK)), "bf16")
+    v = to_act(_normal(rng, (T, H, DV)), "bf16")
+    z = to_act(_normal(rng, (T, H, DV)), "bf16")
+    trap = to_act(_normal(rng, (T, H)), "bf16")
+    angles = to_act(_normal(rng, (T, NA)), "bf16")
+    u = _normal(rng, (T, H)).astype(np.float64) - 1.0
+    dt = np.log1p(np.exp(u)).astype(np.float32)
+    adt = (-A[None, :].astype(np.float64) * dt.astype(np.float64)).astype(np.float32)
+    return Mamba3Workload(name or "mamba3_varlen_s%d" % seed, seed, rl, q, k, v, adt, dt, trap, q_bias, k_bias,
+                          angles, d, z)

@@ -17,6 +17,7 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
+_SRCS = [_SRC, os.path.join(_HERE, "oracle_mamba3.c")]
 _LIB = os.path.join(_HERE, "liboracle.so")
 
 F32, BF16 = 0, 1
@@ -25,12 +26,13 @@ OK, INVALID_ARGUMENT, SLOT_OUT_OF_RANGE, SLOT_SHARED, RUN_LENGTHS = 0, 1, 2, 3, 
 
 
 def build(force: bool = False) -> str:
-    """Compile oracle.c with gcc (no fast-math, no FP contraction)."""
-    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+    """Compile oracle.c and oracle_mamba3.c with gcc (no fast-math, no FP contraction)."""
+    stale = not os.path.exists(_LIB) or any(os.path.getmtime(_LIB) < os.path.getmtime(f) for f in _SRCS)
+    if force or stale:
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
-            ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC",
-             _SRC, "-o", tmp, "-lm"])
+            ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp", "-shared", "-fPIC"] + _SRCS +
+            ["-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -65,6 +67,8 @@ def lib() -> ctypes.CDLL:
         for f in (L.oracle_conv1d, L.oracle_scan, L.oracle_gated_rmsnorm, L.oracle_check_batch,
                   L.oracle_max_threads, L.oracle_conv1d_snap, L.oracle_scan_snap, L.oracle_commit):
             f.restype = ctypes.c_int
+        L.oracle_mamba3_forward.argtypes = [vp] * 16 + [i32, i32, vp, i32, i32, i32, i32]
+        L.oracle_mamba3_forward.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [i32]
         L.oracle_set_threads.restype = None
         _lib = L
@@ -205,3 +209,25 @@ def max_threads() -> int:
 
 def set_threads(n: int) -> None:
     lib().oracle_set_threads(int(n))
+
+
+def mamba3_forward(q, k, v, adt, dt, trap, q_bias, k_bias, angles, d, z, run_lengths):
+    """Mamba-3 SISO forward over packed sequences (oracle_mamba3.c).  q, k [T, DK] bf16 bits;
+    v, z [T, H, DV] bf16 bits; adt, dt [T, H] f32; trap [T, H] bf16 bits; q_bias, k_bias [H, DK]
+    f32; angles [T, NA] bf16 bits; d [H] f32.  Returns (status, out [T, H, DV] bf16 bits,
+    final angle [S, H, NA] bf16 bits, final SSM [S, H, DV, DK] f32, final K [S, H, DK] f32,
+    final V [S, H, DV] bf16 bits)."""
+    T, H, DV = v.shape
+    DK = q.shape[1]
+    NA = angles.shape[1]
+    rl = np.ascontiguousarray(run_lengths, dtype=np.int32)
+    S = len(rl)
+    out = np.zeros((T, H, DV), dtype=np.uint16)
+    fa = np.zeros((S, H, NA), dtype=np.uint16)
+    fs = np.zeros((S, H, DV, DK), dtype=np.float32)
+    fk = np.zeros((S, H, DK), dtype=np.float32)
+    fv = np.zeros((S, H, DV), dtype=np.uint16)
+    st = lib().oracle_mamba3_forward(_p(out), _p(fa), _p(fs), _p(fk), _p(fv), _p(q), _p(k), _p(v), _p(adt),
+                                     _p(dt), _p(trap), _p(q_bias), _p(k_bias), _p(angles), _p(d), _p(z), S, T,
+                                     _p(rl), H, DK, DV, NA)
+    return st, out, fa, fs, fk, fv
