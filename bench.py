@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(ROOT, "mamba2_selective_scan_causalconv1d_amd", "csrc")
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "traffic_long_prefill_4x16384.txt")
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector (published)
 
 
 def parse():
@@ -291,6 +292,8 @@ def main():
 
     # ---------------------------------------------------------------- smaller prefills
     others = None if (args.no_others or args.no_decode) else run_other_prefills(args, torch, ops, W, dev)
+    if others is not None:
+        others["mamba3_siso_varlen"] = run_mamba3(args, torch, ops, W, dev)
 
     # ---------------------------------------------------------------- snapshots and verify
     snaps = None
@@ -737,6 +740,67 @@ def _cpu_model():
     except OSError:
         pass
     return None
+
+
+def mamba3_flops(wl, Q=64):
+    """Algorithmic flops of the chunked Mamba-3 forward: per row and head, q.k over the causal
+    triangle of its chunk DK (Q + 1), the masked product with v DV (Q + 1), and the state's
+    output term and the chunk state 2 DK DV each."""
+    T, H, DV = wl.v.shape
+    DK = wl.q.shape[1]
+    return T * H * (DK * (Q + 1) + DV * (Q + 1) + 4 * DK * DV)
+
+
+def run_mamba3(args, torch, ops, W, dev):
+    """The Mamba-3 SISO forward on its seeded packed batch (3-5 sequences of 3-15 chunks, 32
+    heads): 20 calls timed one by one with HIP events, each call's outputs and final states
+    digested and compared with the first call's; per-kernel times from one more call."""
+    wl = W.mamba3_varlen()
+    T, H, DV = wl.v.shape
+    DK, NA, S = wl.q.shape[1], wl.angles.shape[1], len(wl.run_lengths)
+    names = ("q", "k", "v", "adt", "dt", "trap", "q_bias", "k_bias", "angles", "d", "z")
+    ins = [ops.to_device(getattr(wl, n)) for n in names]
+    out = torch.empty((T, H, DV), dtype=torch.bfloat16, device=dev)
+    fa = torch.empty((S, H, NA), dtype=torch.bfloat16, device=dev)
+    fs = torch.empty((S, H, DV, DK), dtype=torch.float32, device=dev)
+    fk = torch.empty((S, H, DK), dtype=torch.float32, device=dev)
+    fv = torch.empty((S, H, DV), dtype=torch.bfloat16, device=dev)
+    b = ops.Mamba3Batch(wl.run_lengths, device=dev)
+    dims = ops.mamba3_dims(H, DK, DV, NA)
+    ws = torch.empty(max(256, ops.mamba3_workspace_bytes(b, dims)), dtype=torch.uint8, device=dev)
+
+    def call():
+        ops.mamba3_siso_forward(out, fa, fs, fk, fv, *ins, b, dims, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    ref = digest(torch, [out, fa, fs, fk, fv])
+    for _ in range(5):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(max(20, args.reps)):
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3)
+        assert digest(torch, [out, fa, fs, fk, fv]) == ref, "a Mamba-3 call's outputs differ from the first"
+    ops.timing_enable(64)
+    call()
+    torch.cuda.synchronize()
+    kern = {}
+    for name, ms in ops.timing_collect(64):
+        kern[name] = kern.get(name, 0.0) + 1e3 * ms
+    ops.timing_enable(0)
+    us = float(np.median(times))
+    fl = mamba3_flops(wl)
+    return {"workload": "mamba3_siso_varlen_s7", "rows": T, "sequences": S, "lengths": [int(x) for x in wl.run_lengths],
+            "heads": H, "qk_dim": DK, "v_dim": DV, "nangles": NA, "median_us": us, "min_us": float(np.min(times)),
+            "tokens_per_s": T / (us * 1e-6), "kernels_us": kern, "alg_flops": fl,
+            "achieved_TFLOPs": fl / (us * 1e-6) / 1e12,
+            "frac_fp32_vector_peak": fl / (us * 1e-6) / 1e12 / FP32_VECTOR_PEAK_TFLOPS,
+            "digest": ref, "digests_matched": len(times) + 1}
 
 
 def cpu_baseline(args, W, wl, sh):

@@ -34,6 +34,16 @@ class RecurrentBatchC(ctypes.Structure):
                 ("dev_slots", ctypes.c_void_p), ("dev_fresh", ctypes.c_void_p)]
 
 
+class Mamba3Dims(ctypes.Structure):
+    _fields_ = [("nheads", ctypes.c_int32), ("qk_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32),
+                ("nangles", ctypes.c_int32)]
+
+
+class Mamba3VarlenC(ctypes.Structure):
+    _fields_ = [("num_seqs", ctypes.c_int32), ("num_rows", ctypes.c_int32), ("run_lengths", ctypes.c_void_p),
+                ("dev_cu_seqlens", ctypes.c_void_p)]
+
+
 class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char_p), ("ms", ctypes.c_float)]
 
@@ -41,6 +51,7 @@ class KernelTime(ctypes.Structure):
 # (name, restype, argtypes) for every function the header declares
 _vp, _i32, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_float, ctypes.c_size_t
 _pb, _pd = ctypes.POINTER(RecurrentBatchC), ctypes.POINTER(Dims)
+_p3b, _p3d = ctypes.POINTER(Mamba3VarlenC), ctypes.POINTER(Mamba3Dims)
 SIGNATURES = [
     ("mamba2_conv1d", _i32, [_vp, _vp, _vp, _vp, _vp, _pb, _pd, _vp]),
     ("mamba2_scan_prefill", _i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _pb, _pd, _vp, _sz, _vp]),
@@ -64,6 +75,8 @@ SIGNATURES = [
     ("mamba2_status_string", ctypes.c_char_p, [_i32]),
     ("mamba2_timing_enable", _i32, [_i32]),
     ("mamba2_timing_collect", _i32, [ctypes.POINTER(KernelTime), _i32]),
+    ("mamba3_siso_forward", _i32, [_vp] * 16 + [_p3b, _p3d, _vp, _sz, _vp]),
+    ("mamba3_siso_forward_workspace_bytes", _sz, [_p3b, _p3d]),
 ]
 
 _lib = None

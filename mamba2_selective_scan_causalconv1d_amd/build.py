@@ -14,7 +14,7 @@ OBJ = os.path.join(ROOT, "_build")
 ARCH = os.environ.get("MAMBA2_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["api.hip", "timing.hip", "conv1d.hip", "gated_rmsnorm.hip", "scan_decode.hip", "snapshots.hip", "padded.hip", "linear.hip",
-           "ssd_common.hip", "ssd_generic.hip", "ssd_mfma.hip"]
+           "ssd_common.hip", "ssd_generic.hip", "ssd_mfma.hip", "mamba3.hip"]
 
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH, "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -1,0 +1,599 @@
+// Mamba-3 SISO forward over packed variable-length sequences, for gfx950.
+//
+// The operator of "Mamba-3 SISO Long-Ragged Multi-Chunk Joint States Full VJP", section
+// "What You Have", steps 1-7, per packed sequence and value head h:
+//   qh_t, kh_t = rotary(q_t + q_bias[h], phi_t), rotary(k_t + k_bias[h], phi_t)  (one Q/K head
+//               shared by the H value heads; pair a = components (2a, 2a+1) turned by phi_t[a])
+//   phi_t[a]  = (sum_{s<=t} tanh(angles_s[a]) pi dt_s[h]) mod 2 pi
+//   p = sigmoid(trap); sg_t = dt_{t+1} (1 - p_{t+1}) (0 at the sequence's last token);
+//   scale_t = dt_t p_t + sg_t
+//   y_t = sum_{s<=t} exp(sum_{r=s+1..t} adt_r) (qh_t . kh_s) scale_s v_s + d v_t - sg_t (qh_t . kh_t) v_t
+//   out_t = y_t z_t sigmoid(z_t)
+// and per sequence the final angle, the final state sum_s exp(sum_{r>s} adt_r) scale_s v_s kh_s^T,
+// the last token's key kh and value v.
+//
+// Chunked form (64-row chunks, each within one sequence), with cs_i the sum of adt over the
+// chunk's rows up to i and S_in the state entering the chunk:
+//   y_i = sum_{j<=i} M_ij v_j + exp(cs_i) qh_i . S_in,
+//   M_ij = (qh_i . kh_j) exp(cs_i - cs_j) scale_j (j < i),  M_ii = (qh_i . kh_i) dt_i p_i + d
+//   (the diagonal folds the correction: scale_i - sg_i = dt_i p_i, and the skip d),
+//   S_loc = sum_j exp(cs_last - cs_j) scale_j v_j kh_j^T,  S_in(next) = exp(cs_last) S_in + S_loc.
+// Launches: chunk tables; per (chunk, head) the chunk's rotary-angle totals; per (chunk, head)
+// the chunk state (and a sequence's finals); the state pass per (sequence, head); per (chunk,
+// head) the outputs.  The contractions (q.k over a chunk, the state's output term, M v and the
+// chunk state) run on the fp32 matrix instruction v_mfma_f32_16x16x4f32 with operands staged in
+// LDS: the operator's queries and keys are fp32 values after the bias and the rotation, and
+// fp32 keeps every contraction well inside the output and state bars.  Lane layout (checked on
+// the GPU): lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; result register r of lane l
+// is D[4 (l / 16) + r][l % 16].  Each lane reads four consecutive k of its row in one 16-byte
+// LDS read and issues four instructions, so instruction m covers k = 16 c + 4 (l / 16) + m: the
+// same order on both operands, hence the same sum.
+// The rotary angles are summed in double (their running sum covers whole sequences).
+#include <initializer_list>
+
+#include "common.h"
+
+#include "../../include/mamba3.h"
+
+namespace m2 {
+namespace {
+
+constexpr int kC = 64;       // chunk rows
+constexpr int kMaxDK = 128;  // query / key width
+constexpr int kMaxDV = 64;   // value width
+constexpr int kMaxNA = 64;   // rotary pairs
+
+__device__ __forceinline__ float bf(const bf16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+// The rotary angles are summed in double: the running sum covers up to thousands of tokens,
+// and fp32 rounding of its partial sums would add up to ~1e-4 radian.
+constexpr double kTwoPiD = 6.283185307179586476925287;
+constexpr double kPiD = 3.141592653589793238462643;
+__device__ __forceinline__ double mod2pi(double x) {
+  const double r = x - kTwoPiD * floor(x * (1.0 / kTwoPiD));
+  return r < 0.0 ? r + kTwoPiD : (r >= kTwoPiD ? r - kTwoPiD : r);
+}
+// theta dt of one token and pair: tanh in fp32 (relative error ~1e-7), the product in double
+__device__ __forceinline__ double angle_step(const bf16_t* a, float dtv) {
+  return (double)tanhf(bf16_to_f32(*a)) * kPiD * (double)dtv;
+}
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+// D += A B over 16 k: a, b the lane's four consecutive k of its A row and B column.
+__device__ __forceinline__ f32x4 mfma16(const float4& a, const float4& b, f32x4 c) {
+  c = mfma4(a.x, b.x, c);
+  c = mfma4(a.y, b.y, c);
+  c = mfma4(a.z, b.z, c);
+  return mfma4(a.w, b.w, c);
+}
+__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+
+struct M3Ptrs {
+  const bf16_t* q;
+  const bf16_t* k;
+  const bf16_t* v;
+  const float* adt;
+  const float* dt;
+  const bf16_t* trap;
+  const float* q_bias;
+  const float* k_bias;
+  const bf16_t* angles;
+  const float* d;
+  const bf16_t* z;
+  bf16_t* out;
+  bf16_t* fin_angle;
+  float* fin_ssm;
+  float* fin_k;
+  bf16_t* fin_v;
+  const int2* seq_info;   // [S] (first chunk, chunks)
+  const int4* chunk_info;  // [nch] (sequence, first row, rows, index in sequence)
+  float* ang_tot;         // [nch][H][NA] sum over the chunk of tanh(angles) pi dt, then the angle entering the chunk
+  float* decay;           // [nch][H] exp(sum of adt over the chunk)
+  float* state;           // [nch][H][DV][DK]: at chunk c + 1 the local state of chunk c, then S_in(c + 1)
+  int H, DK, DV, NA;
+};
+
+// ------------------------------------------------------------------ rotary-angle totals
+
+// grid (chunk), 256 threads: theta = tanh(angles) pi for the chunk's rows (once, for every
+// head) and the heads' dt in LDS; then per (head, pair) the chunk's sum of theta dt, in double,
+// stored reduced into [0, 2 pi).  Heads in blocks of 64.
+__global__ __launch_bounds__(256) void m3_angle_totals_kernel(M3Ptrs P, int nch) {
+  __shared__ float sTh[kC][kMaxNA + 1];
+  __shared__ float sDt[kC][65];
+  const int c = blockIdx.x;
+  if (c >= nch) return;
+  const int4 ci = P.chunk_info[c];
+  for (int e = threadIdx.x; e < kC * P.NA; e += blockDim.x) {
+    const int j = e / P.NA, a = e - j * P.NA;
+    sTh[j][a] = j < ci.z ? tanhf(bf(P.angles + (size_t)(ci.y + j) * P.NA + a)) : 0.f;
+  }
+  for (int h0 = 0; h0 < P.H; h0 += 64) {
+    const int nh = min(64, P.H - h0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kC * nh; e += blockDim.x) {
+      const int j = e / nh, hh = e - j * nh;
+      sDt[j][hh] = j < ci.z ? P.dt[(size_t)(ci.y + j) * P.H + h0 + hh] : 0.f;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < nh * P.NA; e += blockDim.x) {
+      const int hh = e / P.NA, a = e - hh * P.NA;
+      double acc = 0.0;
+      for (int j = 0; j < ci.z; ++j) acc += (double)sTh[j][a] * (double)sDt[j][hh];
+      P.ang_tot[((size_t)c * P.H + h0 + hh) * P.NA + a] = (float)mod2pi(acc * kPiD);
+    }
+  }
+}
+
+// grid (sequence, (head, pair) blocks), 256 threads: per (head, pair), the rotary angle entering
+// each chunk of the sequence (the sum of the earlier chunks' totals, mod 2 pi), in place of the
+// totals.  The totals are loaded four chunks at a time.
+__global__ __launch_bounds__(256) void m3_angle_prefix_kernel(M3Ptrs P, int S) {
+  const int s = blockIdx.x;
+  const int e = blockIdx.y * blockDim.x + threadIdx.x;
+  if (s >= S || e >= P.H * P.NA) return;
+  const int2 si = P.seq_info[s];
+  double acc = 0.0;
+  for (int k0 = 0; k0 < si.y; k0 += 4) {
+    float t[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) t[i] = k0 + i < si.y ? P.ang_tot[(size_t)(si.x + k0 + i) * P.H * P.NA + e] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (k0 + i < si.y) {
+        P.ang_tot[(size_t)(si.x + k0 + i) * P.H * P.NA + e] = (float)acc;
+        acc = mod2pi(acc + (double)t[i]);
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ chunk rows
+
+// Per-row scalars of a chunk for head h and its rotary angles, in LDS:
+//   cs[i] = sum of adt over rows <= i of the chunk; sc[i] = scale_i; dp[i] = dt_i p_i;
+//   phi[i][a] = the rotary angle of row i, pair a, and its cosine and sine.
+// kCS: the rotation kept as cos and sin (for two rotations of the same rows), else the angle.
+template <bool kCS>
+struct RowLds;
+template <>
+struct RowLds<false> {
+  float cs[kC], sc[kC], dp[kC];
+  float phi[kC][kMaxNA];
+};
+template <>
+struct RowLds<true> {
+  float cs[kC], sc[kC], dp[kC];
+  float cosv[kC][kMaxNA], sinv[kC][kMaxNA];
+};
+
+template <bool kCS>
+__device__ void chunk_rows(const M3Ptrs& P, int c, const int4& ci, int h, RowLds<kCS>& L) {
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, nw = blockDim.x >> 6;
+  const int r = ci.y + lane;
+  const bool on = lane < ci.z;
+  const int2 si = P.seq_info[ci.x];
+  if (w == 0) {
+    // decay prefix, p, scale (the next row may lie in the next chunk of the same sequence)
+    const float a = on ? P.adt[(size_t)r * P.H + h] : 0.f;
+    float cs = a;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const float t = __shfl_up(cs, o, 64);
+      if (lane >= o) cs += t;
+    }
+    const bool last_chunk = ci.w == si.y - 1;
+    const bool has_next = on && (lane + 1 < ci.z || !last_chunk);
+    const float dtv = on ? P.dt[(size_t)r * P.H + h] : 0.f;
+    const float p = on ? sigmoidf_(bf(P.trap + (size_t)r * P.H + h)) : 0.f;
+    float sg = 0.f;
+    if (has_next) {
+      const float dtn = P.dt[(size_t)(r + 1) * P.H + h];
+      const float pn = sigmoidf_(bf(P.trap + (size_t)(r + 1) * P.H + h));
+      sg = dtn * (1.f - pn);
+    }
+    L.cs[lane] = cs;
+    L.sc[lane] = dtv * p + sg;
+    L.dp[lane] = dtv * p;
+  }
+  // rotary angles: the angle entering the chunk (the prefix kernel's), then the running sum
+  // over this chunk's rows
+  const float dtv = on ? P.dt[(size_t)r * P.H + h] : 0.f;
+  for (int a = w; a < P.NA; a += nw) {
+    const double base = (double)P.ang_tot[((size_t)c * P.H + h) * P.NA + a];
+    double v = on ? angle_step(P.angles + (size_t)r * P.NA + a, dtv) : 0.0;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const double t = __shfl_up(v, o, 64);
+      if (lane >= o) v += t;
+    }
+    const float ph = (float)mod2pi(base + v);
+    if constexpr (kCS) {
+      float sn, cs;
+      sincosf(ph, &sn, &cs);
+      L.cosv[lane][a] = cs;
+      L.sinv[lane][a] = sn;
+    } else {
+      L.phi[lane][a] = ph;
+    }
+  }
+}
+
+// dst = rotary(src_i + bias, phi_i) for the chunk's rows (zeros past its end), fp32: row i at
+// dst[i * ld + n], or transposed (kT) at dst[n * ld + i].  One thread per (row, component pair).
+template <bool kT, bool kCS>
+__device__ void rotated_rows(const bf16_t* src, const float* bias, const RowLds<kCS>& L, const int4& ci, int DK,
+                             int NA, float* dst, int ld) {
+  const int npair = DK / 2;
+  for (int e = threadIdx.x; e < kC * npair; e += blockDim.x) {
+    const int i = e / npair, a = e - i * npair;
+    float x0 = 0.f, x1 = 0.f;
+    if (i < ci.z) {
+      const uint32_t two = *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + i) * DK + 2 * a);
+      x0 = bf16_to_f32(two & 0xffffu) + bias[2 * a];
+      x1 = bf16_to_f32(two >> 16) + bias[2 * a + 1];
+      if (a < NA) {
+        float cs, sn;
+        if constexpr (kCS) {
+          cs = L.cosv[i][a];
+          sn = L.sinv[i][a];
+        } else {
+          sincosf(L.phi[i][a], &sn, &cs);
+        }
+        const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
+        x0 = r0;
+        x1 = r1;
+      }
+    }
+    if (kT) {
+      dst[(2 * a) * ld + i] = x0;
+      dst[(2 * a + 1) * ld + i] = x1;
+    } else {
+      dst[i * ld + 2 * a] = x0;
+      dst[i * ld + 2 * a + 1] = x1;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ chunk states
+
+constexpr int kLdK = kMaxDK + 4;  // LDS row pitch of query / key / state rows (floats)
+constexpr int kLdT = kC + 4;      // LDS row pitch of transposed tiles (a chunk's rows along a row)
+
+// grid (chunk, head), 512 threads: S_loc = sum_j exp(cs_last - cs_j) scale_j v_j kh_j^T, stored
+// at chunk c + 1 (the sequence's last chunk: in the final-state output, which the pass then
+// completes); the chunk's decay factor; for a sequence's last chunk, its final K, V and angle.
+// S_loc [DV][DK] = (w o V)^T K: 16 x 16 tiles dealt over the eight waves, the chunk's rows as k,
+// both operands transposed in LDS so that a lane's four k are one 16-byte read.
+__global__ __launch_bounds__(512) void m3_chunk_state_kernel(M3Ptrs P, int nch) {
+  __shared__ __attribute__((aligned(16))) float sKt[kMaxDK * kLdT];  // kh^T [n][j]
+  __shared__ __attribute__((aligned(16))) float sVt[kMaxDV * kLdT];  // (w v)^T [e][j]
+  __shared__ RowLds<false> L;
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= nch) return;
+  const int4 ci = P.chunk_info[c];
+  const int2 si = P.seq_info[ci.x];
+  const bool last = ci.w == si.y - 1;
+  chunk_rows(P, c, ci, h, L);
+  __syncthreads();
+  rotated_rows<true, false>(P.k, P.k_bias + (size_t)h * P.DK, L, ci, P.DK, P.NA, sKt, kLdT);
+  const float cl = L.cs[ci.z - 1];
+  for (int e = threadIdx.x; e < kC * P.DV; e += blockDim.x) {
+    const int j = e / P.DV, f = e - j * P.DV;
+    float val = 0.f;
+    if (j < ci.z) val = bf(P.v + ((size_t)(ci.y + j) * P.H + h) * P.DV + f) * (__expf(cl - L.cs[j]) * L.sc[j]);
+    sVt[f * kLdT + j] = val;
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const int ne = P.DV / 16, nn = P.DK / 16;
+  float* dst = last ? P.fin_ssm + ((size_t)ci.x * P.H + h) * (size_t)P.DV * P.DK
+                    : P.state + ((size_t)(c + 1) * P.H + h) * (size_t)P.DV * P.DK;
+  const int nkc = (ci.z + 15) / 16;  // 16-row steps holding rows of the chunk (the rest is zero)
+  for (int t = w; t < ne * nn; t += (int)(blockDim.x >> 6)) {
+    const int eb = t / nn, nb = t - eb * nn;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int kc = 0; kc < nkc; ++kc) {
+      const float4 a4 = lds4(sVt + (eb * 16 + lr) * kLdT + 16 * kc + 4 * lg);
+      const float4 b4 = lds4(sKt + (nb * 16 + lr) * kLdT + 16 * kc + 4 * lg);
+      acc = mfma16(a4, b4, acc);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dst[(size_t)(eb * 16 + 4 * lg + r) * P.DK + nb * 16 + lr] = acc[r];
+  }
+  if (threadIdx.x == 0) P.decay[(size_t)c * P.H + h] = __expf(cl);
+  if (last) {
+    const int il = ci.z - 1;
+    for (int n = threadIdx.x; n < P.DK; n += blockDim.x)
+      P.fin_k[((size_t)ci.x * P.H + h) * P.DK + n] = sKt[n * kLdT + il];
+    for (int f = threadIdx.x; f < P.DV; f += blockDim.x)
+      P.fin_v[((size_t)ci.x * P.H + h) * P.DV + f] = P.v[((size_t)(ci.y + il) * P.H + h) * P.DV + f];
+    for (int a2 = threadIdx.x; a2 < P.NA; a2 += blockDim.x)
+      P.fin_angle[((size_t)ci.x * P.H + h) * P.NA + a2] = (bf16_t)f32_to_bf16(L.phi[il][a2]);
+  }
+}
+
+// ------------------------------------------------------------------ state pass
+
+// One thread per float4 of a head's state, per sequence (strided over grid z): S_in(0) = 0;
+// S_in(c + 1) = dec(c) S_in(c) + S_loc(c) written over S_loc(c) at chunk c + 1; the final
+// state = dec(last) S_in(last) + S_loc(last), completed in place in the final-state output.
+__global__ __launch_bounds__(256) void m3_pass_kernel(M3Ptrs P, int S) {
+  const int f = blockIdx.x * blockDim.x + threadIdx.x;
+  const int h = blockIdx.y;
+  const int f4 = P.DV * P.DK / 4;
+  if (f >= f4) return;
+  for (int s = blockIdx.z; s < S; s += gridDim.z) {
+    const int2 si = P.seq_info[s];
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k = 0; k < si.y; ++k) {
+      const int c = si.x + k;
+      const float dec = P.decay[(size_t)c * P.H + h];
+      float4* loc = k + 1 < si.y ? reinterpret_cast<float4*>(P.state + ((size_t)(c + 1) * P.H + h) * (size_t)P.DV * P.DK)
+                                 : reinterpret_cast<float4*>(P.fin_ssm + ((size_t)s * P.H + h) * (size_t)P.DV * P.DK);
+      const float4 l = loc[f];
+      acc = make_float4(fmaf(dec, acc.x, l.x), fmaf(dec, acc.y, l.y), fmaf(dec, acc.z, l.z), fmaf(dec, acc.w, l.w));
+      loc[f] = acc;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ outputs
+
+// grid (chunk, head), 512 threads (two waves per SIMD at one workgroup per CU).  (1) rotated
+// queries and keys of the chunk in LDS (rows), the
+// values transposed; (2) G = qh kh^T on the ten lower-triangular 16 x 16 tiles, turned into
+// M (exp(cs_i - cs_j) scale_j below the diagonal, dt_i p_i and d on it, zero above), in LDS;
+// (3) the state entering the chunk over the keys' LDS; (4) Y = exp(cs_i) qh S_in^T + M v on
+// 16 x 16 tiles (rows x value columns), the gate, bf16 stores.
+__global__ __launch_bounds__(512) void m3_chunk_out_kernel(M3Ptrs P, int nch) {
+  __shared__ __attribute__((aligned(16))) float sQ[kC * kLdK];
+  __shared__ __attribute__((aligned(16))) float sKS[kC * kLdK];  // keys [j][n], then S_in [e][n]
+  __shared__ __attribute__((aligned(16))) float sVt[kMaxDV * kLdT];  // v^T [e][j]
+  __shared__ __attribute__((aligned(16))) float sM[kC * kLdT];
+  __shared__ RowLds<true> L;
+  const int c = blockIdx.x, h = blockIdx.y;
+  if (c >= nch) return;
+  const int4 ci = P.chunk_info[c];
+  chunk_rows(P, c, ci, h, L);
+  __syncthreads();
+  rotated_rows<false, true>(P.q, P.q_bias + (size_t)h * P.DK, L, ci, P.DK, P.NA, sQ, kLdK);
+  rotated_rows<false, true>(P.k, P.k_bias + (size_t)h * P.DK, L, ci, P.DK, P.NA, sKS, kLdK);
+  for (int e = threadIdx.x; e < kC * P.DV; e += blockDim.x) {
+    const int j = e / P.DV, f = e - j * P.DV;
+    sVt[f * kLdT + j] = j < ci.z ? bf(P.v + ((size_t)(ci.y + j) * P.H + h) * P.DV + f) : 0.f;
+  }
+  __syncthreads();
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
+  const float dh = P.d[h];
+  const int nkc = P.DK / 16;
+  const int nib = (ci.z + 15) / 16;  // 16-row blocks holding rows of the chunk
+  // M on the lower-triangular tiles (ib, jb), jb <= ib; tiles dealt round robin over the waves
+  const int nwv = blockDim.x >> 6;
+  for (int t = w; t < 10; t += nwv) {
+    const int ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+    const int jb = t - ib * (ib + 1) / 2;
+    f32x4 g = {0.f, 0.f, 0.f, 0.f};
+    if (ib < nib) {
+      for (int kc = 0; kc < nkc; ++kc)
+        g = mfma16(lds4(sQ + (ib * 16 + lr) * kLdK + 16 * kc + 4 * lg), lds4(sKS + (jb * 16 + lr) * kLdK + 16 * kc + 4 * lg),
+                   g);
+    }
+    const int j = jb * 16 + lr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = ib * 16 + 4 * lg + r;
+      float m = 0.f;
+      if (j < i) m = g[r] * __expf(L.cs[i] - L.cs[j]) * L.sc[j];
+      else if (j == i) m = fmaf(g[r], L.dp[i], dh);
+      sM[i * kLdT + j] = m;
+    }
+  }
+  // the tiles above the diagonal are zero
+  for (int e = threadIdx.x; e < kC * kC; e += blockDim.x) {
+    const int i = e / kC, j = e - i * kC;
+    if ((j >> 4) > (i >> 4)) sM[i * kLdT + j] = 0.f;
+  }
+  __syncthreads();  // M complete; the keys are no longer read
+  const bool has_in = ci.w > 0;
+  if (has_in) {
+    const float* sin = P.state + ((size_t)c * P.H + h) * (size_t)P.DV * P.DK;
+    for (int e = threadIdx.x; e < P.DV * (P.DK / 4); e += blockDim.x) {
+      const int f = e / (P.DK / 4), n4 = e - f * (P.DK / 4);
+      *reinterpret_cast<float4*>(sKS + f * kLdK + 4 * n4) = reinterpret_cast<const float4*>(sin + (size_t)f * P.DK)[n4];
+    }
+  }
+  __syncthreads();
+  const int neb = P.DV / 16;
+  for (int t = w; t < nib * neb; t += nwv) {
+    const int ib = t / neb, eb = t - ib * neb;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    if (has_in) {
+      for (int kc = 0; kc < nkc; ++kc)
+        y = mfma16(lds4(sQ + (ib * 16 + lr) * kLdK + 16 * kc + 4 * lg), lds4(sKS + (eb * 16 + lr) * kLdK + 16 * kc + 4 * lg),
+                   y);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) y[r] *= __expf(L.cs[ib * 16 + 4 * lg + r]);
+    }
+    for (int jc = 0; jc <= ib; ++jc)
+      y = mfma16(lds4(sM + (ib * 16 + lr) * kLdT + 16 * jc + 4 * lg), lds4(sVt + (eb * 16 + lr) * kLdT + 16 * jc + 4 * lg), y);
+    const int f = eb * 16 + lr;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = ib * 16 + 4 * lg + r;
+      if (i < ci.z) {
+        const size_t o = ((size_t)(ci.y + i) * P.H + h) * P.DV + f;
+        const float zf = bf(P.z + o);
+        P.out[o] = (bf16_t)f32_to_bf16(y[r] * zf * sigmoidf_(zf));
+      }
+    }
+  }
+}
+
+size_t al256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// The operator's arguments (device pointers unless noted).
+struct M3Args {
+  void* out;
+  void* fin_angle;
+  float* fin_ssm;
+  float* fin_k;
+  void* fin_v;
+  const void *q, *k, *v;
+  const float *adt, *dt;
+  const void* trap;
+  const float *q_bias, *k_bias;
+  const void* angles;
+  const float* d;
+  const void* z;
+  const int32_t* cu_seqlens;
+  int32_t num_seqs;
+  mamba3_dims dims;
+};
+
+}  // namespace
+
+// Workspace layout of the Mamba-3 forward (each section 256-byte aligned).
+struct M3Layout {
+  int64_t nch;
+  size_t off_seq, off_chunk, off_ang, off_dec, off_state, total;
+};
+
+M3Layout m3_layout(const mamba3_varlen* b, const mamba3_dims* d) {
+  M3Layout L{};
+  int64_t nch = 0;
+  for (int s = 0; s < b->num_seqs; ++s) nch += (b->run_lengths[s] + kC - 1) / kC;
+  L.nch = nch;
+  size_t off = 0;
+  L.off_seq = off;
+  off = al256(off + (size_t)b->num_seqs * sizeof(int2));
+  L.off_chunk = off;
+  off = al256(off + (size_t)nch * sizeof(int4));
+  L.off_ang = off;
+  off = al256(off + (size_t)nch * d->nheads * d->nangles * sizeof(float));
+  L.off_dec = off;
+  off = al256(off + (size_t)nch * d->nheads * sizeof(float));
+  L.off_state = off;
+  off = al256(off + (size_t)nch * d->nheads * d->v_dim * d->qk_dim * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+bool m3_supported(const mamba3_dims* d) {
+  // the matrix tiles are 16 wide in both widths
+  return d->nheads >= 1 && d->qk_dim >= 16 && d->qk_dim <= kMaxDK && d->qk_dim % 16 == 0 && d->v_dim >= 16 &&
+         d->v_dim <= kMaxDV && d->v_dim % 16 == 0 && d->nangles >= 0 && d->nangles <= kMaxNA &&
+         2 * d->nangles <= d->qk_dim;
+}
+
+hipError_t launch_segment_tables(const int32_t* cu, int S, int seg_len, int2* seq_info, int4* seg_info,
+                                 hipStream_t st);
+
+namespace {
+hipError_t launch_mamba3_forward(const M3Args& a, const M3Layout& lay, char* ws, hipStream_t st) {
+  M3Ptrs P{};
+  P.q = (const bf16_t*)a.q;
+  P.k = (const bf16_t*)a.k;
+  P.v = (const bf16_t*)a.v;
+  P.adt = a.adt;
+  P.dt = a.dt;
+  P.trap = (const bf16_t*)a.trap;
+  P.q_bias = a.q_bias;
+  P.k_bias = a.k_bias;
+  P.angles = (const bf16_t*)a.angles;
+  P.d = a.d;
+  P.z = (const bf16_t*)a.z;
+  P.out = (bf16_t*)a.out;
+  P.fin_angle = (bf16_t*)a.fin_angle;
+  P.fin_ssm = a.fin_ssm;
+  P.fin_k = a.fin_k;
+  P.fin_v = (bf16_t*)a.fin_v;
+  P.seq_info = (const int2*)(ws + lay.off_seq);
+  P.chunk_info = (const int4*)(ws + lay.off_chunk);
+  P.ang_tot = (float*)(ws + lay.off_ang);
+  P.decay = (float*)(ws + lay.off_dec);
+  P.state = (float*)(ws + lay.off_state);
+  P.H = a.dims.nheads;
+  P.DK = a.dims.qk_dim;
+  P.DV = a.dims.v_dim;
+  P.NA = a.dims.nangles;
+  const int S = a.num_seqs;
+  const int nch = (int)lay.nch;
+  hipError_t e = launch_segment_tables(a.cu_seqlens, S, kC, (int2*)(ws + lay.off_seq), (int4*)(ws + lay.off_chunk), st);
+  if (e != hipSuccess) return e;
+  if (P.NA > 0) {
+    M2_LAUNCH("m3_angle_totals", m3_angle_totals_kernel, dim3((unsigned)nch), dim3(256), 0, st, P, nch);
+    M2_LAUNCH("m3_angle_prefix", m3_angle_prefix_kernel, dim3((unsigned)S, (unsigned)((P.H * P.NA + 255) / 256)),
+              dim3(256), 0, st, P, S);
+  }
+  M2_LAUNCH("m3_chunk_state", m3_chunk_state_kernel, dim3((unsigned)nch, (unsigned)P.H), dim3(512), 0, st, P, nch);
+  const int f4 = P.DV * P.DK / 4;
+  M2_LAUNCH("m3_pass", m3_pass_kernel, dim3((unsigned)((f4 + 255) / 256), (unsigned)P.H, (unsigned)(S < 65535 ? S : 65535)),
+            dim3(256), 0, st, P, S);
+  M2_LAUNCH("m3_chunk_out", m3_chunk_out_kernel, dim3((unsigned)nch, (unsigned)P.H), dim3(512), 0, st, P, nch);
+  return hipSuccess;
+}
+
+bool aligned16_all(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (((uintptr_t)p & 15) != 0) return false;
+  return true;
+}
+
+// Run lengths: each >= 1, summing to num_rows; sizes within 32-bit element offsets.
+mamba2_status m3_check(const mamba3_varlen* b, const mamba3_dims* d) {
+  if (!b || !d) return MAMBA2_INVALID_ARGUMENT;
+  if (b->num_seqs < 0 || b->num_rows < 0) return MAMBA2_INVALID_ARGUMENT;
+  if (d->nheads < 1 || d->qk_dim < 1 || d->v_dim < 1 || d->nangles < 0 || 2 * (int64_t)d->nangles > d->qk_dim)
+    return MAMBA2_INVALID_ARGUMENT;
+  if (b->num_seqs > 0 && (!b->run_lengths || !b->dev_cu_seqlens)) return MAMBA2_INVALID_ARGUMENT;
+  int64_t sum = 0;
+  for (int s = 0; s < b->num_seqs; ++s) {
+    if (b->run_lengths[s] < 1) return MAMBA2_RUN_LENGTHS;
+    sum += b->run_lengths[s];
+  }
+  if (sum != b->num_rows) return MAMBA2_RUN_LENGTHS;
+  if (!m3_supported(d)) return MAMBA2_NOT_IMPLEMENTED;
+  const int64_t T = b->num_rows;
+  if (T * d->nheads * d->v_dim >= ((int64_t)1 << 31) || T * d->qk_dim >= ((int64_t)1 << 31))
+    return MAMBA2_NOT_IMPLEMENTED;
+  return MAMBA2_OK;
+}
+}  // namespace
+
+}  // namespace m2
+
+using namespace m2;
+
+extern "C" {
+
+size_t mamba3_siso_forward_workspace_bytes(const mamba3_varlen* batch, const mamba3_dims* dims) {
+  if (m3_check(batch, dims) != MAMBA2_OK || batch->num_rows == 0) return 0;
+  return m3_layout(batch, dims).total;
+}
+
+mamba2_status mamba3_siso_forward(void* out, void* final_angle, float* final_ssm, float* final_k, void* final_v,
+                                  const void* q, const void* k, const void* v, const float* adt, const float* dt,
+                                  const void* trap, const float* q_bias, const float* k_bias, const void* angles,
+                                  const float* d, const void* z, const mamba3_varlen* batch, const mamba3_dims* dims,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+  mamba2_status st = m3_check(batch, dims);
+  if (st != MAMBA2_OK) return st;
+  if (batch->num_rows == 0) return MAMBA2_OK;
+  if (!out || (dims->nangles > 0 && !final_angle) || !final_ssm || !final_k || !final_v || !q || !k || !v || !adt ||
+      !dt || !trap || !q_bias || !k_bias || (dims->nangles > 0 && !angles) || !d || !z)
+    return MAMBA2_INVALID_ARGUMENT;
+  if (!aligned16_all({out, final_ssm, final_k, q, k, v, z, q_bias, k_bias})) return MAMBA2_INVALID_ARGUMENT;
+  const M3Layout lay = m3_layout(batch, dims);
+  if (!workspace || workspace_bytes < lay.total) return MAMBA2_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & 255) != 0) return MAMBA2_INVALID_ARGUMENT;
+  M3Args a{out, final_angle, final_ssm, final_k, final_v, q, k, v, adt, dt, trap, q_bias, k_bias, angles, d, z,
+           batch->dev_cu_seqlens, batch->num_seqs, *dims};
+  return launch_mamba3_forward(a, lay, (char*)workspace, (hipStream_t)stream) == hipSuccess ? MAMBA2_OK
+                                                                                            : MAMBA2_HIP_ERROR;
+}
+
+}  // extern "C"

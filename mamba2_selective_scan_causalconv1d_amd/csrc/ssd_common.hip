@@ -176,6 +176,14 @@ ScanLayout scan_layout(const mamba2_recurrent_batch* rb, const mamba2_dims* d, i
   return L;
 }
 
+// Sequence and segment tables of any packed batch (also the chunk tables of the Mamba-3
+// forward): seq_info [S], seg_info [number of segments].
+hipError_t launch_segment_tables(const int32_t* cu, int S, int seg_len, int2* seq_info, int4* seg_info,
+                                 hipStream_t st) {
+  M2_LAUNCH("scan_setup", scan_setup_kernel, dim3(1), dim3(kSetupThreads), 0, st, cu, S, seg_len, seq_info, seg_info);
+  return hipSuccess;
+}
+
 hipError_t launch_scan_setup(const ScanArgs& a, hipStream_t st) {
   M2_LAUNCH("scan_setup", scan_setup_kernel, dim3(1), dim3(kSetupThreads), 0, st, a.bd.cu_seqlens,
             a.bd.num_seqs, a.lay.seg_len, (int2*)(a.ws + a.lay.off_seq_info),

@@ -15,7 +15,7 @@ import numpy as np
 import torch
 
 from . import _lib
-from ._lib import Dims, KernelTime, Mamba2Error, RecurrentBatchC  # noqa: F401
+from ._lib import Dims, KernelTime, Mamba2Error, Mamba3Dims, Mamba3VarlenC, RecurrentBatchC  # noqa: F401
 
 LIB = _lib.load()
 
@@ -226,6 +226,53 @@ def timing_collect(max_records: int = 4096):
     if n < 0:
         raise Mamba2Error(_lib.HIP_ERROR, "mamba2_timing_collect")
     return [(buf[i].name.decode(), float(buf[i].ms)) for i in range(n)]
+
+
+# ------------------------------------------------------------------ Mamba-3 SISO forward
+
+
+class Mamba3Batch:
+    """Packed sequences of the Mamba-3 forward: host run lengths and the device cu_seqlens."""
+
+    def __init__(self, run_lengths: Sequence[int], device="cuda"):
+        self.run_lengths = np.ascontiguousarray(run_lengths, dtype=np.int32)
+        n = len(self.run_lengths)
+        cu = np.zeros(n + 1, dtype=np.int32)
+        cu[1:] = np.cumsum(self.run_lengths, dtype=np.int64).astype(np.int32)
+        self.num_rows = int(self.run_lengths.astype(np.int64).sum())
+        self.dev_cu = torch.from_numpy(cu).to(device) if device is not None else None
+        dptr = self.dev_cu.data_ptr() if self.dev_cu is not None else (1 if n > 0 else 0)
+        self.c = Mamba3VarlenC(n, self.num_rows, self.run_lengths.ctypes.data, dptr)
+
+    @property
+    def num_seqs(self) -> int:
+        return len(self.run_lengths)
+
+    def ref(self):
+        return ctypes.byref(self.c)
+
+
+def mamba3_dims(nheads, qk_dim, v_dim, nangles) -> Mamba3Dims:
+    return Mamba3Dims(nheads, qk_dim, v_dim, nangles)
+
+
+def mamba3_workspace_bytes(batch: Mamba3Batch, dims: Mamba3Dims) -> int:
+    return int(LIB.mamba3_siso_forward_workspace_bytes(batch.ref(), ctypes.byref(dims)))
+
+
+def mamba3_siso_forward(out, final_angle, final_ssm, final_k, final_v, q, k, v, adt, dt, trap, q_bias, k_bias,
+                        angles, d, z, batch: Mamba3Batch, dims: Mamba3Dims, workspace: Optional[torch.Tensor] = None,
+                        stream=None):
+    if workspace is None:
+        workspace = torch.empty(max(mamba3_workspace_bytes(batch, dims), 256), dtype=torch.uint8, device=q.device)
+    fa = _ptr(final_angle) if final_angle is not None and final_angle.numel() > 0 else None
+    st = LIB.mamba3_siso_forward(_ptr(out), fa, _ptr(final_ssm), _ptr(final_k), _ptr(final_v), _ptr(q),
+                                 _ptr(k), _ptr(v), _ptr(adt), _ptr(dt), _ptr(trap), _ptr(q_bias), _ptr(k_bias),
+                                 _ptr(angles) if angles is not None and angles.numel() > 0 else None, _ptr(d), _ptr(z),
+                                 batch.ref(), ctypes.byref(dims), _ptr(workspace),
+                                 workspace.numel() * workspace.element_size(), _stream(stream))
+    _lib.check(st, "mamba3_siso_forward")
+    return workspace
 
 
 # ------------------------------------------------------------------ host <-> device helpers

@@ -68,3 +68,13 @@ def test_digest_sees_every_bit():
     assert bench.digest(torch, [s]) != d0
     b = t.to(torch.bfloat16)
     assert bench.digest(torch, [b]) == bench.digest(torch, [b.clone()])
+
+
+def test_mamba3_flop_count():
+    """Per row and head at chunk 64, Q/K width 128, V width 64: q.k over the causal triangle
+    128 * 65, the masked product with v 64 * 65, the state's output term and the chunk state
+    2 * 128 * 64 each: 45,248 flops."""
+    wl = W.mamba3_varlen()
+    T, H = wl.num_rows, wl.nheads
+    assert bench.mamba3_flops(wl) == T * H * (128 * 65 + 64 * 65 + 4 * 128 * 64)
+    assert bench.mamba3_flops(wl) / (T * H) == 45248

@@ -11,7 +11,7 @@ import pytest
 import oracle
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "mamba2.h")
+HEADERS = [os.path.join(ROOT, "include", "mamba2.h"), os.path.join(ROOT, "include", "mamba3.h")]
 
 
 @pytest.fixture(scope="module")
@@ -26,9 +26,11 @@ def ops():
 
 
 def _declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    names = re.findall(r"^[A-Za-z_][\w \*]*?\b(mamba2_\w+)\s*\(", src, flags=re.M)
+    names = []
+    for h in HEADERS:
+        src = open(h).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        names += re.findall(r"^[A-Za-z_][\w \*]*?\b(mamba[23]_\w+)\s*\(", src, flags=re.M)
     return sorted(set(names))
 
 
@@ -228,3 +230,31 @@ def test_padded_runs_agree_with_oracle(ops):
         assert st == st_o, (trial, m)
         if st == 0:
             assert np.array_equal(got, lens_o) and int(side[0]) == left_o
+
+
+def test_mamba3_host_checks(ops):
+    """The Mamba-3 entry's host checks, before any device access: run lengths, unsupported
+    widths, too many rotary pairs; the workspace size is 0 for rejected arguments."""
+    from mamba2_selective_scan_causalconv1d_amd import _lib
+
+    d = ops.mamba3_dims(32, 128, 64, 32)
+    ok = ops.Mamba3Batch([100, 300], device=None)
+    assert ops.mamba3_workspace_bytes(ok, d) > 0
+    fake = ctypes.c_void_p(256)
+    args = [fake] * 16
+    for lens, dims, code in (([100, 0], d, _lib.RUN_LENGTHS), ([5, 5], ops.mamba3_dims(32, 160, 64, 32),
+                                                                _lib.NOT_IMPLEMENTED),
+                             ([5, 5], ops.mamba3_dims(32, 128, 64, 65), _lib.INVALID_ARGUMENT),
+                             ([5, 5], ops.mamba3_dims(32, 128, 72, 32), _lib.NOT_IMPLEMENTED)):
+        b = ops.Mamba3Batch(lens, device=None)
+        if lens == [100, 0]:
+            b.c.num_rows = 100
+        st = ops.LIB.mamba3_siso_forward(*args, b.ref(), ctypes.byref(dims), fake, 1 << 30, None)
+        assert st == code, (lens, st)
+        assert ops.mamba3_workspace_bytes(b, dims) == 0
+    # a too-small workspace, and a sum of run lengths other than num_rows
+    st = ops.LIB.mamba3_siso_forward(*args, ok.ref(), ctypes.byref(d), fake, 16, None)
+    assert st == _lib.WORKSPACE_TOO_SMALL
+    bad = ops.Mamba3Batch([100, 300], device=None)
+    bad.c.num_rows = 401
+    assert ops.LIB.mamba3_siso_forward(*args, bad.ref(), ctypes.byref(d), fake, 1 << 30, None) == _lib.RUN_LENGTHS
