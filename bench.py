@@ -210,6 +210,18 @@ def main():
     e1.record()
     torch.cuda.synchronize()
     ms_per_step = e0.elapsed_time(e1) / args.steps
+
+    # per-kernel durations: the same K steps again, straight after the timed region (same
+    # clock state), with the library's HIP events recorded on the launch stream around every
+    # kernel (they add a few us per launch, hence a pass of its own)
+    ops.timing_enable(64 * max(1, args.steps))
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    recs = ops.timing_collect(64 * max(1, args.steps))
+    ops.timing_enable(0)
+    # every step rewrites the same bits, so the outputs and states left now are the timed
+    # steps' ones too
     assert step_digest() == ref_digest, "timed output differs from the parity run"
 
     # repetitions: each step timed on its own with HIP events on the launch stream, then its
@@ -225,16 +237,6 @@ def main():
     reps = {"n": len(rep_ms), "median_ms": float(np.median(rep_ms)), "min_ms": float(np.min(rep_ms)),
             "max_ms": float(np.max(rep_ms)), "median_tokens_per_s": T / (float(np.median(rep_ms)) * 1e-3),
             "digest": ref_digest, "digests_matched": len(rep_ms) + 1}
-
-    # per-kernel durations: the same K steps again, with the library's HIP events recorded on
-    # the launch stream around every kernel (they add a few us per launch, hence a pass of
-    # their own)
-    ops.timing_enable(64 * max(1, args.steps))
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    recs = ops.timing_collect(64 * max(1, args.steps))
-    ops.timing_enable(0)
 
     per = {}
     for name, ms in recs:
