@@ -303,7 +303,8 @@ mamba2_status mamba2_scan_prefill_snap(void* dst, const void* xbc, const void* d
   const ScanLayout lay = scan_layout(rb, dims, seg_len);
   if (!workspace || workspace_bytes < lay.total) return MAMBA2_WORKSPACE_TOO_SMALL;
   if (((uintptr_t)workspace & 255) != 0) return MAMBA2_INVALID_ARGUMENT;
-  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace};
+  // the snapshots are copies of segment entering states: every one must be stored
+  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace, true};
   hipError_t e = launch_scan_prefill(a, (hipStream_t)stream);
   if (e != hipSuccess) return MAMBA2_HIP_ERROR;
   return from_hip(launch_ssm_snapshots(a, ssm_snaps, snapshot_max_per_seq(rb, snap_every), snap_every,

@@ -115,6 +115,10 @@ __device__ __forceinline__ float wave_sum(float v) {
 //   seg_info  int4  [nseg]     (sequence, first row, rows, index within sequence)
 //   seg_decay f32   [nseg][H]  exp(sum of log-decays over the segment), 0 when that sum is
 //                              below -60 (the carried state is dropped)
+//   seg_start i32   [nseg][H]  MFMA path: the first chunk of the segment's local-state walk,
+//                              with a flag where that walk is left to the next segment's
+//                              output kernel (the state is then not stored)
+//   seg_chunk f32   [nseg][64][H]  MFMA path: log-decay sums of the segment's chunks
 //   seg_state f32   [nseg][H][P][N]  at the index of segment k + 1: the local end state
 //                                    of segment k, then the state entering segment k + 1;
 //                                    at a sequence's first index, a copy of its slot
@@ -122,7 +126,7 @@ __device__ __forceinline__ float wave_sum(float v) {
 struct ScanLayout {
   int64_t nseg;
   int32_t seg_len;
-  size_t off_seq_info, off_seg_info, off_seg_decay, off_seg_state, total;
+  size_t off_seq_info, off_seg_info, off_seg_decay, off_seg_start, off_seg_chunk, off_seg_state, total;
 };
 
 ScanLayout scan_layout(const mamba2_recurrent_batch* rb, const mamba2_dims* d, int32_t seg_len);
@@ -163,6 +167,9 @@ struct ScanArgs {
   mamba2_dims dims;
   ScanLayout lay;
   char* ws;
+  // every segment's entering state must be left in seg_state (read afterwards, e.g. for
+  // snapshots): no local-state walk may be left to the output kernels
+  bool keep_seg_states;
 };
 
 hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st);

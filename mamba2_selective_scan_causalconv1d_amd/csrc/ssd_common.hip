@@ -170,6 +170,10 @@ ScanLayout scan_layout(const mamba2_recurrent_batch* rb, const mamba2_dims* d, i
   off = align256(off + (size_t)nseg * sizeof(int4));
   L.off_seg_decay = off;
   off = align256(off + (size_t)nseg * H * sizeof(float));
+  L.off_seg_start = off;
+  off = align256(off + (size_t)nseg * H * sizeof(int32_t));
+  L.off_seg_chunk = off;
+  off = align256(off + (size_t)nseg * 64 * H * sizeof(float));
   L.off_seg_state = off;
   off = align256(off + (size_t)nseg * H * PN * sizeof(float));
   L.total = off;

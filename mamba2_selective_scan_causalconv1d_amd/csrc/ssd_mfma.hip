@@ -59,6 +59,7 @@ constexpr int kQ = 64;   // chunk rows
 constexpr float kFrameMin = 0x1p-20f;  // smallest state-frame scale before a rescale
 constexpr float kDropSpan = 60.f;      // a chunk decaying by more than e^-60 drops the carried state
 constexpr int kTiles = 10;             // lower-triangular 16 x 16 tiles of a 64 x 64 chunk
+constexpr int kMaxSegChunks = 64;      // chunks per segment at most (segments of <= 4096 rows)
 
 // Per-chunk decay quantities of one head (written by the head's two waves, read by all).
 struct Decay {
@@ -78,7 +79,14 @@ struct SegPtrs {
   const int4* seg_info;
   float* seg_decay;
   float* seg_state;
+  int* seg_start;    // [nseg][H]: first chunk the local-state walk takes | kTailLeft when skipped
+  float* seg_chunk;  // [nseg][kMaxSegChunks][H]: log-decay sums of the segment's chunks
+  int tail_ok;       // the output kernel may compute a dropped predecessor's state itself
 };
+
+// seg_start flag: the segment-state kernel left this segment's local state to the output
+// kernel of the next segment (its index in seg_state is not written).
+constexpr int kTailLeft = 1 << 8;
 
 // ------------------------------------------------------------------ small helpers
 
@@ -407,97 +415,28 @@ __device__ __forceinline__ size_t state_elem(int ph, int t, int nb, int lane) {
 
 // ---------------------------------------------------------------- segment states
 
-// Log-decay sums of head h over the chunks of a segment [r0, r0 + nrows): lane q (< 64)
-// receives the sum of a_t = -A softplus(dt_t + bias) over chunk q.  dt is loaded eight
-// chunks at a time before it is used.
-__device__ __forceinline__ float chunk_log_decays(const bf16_t* dt, int r0, int nrows, int H, int h, float A,
-                                                  float bias, int lane) {
-  const int nch = (nrows + kQ - 1) / kQ;
-  float mine = 0.f;
-  for (int q0 = 0; q0 < nch; q0 += 8) {
-    uint32_t b[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = q0 + i;
-      b[i] = q < nch ? dt_bits(dt, r0 + q * kQ, min(kQ, nrows - q * kQ), H, h, lane) : 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int q = q0 + i;
-      if (q < nch) {
-        const int nr = min(kQ, nrows - q * kQ);
-        const float a = lane < nr ? -A * softplus_f32(bf16_to_f32(b[i]) + bias) : 0.f;
-        const float sum = lane_value(wave_scan_incl(a), 63);
-        if (lane == q) mine = sum;
-      }
-    }
-  }
-  return mine;
-}
-
-// Single-buffered tiles: with two heads per workgroup three workgroups fit a CU (LDS and
-// registers), and each one's copies are covered by the other two's work.
-//
-// The walk starts at the last chunk q0 whose rows all decay by more than e^-60 before the
-// segment's end (none of the chunks before q0 can change the end state in fp32; chunk q0
-// itself is kept), so where the decay is fast only the segment's last chunk or two are
-// walked.  The segment's total log-decay gives its decay factor for the pass (0 below -60).
-__global__ __launch_bounds__(256, 3) void ssd_state_kernel(const bf16_t* __restrict__ xbc,
-                                                          const bf16_t* __restrict__ dt,
-                                                          const float* __restrict__ a_log,
-                                                          const float* __restrict__ dt_bias,
-                                                          SegPtrs sp, int H, int G, int nitems) {
+// Local state of the segment rows [r0, r0 + nrows) of heads h0.. (two waves per head, B
+// and x copied through sB and sX, decays through sD), walked from chunk q0 with a zero
+// entering state: on return S holds the wave's rows of S_loc, frame-corrected, and the
+// tiles and decay slots are free again.
+__device__ __forceinline__ void walk_local_state(f32x4 (&S)[2][8], const bf16_t* xbc, const bf16_t* dt, int r0,
+                                                 int nrows, int q0, int H, int h, float A, float bias,
+                                                 uint32_t ld, uint32_t colB, uint32_t colX, bf16_t* sB,
+                                                 bf16_t (*sX)[kQ * kP], Decay (*sD)[2], const Lofs& lo,
+                                                 const DmaOfs& dof, int w, int lane, int hh, int ph) {
   constexpr int HB = 2;
-  __shared__ __attribute__((aligned(16))) bf16_t sB[kQ * kN];
-  __shared__ __attribute__((aligned(16))) bf16_t sX[HB][kQ * kP];
-  __shared__ __attribute__((aligned(16))) Decay sD[2][HB];
-  __shared__ int sStart[HB];
-
-  const int nhg = H / HB;
-  const int item = work_item(blockIdx.x, nitems);
-  const int seg = item / nhg, h0 = (item % nhg) * HB;
-  const int4 si0 = sp.seg_info[seg];
-  const int4 si = make_int4(uniform(si0.x), uniform(si0.y), uniform(si0.z), uniform(si0.w));
-  if (si.w == uniform(sp.seq_info[si.x].y) - 1) return;  // a sequence's last segment needs no local state
-
-  const int w = uniform((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int hh = w >> 1, ph = w & 1, h = h0 + hh;
-  const int Di = H * kP;
-  const uint32_t ld = (uint32_t)(Di + 2 * G * kN);
-  const int grp = h0 / (H / G);
-  const uint32_t colB[1] = {(uint32_t)(Di + grp * kN)};
-  const uint32_t colX = (uint32_t)(h0 * kP);
-  const float A = __expf(a_log[h]), bias = dt_bias[h];
-  const int nchunks = (si.z + kQ - 1) / kQ;
-  const Lofs lo = lane_offsets(lane, ph);
-  const DmaOfs dof = dma_offsets(lane, w, ld);
-
-  // the segment's chunk decays: E_q = log-decay from the start of chunk q to the segment's end
-  {
-    const float c = chunk_log_decays(dt, si.y, si.z, H, h, A, bias, lane);
-    const float incl = wave_scan_incl(c);
-    const float total = lane_value(incl, 63);
-    const float E = total - incl + c;
-    const uint64_t drop = __ballot(lane >= 1 && lane < nchunks && E < -kDropSpan);
-    if (ph == 0 && lane == 0) {
-      sStart[hh] = drop ? 63 - __builtin_clzll(drop) : 0;
-      sp.seg_decay[(size_t)seg * H + h] = total < -kDropSpan ? 0.f : __expf(total);
-    }
-  }
-  __syncthreads();
-  const int q0 = uniform(min(sStart[0], sStart[1]));
-
-  auto rows_of = [&](int q) { return xbc + (size_t)(si.y + q * kQ) * ld; };
-  auto nr_of = [&](int q) { return min(kQ, si.z - q * kQ); };
-  auto dt_of = [&](int q) { return dt_bits(dt, si.y + q * kQ, nr_of(q), H, h, lane); };
+  const int nchunks = (nrows + kQ - 1) / kQ;
+  const uint32_t col[1] = {colB};
+  auto rows_of = [&](int q) { return xbc + (size_t)(r0 + q * kQ) * ld; };
+  auto nr_of = [&](int q) { return min(kQ, nrows - q * kQ); };
+  auto dt_of = [&](int q) { return dt_bits(dt, r0 + q * kQ, nr_of(q), H, h, lane); };
   auto load = [&](int q) {
     bf16_t* const dst[1] = {sB};
     const int nrb = nr_of(q) * (int)ld * 2;
-    load_bc<HB, 1>(rows_of(q), nrb, 2u * ld, colB, dst, dof, w);
+    load_bc<HB, 1>(rows_of(q), nrb, 2u * ld, col, dst, dof, w);
     load_x<HB>(rows_of(q), nrb, 2u * ld, colX, sX, dof, w);
   };
 
-  f32x4 S[2][8];
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -530,16 +469,134 @@ __global__ __launch_bounds__(256, 3) void ssd_state_kernel(const bf16_t* __restr
       chunk_decay_update(sD[st ^ 1][hh], bf16_to_f32(dtn), A, bias, nr_of(q + 1), lane, ph, lam, lsum);
     dtn = dtn2;
   }
+  const float lam_end = uniformf(sD[(nchunks - 1) & 1][hh].lam_next);
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) S[t][nb] *= lam_end;
+  __syncthreads();  // every wave has read its frame scale: the decay slots are free
+}
+
+// Log-decay sums of every chunk of every segment but a sequence's last, per head: the sum of
+// a_t = -exp(A_log) softplus(dt_t + dt_bias) over the chunk's rows.  One wave per (segment,
+// chunk), lane = head (heads in blocks of 64), so that each load of dt is one contiguous row
+// and the softplus work is spread over the whole chip; cpb workgroups of four waves per
+// segment.
+__global__ __launch_bounds__(256) void chunk_sums_kernel(const bf16_t* __restrict__ dt,
+                                                         const float* __restrict__ a_log,
+                                                         const float* __restrict__ dt_bias, SegPtrs sp, int H,
+                                                         int cpb) {
+  const int seg = blockIdx.x / cpb;
+  const int q = (blockIdx.x % cpb) * 4 + ((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int4 si0 = sp.seg_info[seg];
+  const int4 si = make_int4(uniform(si0.x), uniform(si0.y), uniform(si0.z), uniform(si0.w));
+  if (si.w == uniform(sp.seq_info[si.x].y) - 1 || q * kQ >= si.z) return;  // wave-uniform; no barriers
+  const int nr = min(kQ, si.z - q * kQ);
+  // rows past the chunk's end read as zero and are not summed; lanes past H are unused
+  const Rsrc r = make_rsrc(dt + (size_t)(si.y + q * kQ) * H, (int64_t)nr * H * 2);
+  for (int hb = 0; hb < H; hb += 64) {
+    const int h = hb + lane;
+    const float A = h < H ? __expf(a_log[h]) : 0.f, bias = h < H ? dt_bias[h] : 0.f;
+    uint32_t b[kQ];  // every row's load in flight before the first is used
+#pragma unroll
+    for (int i = 0; i < kQ; ++i) b[i] = __builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)((i * H + h) * 2), 0, 0);
+    float sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < kQ; ++i)
+      if (i < nr) sum += -A * softplus_f32(bf16_to_f32(b[i]) + bias);
+    if (h < H) sp.seg_chunk[((size_t)seg * kMaxSegChunks + q) * H + h] = sum;
+  }
+}
+
+// From the chunk sums of segment sg (nrows rows), head hd, lane = chunk: the segment's total
+// log-decay and the first chunk its local-state walk must take, the last chunk q >= 1 whose
+// rows all decay by more than e^-60 before the segment's end (none of the chunks before it
+// can change the end state in fp32).
+__device__ __forceinline__ int seg_first_chunk(const SegPtrs& sp, int sg, int nrows, int H, int hd, int lane,
+                                               float& total) {
+  const int nch = (nrows + kQ - 1) / kQ;
+  const float c = lane < nch ? sp.seg_chunk[((size_t)sg * kMaxSegChunks + lane) * H + hd] : 0.f;
+  const float incl = wave_scan_incl(c);
+  total = lane_value(incl, 63);
+  const float E = total - incl + c;  // log-decay from the start of chunk `lane` to the segment's end
+  const uint64_t drop = __ballot(lane >= 1 && lane < nch && E < -kDropSpan);
+  return drop ? 63 - __builtin_clzll(drop) : 0;
+}
+
+// Single-buffered tiles: with two heads per workgroup three workgroups fit a CU (LDS and
+// registers), and each one's copies are covered by the other two's work.
+//
+// The walk starts at the earlier of the two heads' first chunks (seg_first_chunk), so
+// where the decay is fast only the segment's last chunk or two are walked.  The segment's
+// total log-decay gives its decay factor for the pass (0 below -60).  When both
+// heads' factors are 0 for this segment and for the next one (or the next is the
+// sequence's last), nothing but the output kernel of the next segment reads this local
+// state: the walk is left to that kernel (seg_start flag kTailLeft), which does it itself
+// from the same chunk with the same arithmetic instead of reading the state back.
+__global__ __launch_bounds__(256, 3) void ssd_state_kernel(const bf16_t* __restrict__ xbc,
+                                                          const bf16_t* __restrict__ dt,
+                                                          const float* __restrict__ a_log,
+                                                          const float* __restrict__ dt_bias,
+                                                          SegPtrs sp, int H, int G, int nitems) {
+  constexpr int HB = 2;
+  __shared__ __attribute__((aligned(16))) bf16_t sB[kQ * kN];
+  __shared__ __attribute__((aligned(16))) bf16_t sX[HB][kQ * kP];
+  __shared__ __attribute__((aligned(16))) Decay sD[2][HB];
+  __shared__ int sStart[HB];
+  __shared__ int sDead[HB];  // this segment's and the next one's factors both 0
+
+  const int nhg = H / HB;
+  const int item = work_item(blockIdx.x, nitems);
+  const int seg = item / nhg, h0 = (item % nhg) * HB;
+  const int4 si0 = sp.seg_info[seg];
+  const int4 si = make_int4(uniform(si0.x), uniform(si0.y), uniform(si0.z), uniform(si0.w));
+  if (si.w == uniform(sp.seq_info[si.x].y) - 1) return;  // a sequence's last segment needs no local state
+
+  const int w = uniform((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int hh = w >> 1, ph = w & 1, h = h0 + hh;
+  const int Di = H * kP;
+  const uint32_t ld = (uint32_t)(Di + 2 * G * kN);
+  const int grp = h0 / (H / G);
+  const uint32_t colB[1] = {(uint32_t)(Di + grp * kN)};
+  const uint32_t colX = (uint32_t)(h0 * kP);
+  const float A = __expf(a_log[h]), bias = dt_bias[h];
+  const Lofs lo = lane_offsets(lane, ph);
+  const DmaOfs dof = dma_offsets(lane, w, ld);
+
+  // first chunk and decay factor per head; the walk left to the next output kernel?
+  {
+    float total;
+    const int q0h = seg_first_chunk(sp, seg, si.z, H, h, lane, total);
+    bool dead = total < -kDropSpan;
+    if (sp.tail_ok && dead && si.w + 2 < uniform(sp.seq_info[si.x].y)) {
+      const int4 sn = sp.seg_info[seg + 1];
+      float tn;
+      (void)seg_first_chunk(sp, seg + 1, uniform(sn.z), H, h, lane, tn);
+      dead = tn < -kDropSpan;
+    }
+    if (ph == 0 && lane == 0) {
+      sStart[hh] = q0h;
+      sDead[hh] = dead;
+      sp.seg_decay[(size_t)seg * H + h] = total < -kDropSpan ? 0.f : __expf(total);
+    }
+  }
+  __syncthreads();
+  const int q0 = uniform(min(sStart[0], sStart[1]));
+  const bool left = sp.tail_ok && sDead[0] && sDead[1];
+  if (threadIdx.x < HB) sp.seg_start[(size_t)seg * H + h0 + threadIdx.x] = q0 | (left ? kTailLeft : 0);
+  if (left) return;  // uniform over the workgroup
+
+  f32x4 S[2][8];
+  walk_local_state(S, xbc, dt, si.y, si.z, q0, H, h, A, bias, ld, colB[0], colX, sB, sX, sD, lo, dof, w, lane, hh,
+                   ph);
 
   // S_loc of this segment, at the index of the next segment of the sequence
-  const float lam_end = uniformf(sD[(nchunks - 1) & 1][hh].lam_next);
   float* out = sp.seg_state + ((size_t)(seg + 1) * H + h) * (size_t)(kP * kN);
   const int lane_st = opaque(lane);
 #pragma unroll
   for (int t = 0; t < 2; ++t)
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb)
-      *reinterpret_cast<f32x4*>(out + state_elem(ph, t, nb, lane_st)) = S[t][nb] * lam_end;
+    for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<f32x4*>(out + state_elem(ph, t, nb, lane_st)) = S[t][nb];
 }
 
 // ---------------------------------------------------------------- outputs
@@ -595,15 +652,22 @@ __global__ __launch_bounds__(256, 2) void ssd_scan_kernel(
 
   // the state entering the segment, frame scale 1: zero for a fresh sequence's first
   // segment; the slot itself for a resumed sequence of one segment (each lane reads here
-  // and writes at the end the same elements); else what the pass left at this segment's
-  // index (for a first segment, the pass's copy of the slot, which the sequence's last
-  // segment overwrites during this launch)
+  // and writes at the end the same elements); the previous segment's local state, walked
+  // here from its first kept chunk, where the segment-state kernel left it to this kernel
+  // (the previous segment then decays by more than e^-60, so that is the whole entering
+  // state); else what the pass left at this segment's index (for a first segment, the
+  // pass's copy of the slot, which the sequence's last segment overwrites during this launch)
   f32x4 S[2][8];
+  const int prev = si.w > 0 ? uniform(sp.seg_start[(size_t)(seg - 1) * H + h0]) : 0;
   if (si.w == 0 && fresh[si.x]) {
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) S[t][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  } else if (prev & kTailLeft) {
+    const int4 sq0 = sp.seg_info[seg - 1];
+    walk_local_state(S, xbc, dt, uniform(sq0.y), uniform(sq0.z), prev & (kTailLeft - 1), H, h, A, bias, ld,
+                     colBC[0], colX, sB, sX, sD, lo, dof, w, lane, hh, ph);
   } else {
     const float* in = (si.w == 0 && last) ? pool + ((size_t)slots[si.x] * H + h) * (size_t)(kP * kN)
                                           : sp.seg_state + ((size_t)seg * H + h) * (size_t)(kP * kN);
@@ -826,10 +890,16 @@ int32_t scan_mfma_segment_length(const mamba2_recurrent_batch* rb, const mamba2_
 
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t st) {
   const SegPtrs sp{(const int2*)(a.ws + a.lay.off_seq_info), (const int4*)(a.ws + a.lay.off_seg_info),
-                   (float*)(a.ws + a.lay.off_seg_decay), (float*)(a.ws + a.lay.off_seg_state)};
+                   (float*)(a.ws + a.lay.off_seg_decay), (float*)(a.ws + a.lay.off_seg_state),
+                   (int*)(a.ws + a.lay.off_seg_start), (float*)(a.ws + a.lay.off_seg_chunk),
+                   a.keep_seg_states ? 0 : 1};
   const mamba2_dims& d = a.dims;
   const int nitems = (int)(a.lay.nseg * (d.nheads / kHeadsPerBlock));
   if (nitems == 0) return hipSuccess;
+  if (a.lay.seg_len > kMaxSegChunks * kQ) return hipErrorInvalidValue;  // the chunk-sum table
+  const int cpb = (a.lay.seg_len + 4 * kQ - 1) / (4 * kQ);  // workgroups of four chunks per segment
+  M2_LAUNCH("chunk_sums", chunk_sums_kernel, dim3((unsigned)(a.lay.nseg * cpb)), dim3(256), 0, st,
+            (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, cpb);
   M2_LAUNCH("ssd_state", ssd_state_kernel, dim3((unsigned)nitems), dim3(256), 0, st, (const bf16_t*)a.xbc,
             (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, d.ngroups, nitems);
   hipError_t e = launch_scan_pass(a, st);
