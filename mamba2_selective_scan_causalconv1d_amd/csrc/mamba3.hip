@@ -42,6 +42,7 @@ constexpr int kC = 64;       // chunk rows
 constexpr int kMaxDK = 128;  // query / key width
 constexpr int kMaxDV = 64;   // value width
 constexpr int kMaxNA = 64;   // rotary pairs
+constexpr int kBlock = 1024;  // threads of the chunk-state and output workgroups (16 waves)
 
 __device__ __forceinline__ float bf(const bf16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
@@ -53,21 +54,39 @@ __device__ __forceinline__ double mod2pi(double x) {
   const double r = x - kTwoPiD * floor(x * (1.0 / kTwoPiD));
   return r < 0.0 ? r + kTwoPiD : (r >= kTwoPiD ? r - kTwoPiD : r);
 }
-// theta dt of one token and pair: tanh in fp32 (relative error ~1e-7), the product in double
-__device__ __forceinline__ double angle_step(const bf16_t* a, float dtv) {
-  return (double)tanhf(bf16_to_f32(*a)) * kPiD * (double)dtv;
+// tanh from the hardware exponential and reciprocal: 1 - 2 / (e^{2|x|} + 1), absolute error
+// ~1e-7 (what an angle needs), with the sign of x
+__device__ __forceinline__ float tanh_fast(float x) {
+  const float t = 1.f - 2.f * __builtin_amdgcn_rcpf(__expf(2.f * fabsf(x)) + 1.f);
+  return copysignf(t, x);
+}
+// Inclusive prefix sum over the 64 lanes of a wave: shifts within 16-lane rows, then the row
+// totals broadcast forward.  All 64 lanes must be active.
+template <int kCtrl, int kRowMask>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, kRowMask, 0xf, false));
+}
+__device__ __forceinline__ float wave_scan(float v) {
+  v = dpp_add<0x111, 0xf>(v);  // row_shr:1
+  v = dpp_add<0x112, 0xf>(v);  // row_shr:2
+  v = dpp_add<0x114, 0xf>(v);  // row_shr:4
+  v = dpp_add<0x118, 0xf>(v);  // row_shr:8
+  v = dpp_add<0x142, 0xa>(v);  // row_bcast:15
+  return dpp_add<0x143, 0xc>(v);  // row_bcast:31
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
-// D += A B over 16 k: a, b the lane's four consecutive k of its A row and B column.
-__device__ __forceinline__ f32x4 mfma16(const float4& a, const float4& b, f32x4 c) {
-  c = mfma4(a.x, b.x, c);
-  c = mfma4(a.y, b.y, c);
-  c = mfma4(a.z, b.z, c);
-  return mfma4(a.w, b.w, c);
+// D += A B over 16 k (a, b: the lane's four consecutive k of its A row and B column) over two
+// accumulators (k = 0, 2 into c0, k = 1, 3 into c1; the caller adds them): two independent
+// chains, so one instruction's latency overlaps the other chain's issue.
+__device__ __forceinline__ void mfma16x2(const float4& a, const float4& b, f32x4& c0, f32x4& c1) {
+  c0 = mfma4(a.x, b.x, c0);
+  c1 = mfma4(a.y, b.y, c1);
+  c0 = mfma4(a.z, b.z, c0);
+  c1 = mfma4(a.w, b.w, c1);
 }
 __device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
 
@@ -178,13 +197,7 @@ __device__ void chunk_rows(const M3Ptrs& P, int c, const int4& ci, int h, RowLds
   const int2 si = P.seq_info[ci.x];
   if (w == 0) {
     // decay prefix, p, scale (the next row may lie in the next chunk of the same sequence)
-    const float a = on ? P.adt[(size_t)r * P.H + h] : 0.f;
-    float cs = a;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const float t = __shfl_up(cs, o, 64);
-      if (lane >= o) cs += t;
-    }
+    const float cs = wave_scan(on ? P.adt[(size_t)r * P.H + h] : 0.f);
     const bool last_chunk = ci.w == si.y - 1;
     const bool has_next = on && (lane + 1 < ci.z || !last_chunk);
     const float dtv = on ? P.dt[(size_t)r * P.H + h] : 0.f;
@@ -200,22 +213,27 @@ __device__ void chunk_rows(const M3Ptrs& P, int c, const int4& ci, int h, RowLds
     L.dp[lane] = dtv * p;
   }
   // rotary angles: the angle entering the chunk (the prefix kernel's), then the running sum
-  // over this chunk's rows
+  // over this chunk's rows (at most 64 terms: fp32, by DPP), reduced mod 2 pi in double;
+  // every load of the wave's pairs issued before the first is used
   const float dtv = on ? P.dt[(size_t)r * P.H + h] : 0.f;
-  for (int a = w; a < P.NA; a += nw) {
-    const double base = (double)P.ang_tot[((size_t)c * P.H + h) * P.NA + a];
-    double v = on ? angle_step(P.angles + (size_t)r * P.NA + a, dtv) : 0.0;
+  constexpr int kItA = kMaxNA / (kBlock / 64);
+  float base_f[kItA];
+  bf16_t ang[kItA];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const double t = __shfl_up(v, o, 64);
-      if (lane >= o) v += t;
-    }
-    const float ph = (float)mod2pi(base + v);
+  for (int it = 0; it < kItA; ++it) {
+    const int a = w + it * nw;
+    base_f[it] = a < P.NA ? P.ang_tot[((size_t)c * P.H + h) * P.NA + a] : 0.f;
+    ang[it] = a < P.NA && on ? P.angles[(size_t)r * P.NA + a] : (bf16_t)0;
+  }
+#pragma unroll
+  for (int it = 0; it < kItA; ++it) {
+    const int a = w + it * nw;
+    if (a >= P.NA) break;
+    const float v = wave_scan(on ? tanh_fast(bf16_to_f32(ang[it])) * (float)kPiD * dtv : 0.f);
+    const float ph = (float)mod2pi((double)base_f[it] + (double)v);
     if constexpr (kCS) {
-      float sn, cs;
-      sincosf(ph, &sn, &cs);
-      L.cosv[lane][a] = cs;
-      L.sinv[lane][a] = sn;
+      L.cosv[lane][a] = __cosf(ph);
+      L.sinv[lane][a] = __sinf(ph);
     } else {
       L.phi[lane][a] = ph;
     }
@@ -224,24 +242,39 @@ __device__ void chunk_rows(const M3Ptrs& P, int c, const int4& ci, int h, RowLds
 
 // dst = rotary(src_i + bias, phi_i) for the chunk's rows (zeros past its end), fp32: row i at
 // dst[i * ld + n], or transposed (kT) at dst[n * ld + i].  One thread per (row, component pair).
+// kBlock threads; each thread's loads are all issued before the first is used.
 template <bool kT, bool kCS>
 __device__ void rotated_rows(const bf16_t* src, const float* bias, const RowLds<kCS>& L, const int4& ci, int DK,
                              int NA, float* dst, int ld) {
-  const int npair = DK / 2;
-  for (int e = threadIdx.x; e < kC * npair; e += blockDim.x) {
+  const int npair = DK / 2, n = kC * npair;
+  constexpr int kIt = kC * (kMaxDK / 2) / kBlock;
+  uint32_t raw[kIt];
+  float2 bs[kIt];
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int e = (int)threadIdx.x + it * kBlock, i = e / npair, a = e - i * npair;
+    const bool on = e < n && i < ci.z;
+    raw[it] = on ? *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + i) * DK + 2 * a) : 0u;
+    bs[it] = on ? *reinterpret_cast<const float2*>(bias + 2 * a) : make_float2(0.f, 0.f);
+  }
+#pragma unroll
+  for (int it = 0; it < kIt; ++it) {
+    const int e = (int)threadIdx.x + it * kBlock;
+    if (e >= n) break;
     const int i = e / npair, a = e - i * npair;
     float x0 = 0.f, x1 = 0.f;
     if (i < ci.z) {
-      const uint32_t two = *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + i) * DK + 2 * a);
-      x0 = bf16_to_f32(two & 0xffffu) + bias[2 * a];
-      x1 = bf16_to_f32(two >> 16) + bias[2 * a + 1];
+      const uint32_t two = raw[it];
+      x0 = bf16_to_f32(two & 0xffffu) + bs[it].x;
+      x1 = bf16_to_f32(two >> 16) + bs[it].y;
       if (a < NA) {
         float cs, sn;
         if constexpr (kCS) {
           cs = L.cosv[i][a];
           sn = L.sinv[i][a];
         } else {
-          sincosf(L.phi[i][a], &sn, &cs);
+          sn = __sinf(L.phi[i][a]);
+          cs = __cosf(L.phi[i][a]);
         }
         const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
         x0 = r0;
@@ -263,12 +296,12 @@ __device__ void rotated_rows(const bf16_t* src, const float* bias, const RowLds<
 constexpr int kLdK = kMaxDK + 4;  // LDS row pitch of query / key / state rows (floats)
 constexpr int kLdT = kC + 4;      // LDS row pitch of transposed tiles (a chunk's rows along a row)
 
-// grid (chunk, head), 512 threads: S_loc = sum_j exp(cs_last - cs_j) scale_j v_j kh_j^T, stored
+// grid (chunk, head), kBlock threads: S_loc = sum_j exp(cs_last - cs_j) scale_j v_j kh_j^T, stored
 // at chunk c + 1 (the sequence's last chunk: in the final-state output, which the pass then
 // completes); the chunk's decay factor; for a sequence's last chunk, its final K, V and angle.
-// S_loc [DV][DK] = (w o V)^T K: 16 x 16 tiles dealt over the eight waves, the chunk's rows as k,
+// S_loc [DV][DK] = (w o V)^T K: 16 x 16 tiles dealt over the waves, the chunk's rows as k,
 // both operands transposed in LDS so that a lane's four k are one 16-byte read.
-__global__ __launch_bounds__(512) void m3_chunk_state_kernel(M3Ptrs P, int nch) {
+__global__ __launch_bounds__(kBlock) void m3_chunk_state_kernel(M3Ptrs P, int nch) {
   __shared__ __attribute__((aligned(16))) float sKt[kMaxDK * kLdT];  // kh^T [n][j]
   __shared__ __attribute__((aligned(16))) float sVt[kMaxDV * kLdT];  // (w v)^T [e][j]
   __shared__ RowLds<false> L;
@@ -281,26 +314,38 @@ __global__ __launch_bounds__(512) void m3_chunk_state_kernel(M3Ptrs P, int nch) 
   __syncthreads();
   rotated_rows<true, false>(P.k, P.k_bias + (size_t)h * P.DK, L, ci, P.DK, P.NA, sKt, kLdT);
   const float cl = L.cs[ci.z - 1];
-  for (int e = threadIdx.x; e < kC * P.DV; e += blockDim.x) {
-    const int j = e / P.DV, f = e - j * P.DV;
-    float val = 0.f;
-    if (j < ci.z) val = bf(P.v + ((size_t)(ci.y + j) * P.H + h) * P.DV + f) * (__expf(cl - L.cs[j]) * L.sc[j]);
-    sVt[f * kLdT + j] = val;
+  {
+    constexpr int kIt = kC * kMaxDV / kBlock;
+    bf16_t vv[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
+      vv[it] = e < kC * P.DV && j < ci.z ? P.v[((size_t)(ci.y + j) * P.H + h) * P.DV + f] : (bf16_t)0;
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
+      if (e >= kC * P.DV) break;
+      sVt[f * kLdT + j] = j < ci.z ? bf16_to_f32(vv[it]) * (__expf(cl - L.cs[j]) * L.sc[j]) : 0.f;
+    }
   }
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int ne = P.DV / 16, nn = P.DK / 16;
   float* dst = last ? P.fin_ssm + ((size_t)ci.x * P.H + h) * (size_t)P.DV * P.DK
                     : P.state + ((size_t)(c + 1) * P.H + h) * (size_t)P.DV * P.DK;
-  const int nkc = (ci.z + 15) / 16;  // 16-row steps holding rows of the chunk (the rest is zero)
+  // all four 16-row steps (rows past the chunk's end are zero in both operands), unrolled so
+  // that every operand read is issued ahead of its products
   for (int t = w; t < ne * nn; t += (int)(blockDim.x >> 6)) {
     const int eb = t / nn, nb = t - eb * nn;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int kc = 0; kc < nkc; ++kc) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc;
+#pragma unroll
+    for (int kc = 0; kc < kC / 16; ++kc) {
       const float4 a4 = lds4(sVt + (eb * 16 + lr) * kLdT + 16 * kc + 4 * lg);
       const float4 b4 = lds4(sKt + (nb * 16 + lr) * kLdT + 16 * kc + 4 * lg);
-      acc = mfma16(a4, b4, acc);
+      mfma16x2(a4, b4, acc, acc1);
     }
+    acc += acc1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[(size_t)(eb * 16 + 4 * lg + r) * P.DK + nb * 16 + lr] = acc[r];
   }
@@ -343,13 +388,17 @@ __global__ __launch_bounds__(256) void m3_pass_kernel(M3Ptrs P, int S) {
 
 // ------------------------------------------------------------------ outputs
 
-// grid (chunk, head), 512 threads (two waves per SIMD at one workgroup per CU).  (1) rotated
+// grid (chunk, head), kBlock threads (four waves per SIMD at one workgroup per CU, which the
+// LDS allows).  (1) rotated
 // queries and keys of the chunk in LDS (rows), the
 // values transposed; (2) G = qh kh^T on the ten lower-triangular 16 x 16 tiles, turned into
 // M (exp(cs_i - cs_j) scale_j below the diagonal, dt_i p_i and d on it, zero above), in LDS;
 // (3) the state entering the chunk over the keys' LDS; (4) Y = exp(cs_i) qh S_in^T + M v on
 // 16 x 16 tiles (rows x value columns), the gate, bf16 stores.
-__global__ __launch_bounds__(512) void m3_chunk_out_kernel(M3Ptrs P, int nch) {
+// NKC: the query / key width in 16-column steps when fixed at compile time (8: width 128),
+// else 0 (the width's steps counted at run time).
+template <int NKC>
+__global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch) {
   __shared__ __attribute__((aligned(16))) float sQ[kC * kLdK];
   __shared__ __attribute__((aligned(16))) float sKS[kC * kLdK];  // keys [j][n], then S_in [e][n]
   __shared__ __attribute__((aligned(16))) float sVt[kMaxDV * kLdT];  // v^T [e][j]
@@ -362,14 +411,25 @@ __global__ __launch_bounds__(512) void m3_chunk_out_kernel(M3Ptrs P, int nch) {
   __syncthreads();
   rotated_rows<false, true>(P.q, P.q_bias + (size_t)h * P.DK, L, ci, P.DK, P.NA, sQ, kLdK);
   rotated_rows<false, true>(P.k, P.k_bias + (size_t)h * P.DK, L, ci, P.DK, P.NA, sKS, kLdK);
-  for (int e = threadIdx.x; e < kC * P.DV; e += blockDim.x) {
-    const int j = e / P.DV, f = e - j * P.DV;
-    sVt[f * kLdT + j] = j < ci.z ? bf(P.v + ((size_t)(ci.y + j) * P.H + h) * P.DV + f) : 0.f;
+  {
+    constexpr int kIt = kC * kMaxDV / kBlock;
+    bf16_t vv[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
+      vv[it] = e < kC * P.DV && j < ci.z ? P.v[((size_t)(ci.y + j) * P.H + h) * P.DV + f] : (bf16_t)0;
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
+      if (e >= kC * P.DV) break;
+      sVt[f * kLdT + j] = bf16_to_f32(vv[it]);
+    }
   }
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const float dh = P.d[h];
-  const int nkc = P.DK / 16;
+  const int nkc = NKC ? NKC : P.DK / 16;
   const int nib = (ci.z + 15) / 16;  // 16-row blocks holding rows of the chunk
   // M on the lower-triangular tiles (ib, jb), jb <= ib; tiles dealt round robin over the waves
   const int nwv = blockDim.x >> 6;
@@ -378,9 +438,12 @@ __global__ __launch_bounds__(512) void m3_chunk_out_kernel(M3Ptrs P, int nch) {
     const int jb = t - ib * (ib + 1) / 2;
     f32x4 g = {0.f, 0.f, 0.f, 0.f};
     if (ib < nib) {
+      f32x4 g1 = g;
+#pragma unroll 8
       for (int kc = 0; kc < nkc; ++kc)
-        g = mfma16(lds4(sQ + (ib * 16 + lr) * kLdK + 16 * kc + 4 * lg), lds4(sKS + (jb * 16 + lr) * kLdK + 16 * kc + 4 * lg),
-                   g);
+        mfma16x2(lds4(sQ + (ib * 16 + lr) * kLdK + 16 * kc + 4 * lg), lds4(sKS + (jb * 16 + lr) * kLdK + 16 * kc + 4 * lg),
+                 g, g1);
+      g += g1;
     }
     const int j = jb * 16 + lr;
 #pragma unroll
@@ -401,33 +464,56 @@ __global__ __launch_bounds__(512) void m3_chunk_out_kernel(M3Ptrs P, int nch) {
   const bool has_in = ci.w > 0;
   if (has_in) {
     const float* sin = P.state + ((size_t)c * P.H + h) * (size_t)P.DV * P.DK;
-    for (int e = threadIdx.x; e < P.DV * (P.DK / 4); e += blockDim.x) {
+    constexpr int kIt = kMaxDV * kMaxDK / 4 / kBlock;
+    const int n4s = P.DV * (P.DK / 4);
+    float4 sv[kIt];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = (int)threadIdx.x + it * kBlock;
+      sv[it] = e < n4s ? reinterpret_cast<const float4*>(sin)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int e = (int)threadIdx.x + it * kBlock;
+      if (e >= n4s) break;
       const int f = e / (P.DK / 4), n4 = e - f * (P.DK / 4);
-      *reinterpret_cast<float4*>(sKS + f * kLdK + 4 * n4) = reinterpret_cast<const float4*>(sin + (size_t)f * P.DK)[n4];
+      *reinterpret_cast<float4*>(sKS + f * kLdK + 4 * n4) = sv[it];
     }
   }
   __syncthreads();
   const int neb = P.DV / 16;
   for (int t = w; t < nib * neb; t += nwv) {
     const int ib = t / neb, eb = t - ib * neb;
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    const int f = eb * 16 + lr;
+    float zf[4];  // the gate's inputs, loaded before the products
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = ib * 16 + 4 * lg + r;
+      zf[r] = i < ci.z ? bf(P.z + ((size_t)(ci.y + i) * P.H + h) * P.DV + f) : 0.f;
+    }
+    f32x4 y = {0.f, 0.f, 0.f, 0.f}, y1 = y;
     if (has_in) {
+#pragma unroll 8
       for (int kc = 0; kc < nkc; ++kc)
-        y = mfma16(lds4(sQ + (ib * 16 + lr) * kLdK + 16 * kc + 4 * lg), lds4(sKS + (eb * 16 + lr) * kLdK + 16 * kc + 4 * lg),
-                   y);
+        mfma16x2(lds4(sQ + (ib * 16 + lr) * kLdK + 16 * kc + 4 * lg), lds4(sKS + (eb * 16 + lr) * kLdK + 16 * kc + 4 * lg),
+                 y, y1);
+      y += y1;
+      y1 = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int r = 0; r < 4; ++r) y[r] *= __expf(L.cs[ib * 16 + 4 * lg + r]);
     }
-    for (int jc = 0; jc <= ib; ++jc)
-      y = mfma16(lds4(sM + (ib * 16 + lr) * kLdT + 16 * jc + 4 * lg), lds4(sVt + (eb * 16 + lr) * kLdT + 16 * jc + 4 * lg), y);
-    const int f = eb * 16 + lr;
+    // all four column steps: M is zero above its diagonal tiles and v past the chunk's end
+#pragma unroll
+    for (int jc = 0; jc < kC / 16; ++jc)
+      mfma16x2(lds4(sM + (ib * 16 + lr) * kLdT + 16 * jc + 4 * lg), lds4(sVt + (eb * 16 + lr) * kLdT + 16 * jc + 4 * lg), y,
+               y1);
+    y += y1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = ib * 16 + 4 * lg + r;
       if (i < ci.z) {
         const size_t o = ((size_t)(ci.y + i) * P.H + h) * P.DV + f;
-        const float zf = bf(P.z + o);
-        P.out[o] = (bf16_t)f32_to_bf16(y[r] * zf * sigmoidf_(zf));
+        P.out[o] = (bf16_t)f32_to_bf16(y[r] * zf[r] * sigmoidf_(zf[r]));
       }
     }
   }
@@ -529,11 +615,15 @@ hipError_t launch_mamba3_forward(const M3Args& a, const M3Layout& lay, char* ws,
     M2_LAUNCH("m3_angle_prefix", m3_angle_prefix_kernel, dim3((unsigned)S, (unsigned)((P.H * P.NA + 255) / 256)),
               dim3(256), 0, st, P, S);
   }
-  M2_LAUNCH("m3_chunk_state", m3_chunk_state_kernel, dim3((unsigned)nch, (unsigned)P.H), dim3(512), 0, st, P, nch);
+  M2_LAUNCH("m3_chunk_state", m3_chunk_state_kernel, dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P, nch);
   const int f4 = P.DV * P.DK / 4;
   M2_LAUNCH("m3_pass", m3_pass_kernel, dim3((unsigned)((f4 + 255) / 256), (unsigned)P.H, (unsigned)(S < 65535 ? S : 65535)),
             dim3(256), 0, st, P, S);
-  M2_LAUNCH("m3_chunk_out", m3_chunk_out_kernel, dim3((unsigned)nch, (unsigned)P.H), dim3(512), 0, st, P, nch);
+  if (P.DK == 128) {
+    M2_LAUNCH("m3_chunk_out", m3_chunk_out_kernel<8>, dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P, nch);
+  } else {
+    M2_LAUNCH("m3_chunk_out", m3_chunk_out_kernel<0>, dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P, nch);
+  }
   return hipSuccess;
 }
 
