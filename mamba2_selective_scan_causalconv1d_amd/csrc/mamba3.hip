@@ -117,9 +117,10 @@ struct M3Ptrs {
 
 // ------------------------------------------------------------------ rotary-angle totals
 
-// grid (chunk), 256 threads: theta = tanh(angles) pi for the chunk's rows (once, for every
-// head) and the heads' dt in LDS; then per (head, pair) the chunk's sum of theta dt, in double,
-// stored reduced into [0, 2 pi).  Heads in blocks of 64.
+// grid (chunk, head block of kAngHeads), 256 threads: theta = tanh(angles) pi for the chunk's
+// rows and the block's dt in LDS; then per (head, pair) the chunk's sum of theta dt, in double,
+// stored reduced into [0, 2 pi).
+constexpr int kAngHeads = 8;
 __global__ __launch_bounds__(256) void m3_angle_totals_kernel(M3Ptrs P, int nch) {
   __shared__ float sTh[kC][kMaxNA + 1];
   __shared__ float sDt[kC][65];
@@ -130,8 +131,9 @@ __global__ __launch_bounds__(256) void m3_angle_totals_kernel(M3Ptrs P, int nch)
     const int j = e / P.NA, a = e - j * P.NA;
     sTh[j][a] = j < ci.z ? tanhf(bf(P.angles + (size_t)(ci.y + j) * P.NA + a)) : 0.f;
   }
-  for (int h0 = 0; h0 < P.H; h0 += 64) {
-    const int nh = min(64, P.H - h0);
+  {
+    const int h0 = blockIdx.y * kAngHeads;
+    const int nh = min(kAngHeads, P.H - h0);
     __syncthreads();
     for (int e = threadIdx.x; e < kC * nh; e += blockDim.x) {
       const int j = e / nh, hh = e - j * nh;
@@ -374,14 +376,29 @@ __global__ __launch_bounds__(256) void m3_pass_kernel(M3Ptrs P, int S) {
   for (int s = blockIdx.z; s < S; s += gridDim.z) {
     const int2 si = P.seq_info[s];
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int k = 0; k < si.y; ++k) {
+    auto at = [&](int k) -> float4* {  // chunk k's local state, where S_in of chunk k + 1 goes
       const int c = si.x + k;
-      const float dec = P.decay[(size_t)c * P.H + h];
-      float4* loc = k + 1 < si.y ? reinterpret_cast<float4*>(P.state + ((size_t)(c + 1) * P.H + h) * (size_t)P.DV * P.DK)
-                                 : reinterpret_cast<float4*>(P.fin_ssm + ((size_t)s * P.H + h) * (size_t)P.DV * P.DK);
-      const float4 l = loc[f];
-      acc = make_float4(fmaf(dec, acc.x, l.x), fmaf(dec, acc.y, l.y), fmaf(dec, acc.z, l.z), fmaf(dec, acc.w, l.w));
-      loc[f] = acc;
+      return k + 1 < si.y ? reinterpret_cast<float4*>(P.state + ((size_t)(c + 1) * P.H + h) * (size_t)P.DV * P.DK)
+                          : reinterpret_cast<float4*>(P.fin_ssm + ((size_t)s * P.H + h) * (size_t)P.DV * P.DK);
+    };
+    // the local states and decays of kBatchM chunks are loaded before the chain runs through them
+    constexpr int kBatchM = 8;
+    for (int k0 = 0; k0 < si.y; k0 += kBatchM) {
+      float4 l[kBatchM];
+      float dec[kBatchM];
+#pragma unroll
+      for (int i = 0; i < kBatchM; ++i) {
+        const int k = k0 + i;
+        dec[i] = k < si.y ? P.decay[(size_t)(si.x + k) * P.H + h] : 0.f;
+        l[i] = k < si.y ? at(k)[f] : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+      for (int i = 0; i < kBatchM; ++i) {
+        if (k0 + i >= si.y) break;
+        acc = make_float4(fmaf(dec[i], acc.x, l[i].x), fmaf(dec[i], acc.y, l[i].y), fmaf(dec[i], acc.z, l[i].z),
+                          fmaf(dec[i], acc.w, l[i].w));
+        at(k0 + i)[f] = acc;
+      }
     }
   }
 }
@@ -611,7 +628,8 @@ hipError_t launch_mamba3_forward(const M3Args& a, const M3Layout& lay, char* ws,
   hipError_t e = launch_segment_tables(a.cu_seqlens, S, kC, (int2*)(ws + lay.off_seq), (int4*)(ws + lay.off_chunk), st);
   if (e != hipSuccess) return e;
   if (P.NA > 0) {
-    M2_LAUNCH("m3_angle_totals", m3_angle_totals_kernel, dim3((unsigned)nch), dim3(256), 0, st, P, nch);
+    M2_LAUNCH("m3_angle_totals", m3_angle_totals_kernel, dim3((unsigned)nch, (unsigned)((P.H + kAngHeads - 1) / kAngHeads)),
+              dim3(256), 0, st, P, nch);
     M2_LAUNCH("m3_angle_prefix", m3_angle_prefix_kernel, dim3((unsigned)S, (unsigned)((P.H * P.NA + 255) / 256)),
               dim3(256), 0, st, P, S);
   }
