@@ -244,31 +244,39 @@ __device__ void chunk_rows(const M3Ptrs& P, int c, const int4& ci, int h, RowLds
 
 // dst = rotary(src_i + bias, phi_i) for the chunk's rows (zeros past its end), fp32: row i at
 // dst[i * ld + n], or transposed (kT) at dst[n * ld + i].  One thread per (row, component pair).
-// kBlock threads; each thread's loads are all issued before the first is used.
-template <bool kT, bool kCS>
-__device__ void rotated_rows(const bf16_t* src, const float* bias, const RowLds<kCS>& L, const int4& ci, int DK,
-                             int NA, float* dst, int ld) {
+// The chunk's rows of a [T, DK] bf16 input and a head's bias, as kBlock threads stage them: each
+// thread holds kRowIt (row, component pair) units, fetched with every load in flight at once.
+constexpr int kRowIt = kC * (kMaxDK / 2) / kBlock;
+struct RowUnits {
+  uint32_t raw[kRowIt];
+  float2 bias[kRowIt];
+};
+__device__ __forceinline__ void fetch_rows(RowUnits& u, const bf16_t* src, const float* bias, const int4& ci, int DK) {
   const int npair = DK / 2, n = kC * npair;
-  constexpr int kIt = kC * (kMaxDK / 2) / kBlock;
-  uint32_t raw[kIt];
-  float2 bs[kIt];
 #pragma unroll
-  for (int it = 0; it < kIt; ++it) {
+  for (int it = 0; it < kRowIt; ++it) {
     const int e = (int)threadIdx.x + it * kBlock, i = e / npair, a = e - i * npair;
     const bool on = e < n && i < ci.z;
-    raw[it] = on ? *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + i) * DK + 2 * a) : 0u;
-    bs[it] = on ? *reinterpret_cast<const float2*>(bias + 2 * a) : make_float2(0.f, 0.f);
+    u.raw[it] = on ? *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + i) * DK + 2 * a) : 0u;
+    u.bias[it] = on ? *reinterpret_cast<const float2*>(bias + 2 * a) : make_float2(0.f, 0.f);
   }
+}
+// dst = rotary(src_i + bias, phi_i) from the fetched units (zeros past the chunk's end), fp32:
+// row i at dst[i * ld + n], or transposed (kT) at dst[n * ld + i].
+template <bool kT, bool kCS>
+__device__ void rotate_rows(const RowUnits& u, const RowLds<kCS>& L, const int4& ci, int DK, int NA, float* dst,
+                            int ld) {
+  const int npair = DK / 2, n = kC * npair;
 #pragma unroll
-  for (int it = 0; it < kIt; ++it) {
+  for (int it = 0; it < kRowIt; ++it) {
     const int e = (int)threadIdx.x + it * kBlock;
     if (e >= n) break;
     const int i = e / npair, a = e - i * npair;
     float x0 = 0.f, x1 = 0.f;
     if (i < ci.z) {
-      const uint32_t two = raw[it];
-      x0 = bf16_to_f32(two & 0xffffu) + bs[it].x;
-      x1 = bf16_to_f32(two >> 16) + bs[it].y;
+      const uint32_t two = u.raw[it];
+      x0 = bf16_to_f32(two & 0xffffu) + u.bias[it].x;
+      x1 = bf16_to_f32(two >> 16) + u.bias[it].y;
       if (a < NA) {
         float cs, sn;
         if constexpr (kCS) {
@@ -292,6 +300,15 @@ __device__ void rotated_rows(const bf16_t* src, const float* bias, const RowLds<
     }
   }
 }
+// The chunk's rows of head h's values (bf16 [T][H][DV]), kRowIt per thread, zero past the end.
+constexpr int kValIt = kC * kMaxDV / kBlock;
+__device__ __forceinline__ void fetch_values(bf16_t (&vv)[kValIt], const M3Ptrs& P, const int4& ci, int h) {
+#pragma unroll
+  for (int it = 0; it < kValIt; ++it) {
+    const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
+    vv[it] = e < kC * P.DV && j < ci.z ? P.v[((size_t)(ci.y + j) * P.H + h) * P.DV + f] : (bf16_t)0;
+  }
+}
 
 // ------------------------------------------------------------------ chunk states
 
@@ -313,17 +330,16 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_state_kernel(M3Ptrs P, int nc
   const int2 si = P.seq_info[ci.x];
   const bool last = ci.w == si.y - 1;
   chunk_rows(P, c, ci, h, L);
+  // the chunk's keys and values, fetched together (the row scalars' own loads go first)
+  RowUnits ku;
+  fetch_rows(ku, P.k, P.k_bias + (size_t)h * P.DK, ci, P.DK);
+  bf16_t vv[kValIt];
+  fetch_values(vv, P, ci, h);
   __syncthreads();
-  rotated_rows<true, false>(P.k, P.k_bias + (size_t)h * P.DK, L, ci, P.DK, P.NA, sKt, kLdT);
+  rotate_rows<true, false>(ku, L, ci, P.DK, P.NA, sKt, kLdT);
   const float cl = L.cs[ci.z - 1];
   {
-    constexpr int kIt = kC * kMaxDV / kBlock;
-    bf16_t vv[kIt];
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
-      vv[it] = e < kC * P.DV && j < ci.z ? P.v[((size_t)(ci.y + j) * P.H + h) * P.DV + f] : (bf16_t)0;
-    }
+    constexpr int kIt = kValIt;
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
@@ -424,18 +440,31 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= nch) return;
   const int4 ci = P.chunk_info[c];
+  // the chunk's queries, keys and values are fetched before the row scalars are computed
+  RowUnits qu, ku;
+  fetch_rows(qu, P.q, P.q_bias + (size_t)h * P.DK, ci, P.DK);
+  fetch_rows(ku, P.k, P.k_bias + (size_t)h * P.DK, ci, P.DK);
+  bf16_t vv[kValIt];
+  fetch_values(vv, P, ci, h);
+  // and the state entering the chunk (written into the keys' LDS once the keys are done)
+  const bool has_in = ci.w > 0;
+  constexpr int kStIt = kMaxDV * kMaxDK / 4 / kBlock;
+  const int n4s = P.DV * (P.DK / 4);
+  float4 sv[kStIt];
+  {
+    const float4* sin = reinterpret_cast<const float4*>(P.state + ((size_t)c * P.H + h) * (size_t)P.DV * P.DK);
+#pragma unroll
+    for (int it = 0; it < kStIt; ++it) {
+      const int e = (int)threadIdx.x + it * kBlock;
+      sv[it] = has_in && e < n4s ? sin[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  }
   chunk_rows(P, c, ci, h, L);
   __syncthreads();
-  rotated_rows<false, true>(P.q, P.q_bias + (size_t)h * P.DK, L, ci, P.DK, P.NA, sQ, kLdK);
-  rotated_rows<false, true>(P.k, P.k_bias + (size_t)h * P.DK, L, ci, P.DK, P.NA, sKS, kLdK);
+  rotate_rows<false, true>(qu, L, ci, P.DK, P.NA, sQ, kLdK);
+  rotate_rows<false, true>(ku, L, ci, P.DK, P.NA, sKS, kLdK);
   {
-    constexpr int kIt = kC * kMaxDV / kBlock;
-    bf16_t vv[kIt];
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
-      vv[it] = e < kC * P.DV && j < ci.z ? P.v[((size_t)(ci.y + j) * P.H + h) * P.DV + f] : (bf16_t)0;
-    }
+    constexpr int kIt = kValIt;
 #pragma unroll
     for (int it = 0; it < kIt; ++it) {
       const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
@@ -478,19 +507,9 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
     if ((j >> 4) > (i >> 4)) sM[i * kLdT + j] = 0.f;
   }
   __syncthreads();  // M complete; the keys are no longer read
-  const bool has_in = ci.w > 0;
   if (has_in) {
-    const float* sin = P.state + ((size_t)c * P.H + h) * (size_t)P.DV * P.DK;
-    constexpr int kIt = kMaxDV * kMaxDK / 4 / kBlock;
-    const int n4s = P.DV * (P.DK / 4);
-    float4 sv[kIt];
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int e = (int)threadIdx.x + it * kBlock;
-      sv[it] = e < n4s ? reinterpret_cast<const float4*>(sin)[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-#pragma unroll
-    for (int it = 0; it < kIt; ++it) {
+    for (int it = 0; it < kStIt; ++it) {
       const int e = (int)threadIdx.x + it * kBlock;
       if (e >= n4s) break;
       const int f = e / (P.DK / 4), n4 = e - f * (P.DK / 4);
