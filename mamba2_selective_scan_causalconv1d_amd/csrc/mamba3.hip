@@ -18,17 +18,15 @@
 //   M_ij = (qh_i . kh_j) exp(cs_i - cs_j) scale_j (j < i),  M_ii = (qh_i . kh_i) dt_i p_i + d
 //   (the diagonal folds the correction: scale_i - sg_i = dt_i p_i, and the skip d),
 //   S_loc = sum_j exp(cs_last - cs_j) scale_j v_j kh_j^T,  S_in(next) = exp(cs_last) S_in + S_loc.
-// Launches: chunk tables; per (chunk, head) the chunk's rotary-angle totals; per (chunk, head)
-// the chunk state (and a sequence's finals); the state pass per (sequence, head); per (chunk,
-// head) the outputs.  The contractions (q.k over a chunk, the state's output term, M v and the
-// chunk state) run on the fp32 matrix instruction v_mfma_f32_16x16x4f32 with operands staged in
-// LDS: the operator's queries and keys are fp32 values after the bias and the rotation, and
-// fp32 keeps every contraction well inside the output and state bars.  Lane layout (checked on
-// the GPU): lane l supplies A[l % 16][l / 16] and B[l / 16][l % 16]; result register r of lane l
-// is D[4 (l / 16) + r][l % 16].  Each lane reads four consecutive k of its row in one 16-byte
-// LDS read and issues four instructions, so instruction m covers k = 16 c + 4 (l / 16) + m: the
-// same order on both operands, hence the same sum.
-// The rotary angles are summed in double (their running sum covers whole sequences).
+// Launches: chunk tables; per (chunk, head block) the chunk's rotary-angle totals and per
+// (sequence, head) their running sums; per (chunk, head) the chunk state (and a sequence's
+// finals); the state pass per (sequence, head); per (chunk, head) the outputs.  The
+// contractions (q.k over a chunk, the state's output term, M v and the chunk state) take fp32
+// operands (the queries and keys after the bias and the rotation, M, the states, w v): each is
+// split into bf16 hi and lo halves in LDS and multiplied as hi.hi + hi.lo + lo.hi on
+// v_mfma_f32_16x16x32_bf16 (~2^-16 relative, well inside the output and state bars; v, exact
+// in bf16, takes M's two halves directly).  The rotary angles entering each chunk are summed in
+// double (their running sum covers whole sequences); within a chunk (at most 64 terms) in fp32.
 #include <initializer_list>
 
 #include "common.h"
@@ -76,19 +74,27 @@ __device__ __forceinline__ float wave_scan(float v) {
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+// The bf16 form of an fp32 product: each fp32 operand split into a bf16 hi and lo half
+// (x = hi + lo to ~2^-17), the product taken as hi.hi + hi.lo + lo.hi on v_mfma_f32_16x16x32_bf16
+// (the dropped lo.lo term is ~2^-16 of it): three instructions of ~16 cycles for 8192
+// multiply-adds, against eight fp32 16x16x4 ones of ~47.  Operand layout: lane l supplies row
+// (A) or column (B) l % 16 and eight consecutive k, 8 (l / 16) .. + 7, of a 32-wide k step; the
+// result layout is the fp32 instruction's (register r of lane l: D[4 (l / 16) + r][l % 16]).
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f32x4 mfma_bf(const u32x4& a, const u32x4& b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0,
+                                                  0);
 }
-// D += A B over 16 k (a, b: the lane's four consecutive k of its A row and B column) over two
-// accumulators (k = 0, 2 into c0, k = 1, 3 into c1; the caller adds them): two independent
-// chains, so one instruction's latency overlaps the other chain's issue.
-__device__ __forceinline__ void mfma16x2(const float4& a, const float4& b, f32x4& c0, f32x4& c1) {
-  c0 = mfma4(a.x, b.x, c0);
-  c1 = mfma4(a.y, b.y, c1);
-  c0 = mfma4(a.z, b.z, c0);
-  c1 = mfma4(a.w, b.w, c1);
+__device__ __forceinline__ f32x4 mfma3(const u32x4& ah, const u32x4& al, const u32x4& bh, const u32x4& bl, f32x4 c) {
+  c = mfma_bf(ah, bh, c);
+  c = mfma_bf(ah, bl, c);
+  return mfma_bf(al, bh, c);
 }
-__device__ __forceinline__ float4 lds4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ u32x4 lds16(const bf16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
+// hi and lo halves of x, each rounded to nearest even
+__device__ __forceinline__ uint32_t bf_hi(float x) { return f32_to_bf16(x); }
+__device__ __forceinline__ uint32_t bf_lo(float x, uint32_t hi) { return f32_to_bf16(x - bf16_to_f32(hi)); }
 
 struct M3Ptrs {
   const bf16_t* q;
@@ -244,6 +250,7 @@ __device__ void chunk_rows(const M3Ptrs& P, int c, const int4& ci, int h, RowLds
 
 // dst = rotary(src_i + bias, phi_i) for the chunk's rows (zeros past its end), fp32: row i at
 // dst[i * ld + n], or transposed (kT) at dst[n * ld + i].  One thread per (row, component pair).
+__device__ __forceinline__ int pad32(int n) { return (n + 31) & ~31; }
 // The chunk's rows of a [T, DK] bf16 input and a head's bias, as kBlock threads stage them: each
 // thread holds kRowIt (row, component pair) units, fetched with every load in flight at once.
 constexpr int kRowIt = kC * (kMaxDK / 2) / kBlock;
@@ -251,78 +258,132 @@ struct RowUnits {
   uint32_t raw[kRowIt];
   float2 bias[kRowIt];
 };
-__device__ __forceinline__ void fetch_rows(RowUnits& u, const bf16_t* src, const float* bias, const int4& ci, int DK) {
-  const int npair = DK / 2, n = kC * npair;
+// np: component pairs per row of the staging (DK / 2, or more for zero padding); unit e is
+// row e / np, pair e % np.
+__device__ __forceinline__ void fetch_rows(RowUnits& u, const bf16_t* src, const float* bias, const int4& ci, int DK,
+                                           int np) {
+  const int npair = DK / 2, n = kC * np;
 #pragma unroll
   for (int it = 0; it < kRowIt; ++it) {
-    const int e = (int)threadIdx.x + it * kBlock, i = e / npair, a = e - i * npair;
-    const bool on = e < n && i < ci.z;
+    const int e = (int)threadIdx.x + it * kBlock, i = e / np, a = e - i * np;
+    const bool on = e < n && i < ci.z && a < npair;
     u.raw[it] = on ? *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + i) * DK + 2 * a) : 0u;
     u.bias[it] = on ? *reinterpret_cast<const float2*>(bias + 2 * a) : make_float2(0.f, 0.f);
   }
 }
-// dst = rotary(src_i + bias, phi_i) from the fetched units (zeros past the chunk's end), fp32:
-// row i at dst[i * ld + n], or transposed (kT) at dst[n * ld + i].
-template <bool kT, bool kCS>
-__device__ void rotate_rows(const RowUnits& u, const RowLds<kCS>& L, const int4& ci, int DK, int NA, float* dst,
-                            int ld) {
-  const int npair = DK / 2, n = kC * npair;
+// rotary(src_i + bias, phi_i) from the fetched units, as bf16 hi and lo planes [i * ld + n]
+// (zeros past the chunk's end and, along the width, up to the next multiple of 32).
+__device__ void rotate_rows(const RowUnits& u, const RowLds<true>& L, const int4& ci, int DK, int NA, bf16_t* dh,
+                            bf16_t* dl, int ld) {
+  const int npair = DK / 2, np = pad32(DK) / 2, nfill = kC * np;  // np as in the fetch
 #pragma unroll
   for (int it = 0; it < kRowIt; ++it) {
     const int e = (int)threadIdx.x + it * kBlock;
-    if (e >= n) break;
-    const int i = e / npair, a = e - i * npair;
+    if (e >= nfill) break;
+    const int i = e / np, a = e - i * np;
     float x0 = 0.f, x1 = 0.f;
-    if (i < ci.z) {
+    if (i < ci.z && a < npair) {
       const uint32_t two = u.raw[it];
       x0 = bf16_to_f32(two & 0xffffu) + u.bias[it].x;
       x1 = bf16_to_f32(two >> 16) + u.bias[it].y;
       if (a < NA) {
-        float cs, sn;
-        if constexpr (kCS) {
-          cs = L.cosv[i][a];
-          sn = L.sinv[i][a];
-        } else {
-          sn = __sinf(L.phi[i][a]);
-          cs = __cosf(L.phi[i][a]);
-        }
+        const float cs = L.cosv[i][a], sn = L.sinv[i][a];
         const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
         x0 = r0;
         x1 = r1;
       }
     }
-    if (kT) {
-      dst[(2 * a) * ld + i] = x0;
-      dst[(2 * a + 1) * ld + i] = x1;
-    } else {
-      dst[i * ld + 2 * a] = x0;
-      dst[i * ld + 2 * a + 1] = x1;
+    const uint32_t h0 = bf_hi(x0), h1 = bf_hi(x1);
+    *reinterpret_cast<uint32_t*>(dh + i * ld + 2 * a) = h0 | (h1 << 16);
+    *reinterpret_cast<uint32_t*>(dl + i * ld + 2 * a) = bf_lo(x0, h0) | (bf_lo(x1, h1) << 16);
+  }
+}
+// Transposed staging in row pairs: unit e is rows 2 (e / npair) and + 1, component pair
+// e % npair, so that each plane takes one 4-byte store per unit and column.  u.raw[2 it + r]
+// holds row 2 ip + r of unit it; u.bias[it] the pair's bias.
+__device__ __forceinline__ void fetch_rows_t(RowUnits& u, const bf16_t* src, const float* bias, const int4& ci,
+                                             int DK) {
+  const int npair = DK / 2, n = (kC / 2) * npair;
+#pragma unroll
+  for (int it = 0; it < kRowIt / 2; ++it) {
+    const int e = (int)threadIdx.x + it * kBlock, ip = e / npair, a = e - ip * npair;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = 2 * ip + r;
+      u.raw[2 * it + r] = e < n && i < ci.z ? *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + i) * DK + 2 * a) : 0u;
+    }
+    u.bias[it] = e < n ? *reinterpret_cast<const float2*>(bias + 2 * a) : make_float2(0.f, 0.f);
+  }
+}
+// kh^T as hi and lo planes [n][j] (zeros past the chunk's end) from fetch_rows_t's units; fin
+// (may be null): the fp32 values of row il.
+__device__ void rotate_rows_t(const RowUnits& u, const RowLds<false>& L, const int4& ci, int DK, int NA, bf16_t* dh,
+                              bf16_t* dl, int ld, float* fin, int il) {
+  const int npair = DK / 2, n = (kC / 2) * npair;
+#pragma unroll
+  for (int it = 0; it < kRowIt / 2; ++it) {
+    const int e = (int)threadIdx.x + it * kBlock;
+    if (e >= n) break;
+    const int ip = e / npair, a = e - ip * npair;
+    uint32_t hp[2] = {0u, 0u}, lp[2] = {0u, 0u};  // planes of components 2a, 2a + 1: rows 2 ip, 2 ip + 1
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = 2 * ip + r;
+      float x0 = 0.f, x1 = 0.f;
+      if (i < ci.z) {
+        const uint32_t two = u.raw[2 * it + r];
+        x0 = bf16_to_f32(two & 0xffffu) + u.bias[it].x;
+        x1 = bf16_to_f32(two >> 16) + u.bias[it].y;
+        if (a < NA) {
+          const float sn = __sinf(L.phi[i][a]), cs = __cosf(L.phi[i][a]);
+          const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
+          x0 = r0;
+          x1 = r1;
+        }
+        if (fin && i == il) {
+          fin[2 * a] = x0;
+          fin[2 * a + 1] = x1;
+        }
+      }
+      const uint32_t h0 = bf_hi(x0), h1 = bf_hi(x1);
+      hp[0] |= h0 << (16 * r);
+      hp[1] |= h1 << (16 * r);
+      lp[0] |= bf_lo(x0, h0) << (16 * r);
+      lp[1] |= bf_lo(x1, h1) << (16 * r);
+    }
+    *reinterpret_cast<uint32_t*>(dh + (2 * a) * ld + 2 * ip) = hp[0];
+    *reinterpret_cast<uint32_t*>(dh + (2 * a + 1) * ld + 2 * ip) = hp[1];
+    *reinterpret_cast<uint32_t*>(dl + (2 * a) * ld + 2 * ip) = lp[0];
+    *reinterpret_cast<uint32_t*>(dl + (2 * a + 1) * ld + 2 * ip) = lp[1];
+  }
+}
+// The chunk's rows of head h's values in row pairs: unit e is rows 2 (e / DV) and + 1, column
+// e % DV (vv[2 it + r]: row 2 jp + r), zero past the chunk's end.
+constexpr int kValIt = kC * kMaxDV / kBlock;
+__device__ __forceinline__ void fetch_values_t(bf16_t (&vv)[kValIt], const M3Ptrs& P, const int4& ci, int h) {
+#pragma unroll
+  for (int it = 0; it < kValIt / 2; ++it) {
+    const int e = (int)threadIdx.x + it * kBlock, jp = e / P.DV, f = e - jp * P.DV;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int j = 2 * jp + r;
+      vv[2 * it + r] = e < (kC / 2) * P.DV && j < ci.z ? P.v[((size_t)(ci.y + j) * P.H + h) * P.DV + f] : (bf16_t)0;
     }
   }
 }
-// The chunk's rows of head h's values (bf16 [T][H][DV]), kRowIt per thread, zero past the end.
-constexpr int kValIt = kC * kMaxDV / kBlock;
-__device__ __forceinline__ void fetch_values(bf16_t (&vv)[kValIt], const M3Ptrs& P, const int4& ci, int h) {
-#pragma unroll
-  for (int it = 0; it < kValIt; ++it) {
-    const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
-    vv[it] = e < kC * P.DV && j < ci.z ? P.v[((size_t)(ci.y + j) * P.H + h) * P.DV + f] : (bf16_t)0;
-  }
-}
-
 // ------------------------------------------------------------------ chunk states
 
-constexpr int kLdK = kMaxDK + 4;  // LDS row pitch of query / key / state rows (floats)
-constexpr int kLdT = kC + 4;      // LDS row pitch of transposed tiles (a chunk's rows along a row)
+constexpr int kLdB = kMaxDK + 8;  // LDS row pitch of query / key / state rows (bf16 elements)
+constexpr int kLdT = kC + 8;      // LDS row pitch of transposed tiles (a chunk's rows along a row)
 
 // grid (chunk, head), kBlock threads: S_loc = sum_j exp(cs_last - cs_j) scale_j v_j kh_j^T, stored
 // at chunk c + 1 (the sequence's last chunk: in the final-state output, which the pass then
 // completes); the chunk's decay factor; for a sequence's last chunk, its final K, V and angle.
-// S_loc [DV][DK] = (w o V)^T K: 16 x 16 tiles dealt over the waves, the chunk's rows as k,
-// both operands transposed in LDS so that a lane's four k are one 16-byte read.
+// S_loc [DV][DK] = (w o V)^T K on 16 x 16 tiles dealt over the waves, the chunk's rows as k
+// (two 32-row steps), both operands transposed in LDS as bf16 hi / lo planes.
 __global__ __launch_bounds__(kBlock) void m3_chunk_state_kernel(M3Ptrs P, int nch) {
-  __shared__ __attribute__((aligned(16))) float sKt[kMaxDK * kLdT];  // kh^T [n][j]
-  __shared__ __attribute__((aligned(16))) float sVt[kMaxDV * kLdT];  // (w v)^T [e][j]
+  __shared__ __attribute__((aligned(16))) bf16_t sKt[2][kMaxDK * kLdT];  // kh^T [n][j], hi and lo
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[2][kMaxDV * kLdT];  // (w v)^T [e][j], hi and lo
   __shared__ RowLds<false> L;
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= nch) return;
@@ -332,46 +393,49 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_state_kernel(M3Ptrs P, int nc
   chunk_rows(P, c, ci, h, L);
   // the chunk's keys and values, fetched together (the row scalars' own loads go first)
   RowUnits ku;
-  fetch_rows(ku, P.k, P.k_bias + (size_t)h * P.DK, ci, P.DK);
+  fetch_rows_t(ku, P.k, P.k_bias + (size_t)h * P.DK, ci, P.DK);
   bf16_t vv[kValIt];
-  fetch_values(vv, P, ci, h);
+  fetch_values_t(vv, P, ci, h);
   __syncthreads();
-  rotate_rows<true, false>(ku, L, ci, P.DK, P.NA, sKt, kLdT);
-  const float cl = L.cs[ci.z - 1];
-  {
-    constexpr int kIt = kValIt;
+  const int il = ci.z - 1;
+  rotate_rows_t(ku, L, ci, P.DK, P.NA, sKt[0], sKt[1], kLdT, last ? P.fin_k + ((size_t)ci.x * P.H + h) * P.DK : nullptr,
+                il);
+  const float cl = L.cs[il];
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
-      if (e >= kC * P.DV) break;
-      sVt[f * kLdT + j] = j < ci.z ? bf16_to_f32(vv[it]) * (__expf(cl - L.cs[j]) * L.sc[j]) : 0.f;
+  for (int it = 0; it < kValIt / 2; ++it) {
+    const int e = (int)threadIdx.x + it * kBlock, jp = e / P.DV, f = e - jp * P.DV;
+    if (e >= (kC / 2) * P.DV) break;
+    uint32_t hp = 0u, lp = 0u;
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int j = 2 * jp + r;
+      const float val = j < ci.z ? bf16_to_f32(vv[2 * it + r]) * (__expf(cl - L.cs[j]) * L.sc[j]) : 0.f;
+      const uint32_t hi = bf_hi(val);
+      hp |= hi << (16 * r);
+      lp |= bf_lo(val, hi) << (16 * r);
     }
+    *reinterpret_cast<uint32_t*>(sVt[0] + f * kLdT + 2 * jp) = hp;
+    *reinterpret_cast<uint32_t*>(sVt[1] + f * kLdT + 2 * jp) = lp;
   }
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const int ne = P.DV / 16, nn = P.DK / 16;
   float* dst = last ? P.fin_ssm + ((size_t)ci.x * P.H + h) * (size_t)P.DV * P.DK
                     : P.state + ((size_t)(c + 1) * P.H + h) * (size_t)P.DV * P.DK;
-  // all four 16-row steps (rows past the chunk's end are zero in both operands), unrolled so
-  // that every operand read is issued ahead of its products
+  // both 32-row steps (rows past the chunk's end are zero in both operands)
   for (int t = w; t < ne * nn; t += (int)(blockDim.x >> 6)) {
     const int eb = t / nn, nb = t - eb * nn;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc1 = acc;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kc = 0; kc < kC / 16; ++kc) {
-      const float4 a4 = lds4(sVt + (eb * 16 + lr) * kLdT + 16 * kc + 4 * lg);
-      const float4 b4 = lds4(sKt + (nb * 16 + lr) * kLdT + 16 * kc + 4 * lg);
-      mfma16x2(a4, b4, acc, acc1);
+    for (int ks = 0; ks < kC / 32; ++ks) {
+      const int ao = (eb * 16 + lr) * kLdT + 32 * ks + 8 * lg, bo = (nb * 16 + lr) * kLdT + 32 * ks + 8 * lg;
+      acc = mfma3(lds16(sVt[0] + ao), lds16(sVt[1] + ao), lds16(sKt[0] + bo), lds16(sKt[1] + bo), acc);
     }
-    acc += acc1;
 #pragma unroll
     for (int r = 0; r < 4; ++r) dst[(size_t)(eb * 16 + 4 * lg + r) * P.DK + nb * 16 + lr] = acc[r];
   }
   if (threadIdx.x == 0) P.decay[(size_t)c * P.H + h] = __expf(cl);
   if (last) {
-    const int il = ci.z - 1;
-    for (int n = threadIdx.x; n < P.DK; n += blockDim.x)
-      P.fin_k[((size_t)ci.x * P.H + h) * P.DK + n] = sKt[n * kLdT + il];
     for (int f = threadIdx.x; f < P.DV; f += blockDim.x)
       P.fin_v[((size_t)ci.x * P.H + h) * P.DV + f] = P.v[((size_t)(ci.y + il) * P.H + h) * P.DV + f];
     for (int a2 = threadIdx.x; a2 < P.NA; a2 += blockDim.x)
@@ -422,30 +486,31 @@ __global__ __launch_bounds__(256) void m3_pass_kernel(M3Ptrs P, int S) {
 // ------------------------------------------------------------------ outputs
 
 // grid (chunk, head), kBlock threads (four waves per SIMD at one workgroup per CU, which the
-// LDS allows).  (1) rotated
-// queries and keys of the chunk in LDS (rows), the
-// values transposed; (2) G = qh kh^T on the ten lower-triangular 16 x 16 tiles, turned into
-// M (exp(cs_i - cs_j) scale_j below the diagonal, dt_i p_i and d on it, zero above), in LDS;
-// (3) the state entering the chunk over the keys' LDS; (4) Y = exp(cs_i) qh S_in^T + M v on
-// 16 x 16 tiles (rows x value columns), the gate, bf16 stores.
-// NKC: the query / key width in 16-column steps when fixed at compile time (8: width 128),
-// else 0 (the width's steps counted at run time).
-template <int NKC>
+// LDS allows).  (1) rotated queries and keys of the chunk in LDS (rows, bf16 hi / lo planes,
+// zero-padded to a multiple of 32 columns), the values transposed (bf16, exact); (2) G = qh kh^T
+// on the ten lower-triangular 16 x 16 tiles, turned into M (exp(cs_i - cs_j) scale_j below the
+// diagonal, dt_i p_i and d on it, zero above), in LDS as hi / lo planes; (3) the state entering
+// the chunk over the keys' LDS, as hi / lo planes; (4) Y = exp(cs_i) qh S_in^T + M v on 16 x 16
+// tiles (rows x value columns), the gate, bf16 stores.
+// NKS: the query / key width in 32-column steps when fixed at compile time (4: width 128),
+// else 0 (counted at run time).
+template <int NKS>
 __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch) {
-  __shared__ __attribute__((aligned(16))) float sQ[kC * kLdK];
-  __shared__ __attribute__((aligned(16))) float sKS[kC * kLdK];  // keys [j][n], then S_in [e][n]
-  __shared__ __attribute__((aligned(16))) float sVt[kMaxDV * kLdT];  // v^T [e][j]
-  __shared__ __attribute__((aligned(16))) float sM[kC * kLdT];
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][kC * kLdB];     // qh [i][n], hi and lo
+  __shared__ __attribute__((aligned(16))) bf16_t sKS[2][kC * kLdB];    // kh [j][n], then S_in [e][n]
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[kMaxDV * kLdT];   // v^T [e][j]
+  __shared__ __attribute__((aligned(16))) bf16_t sM[2][kC * kLdT];     // M [i][j], hi and lo
   __shared__ RowLds<true> L;
   const int c = blockIdx.x, h = blockIdx.y;
   if (c >= nch) return;
   const int4 ci = P.chunk_info[c];
+  const int npad = pad32(P.DK) / 2;  // component pairs per staged row, zero padding included
   // the chunk's queries, keys and values are fetched before the row scalars are computed
   RowUnits qu, ku;
-  fetch_rows(qu, P.q, P.q_bias + (size_t)h * P.DK, ci, P.DK);
-  fetch_rows(ku, P.k, P.k_bias + (size_t)h * P.DK, ci, P.DK);
+  fetch_rows(qu, P.q, P.q_bias + (size_t)h * P.DK, ci, P.DK, npad);
+  fetch_rows(ku, P.k, P.k_bias + (size_t)h * P.DK, ci, P.DK, npad);
   bf16_t vv[kValIt];
-  fetch_values(vv, P, ci, h);
+  fetch_values_t(vv, P, ci, h);
   // and the state entering the chunk (written into the keys' LDS once the keys are done)
   const bool has_in = ci.w > 0;
   constexpr int kStIt = kMaxDV * kMaxDK / 4 / kBlock;
@@ -461,21 +526,18 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
   }
   chunk_rows(P, c, ci, h, L);
   __syncthreads();
-  rotate_rows<false, true>(qu, L, ci, P.DK, P.NA, sQ, kLdK);
-  rotate_rows<false, true>(ku, L, ci, P.DK, P.NA, sKS, kLdK);
-  {
-    constexpr int kIt = kValIt;
+  rotate_rows(qu, L, ci, P.DK, P.NA, sQ[0], sQ[1], kLdB);
+  rotate_rows(ku, L, ci, P.DK, P.NA, sKS[0], sKS[1], kLdB);
 #pragma unroll
-    for (int it = 0; it < kIt; ++it) {
-      const int e = (int)threadIdx.x + it * kBlock, j = e / P.DV, f = e - j * P.DV;
-      if (e >= kC * P.DV) break;
-      sVt[f * kLdT + j] = bf16_to_f32(vv[it]);
-    }
+  for (int it = 0; it < kValIt / 2; ++it) {
+    const int e = (int)threadIdx.x + it * kBlock, jp = e / P.DV, f = e - jp * P.DV;
+    if (e >= (kC / 2) * P.DV) break;
+    *reinterpret_cast<uint32_t*>(sVt + f * kLdT + 2 * jp) = (uint32_t)vv[2 * it] | ((uint32_t)vv[2 * it + 1] << 16);
   }
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const float dh = P.d[h];
-  const int nkc = NKC ? NKC : P.DK / 16;
+  const int nks = NKS ? NKS : pad32(P.DK) / 32;
   const int nib = (ci.z + 15) / 16;  // 16-row blocks holding rows of the chunk
   // M on the lower-triangular tiles (ib, jb), jb <= ib; tiles dealt round robin over the waves
   const int nwv = blockDim.x >> 6;
@@ -484,12 +546,10 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
     const int jb = t - ib * (ib + 1) / 2;
     f32x4 g = {0.f, 0.f, 0.f, 0.f};
     if (ib < nib) {
-      f32x4 g1 = g;
-#pragma unroll 8
-      for (int kc = 0; kc < nkc; ++kc)
-        mfma16x2(lds4(sQ + (ib * 16 + lr) * kLdK + 16 * kc + 4 * lg), lds4(sKS + (jb * 16 + lr) * kLdK + 16 * kc + 4 * lg),
-                 g, g1);
-      g += g1;
+for (int ks = 0; ks < nks; ++ks) {
+        const int ao = (ib * 16 + lr) * kLdB + 32 * ks + 8 * lg, bo = (jb * 16 + lr) * kLdB + 32 * ks + 8 * lg;
+        g = mfma3(lds16(sQ[0] + ao), lds16(sQ[1] + ao), lds16(sKS[0] + bo), lds16(sKS[1] + bo), g);
+      }
     }
     const int j = jb * 16 + lr;
 #pragma unroll
@@ -498,22 +558,33 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
       float m = 0.f;
       if (j < i) m = g[r] * __expf(L.cs[i] - L.cs[j]) * L.sc[j];
       else if (j == i) m = fmaf(g[r], L.dp[i], dh);
-      sM[i * kLdT + j] = m;
+      const uint32_t hi = bf_hi(m);
+      sM[0][i * kLdT + j] = (bf16_t)hi;
+      sM[1][i * kLdT + j] = (bf16_t)bf_lo(m, hi);
     }
   }
   // the tiles above the diagonal are zero
   for (int e = threadIdx.x; e < kC * kC; e += blockDim.x) {
     const int i = e / kC, j = e - i * kC;
-    if ((j >> 4) > (i >> 4)) sM[i * kLdT + j] = 0.f;
+    if ((j >> 4) > (i >> 4)) {
+      sM[0][i * kLdT + j] = (bf16_t)0;
+      sM[1][i * kLdT + j] = (bf16_t)0;
+    }
   }
   __syncthreads();  // M complete; the keys are no longer read
   if (has_in) {
+    // S_in rows e, columns n (the columns from DK to the next multiple of 32 stay zero: the
+    // keys' padding)
 #pragma unroll
     for (int it = 0; it < kStIt; ++it) {
       const int e = (int)threadIdx.x + it * kBlock;
       if (e >= n4s) break;
       const int f = e / (P.DK / 4), n4 = e - f * (P.DK / 4);
-      *reinterpret_cast<float4*>(sKS + f * kLdK + 4 * n4) = sv[it];
+      const float4 v4 = sv[it];
+      const uint32_t h0 = bf_hi(v4.x), h1 = bf_hi(v4.y), h2 = bf_hi(v4.z), h3 = bf_hi(v4.w);
+      *reinterpret_cast<uint2*>(sKS[0] + f * kLdB + 4 * n4) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+      *reinterpret_cast<uint2*>(sKS[1] + f * kLdB + 4 * n4) =
+          make_uint2(bf_lo(v4.x, h0) | (bf_lo(v4.y, h1) << 16), bf_lo(v4.z, h2) | (bf_lo(v4.w, h3) << 16));
     }
   }
   __syncthreads();
@@ -527,23 +598,24 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
       const int i = ib * 16 + 4 * lg + r;
       zf[r] = i < ci.z ? bf(P.z + ((size_t)(ci.y + i) * P.H + h) * P.DV + f) : 0.f;
     }
-    f32x4 y = {0.f, 0.f, 0.f, 0.f}, y1 = y;
+    f32x4 y = {0.f, 0.f, 0.f, 0.f};
     if (has_in) {
-#pragma unroll 8
-      for (int kc = 0; kc < nkc; ++kc)
-        mfma16x2(lds4(sQ + (ib * 16 + lr) * kLdK + 16 * kc + 4 * lg), lds4(sKS + (eb * 16 + lr) * kLdK + 16 * kc + 4 * lg),
-                 y, y1);
-      y += y1;
-      y1 = f32x4{0.f, 0.f, 0.f, 0.f};
+for (int ks = 0; ks < nks; ++ks) {
+        const int ao = (ib * 16 + lr) * kLdB + 32 * ks + 8 * lg, bo = (eb * 16 + lr) * kLdB + 32 * ks + 8 * lg;
+        y = mfma3(lds16(sQ[0] + ao), lds16(sQ[1] + ao), lds16(sKS[0] + bo), lds16(sKS[1] + bo), y);
+      }
 #pragma unroll
       for (int r = 0; r < 4; ++r) y[r] *= __expf(L.cs[ib * 16 + 4 * lg + r]);
     }
-    // all four column steps: M is zero above its diagonal tiles and v past the chunk's end
+    // both 32-column steps: M is zero above its diagonal tiles and v past the chunk's end; v is
+    // exact in bf16, so M's two halves take one product each
 #pragma unroll
-    for (int jc = 0; jc < kC / 16; ++jc)
-      mfma16x2(lds4(sM + (ib * 16 + lr) * kLdT + 16 * jc + 4 * lg), lds4(sVt + (eb * 16 + lr) * kLdT + 16 * jc + 4 * lg), y,
-               y1);
-    y += y1;
+    for (int js = 0; js < kC / 32; ++js) {
+      const int ao = (ib * 16 + lr) * kLdT + 32 * js + 8 * lg;
+      const u32x4 vb = lds16(sVt + (eb * 16 + lr) * kLdT + 32 * js + 8 * lg);
+      y = mfma_bf(lds16(sM[0] + ao), vb, y);
+      y = mfma_bf(lds16(sM[1] + ao), vb, y);
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int i = ib * 16 + 4 * lg + r;
@@ -657,7 +729,7 @@ hipError_t launch_mamba3_forward(const M3Args& a, const M3Layout& lay, char* ws,
   M2_LAUNCH("m3_pass", m3_pass_kernel, dim3((unsigned)((f4 + 255) / 256), (unsigned)P.H, (unsigned)(S < 65535 ? S : 65535)),
             dim3(256), 0, st, P, S);
   if (P.DK == 128) {
-    M2_LAUNCH("m3_chunk_out", m3_chunk_out_kernel<8>, dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P, nch);
+    M2_LAUNCH("m3_chunk_out", m3_chunk_out_kernel<4>, dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P, nch);
   } else {
     M2_LAUNCH("m3_chunk_out", m3_chunk_out_kernel<0>, dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P, nch);
   }
