@@ -223,3 +223,23 @@ def test_snapshot_edge_cases(gpu):
     e0 = torch.empty((0, sh.conv_dim), dtype=torch.bfloat16, device="cuda")
     ops.scan_verify(e0, e0, e0, p.a_log, p.dt_bias, p.D, sp, None, empty, dims)
     ops.commit_snapshots(sp, cp, None, None, 1, None, empty, dims)
+
+
+@pytest.mark.parametrize("make", ["long_prefill", "decay_span_prefill"])
+def test_tail_walk_matches_stored_segment_states(gpu, make):
+    """The plain prefill lets the output workgroup of a segment recompute a predecessor's local
+    state when that predecessor decays below e^-60 (nothing else reads it); the snapshot entry
+    stores, chains and reads every segment's state.  With snapshots every 1024 rows both take the
+    same 1024-row segments, so y and the final slots agree bit for bit: on the long prefill
+    (every segment decays that much) and on the decay-span batch (mixed per head pair)."""
+    wl = getattr(W, make)()
+    b = gpu.batch_of(wl)
+    p = gpu.Params(wl)
+    xa_g, _ = gpu.gpu_conv(wl, wl.xbc, wl.conv_pool, b, p)
+    y_plain, sp_plain = gpu.gpu_scan(wl, xa_g, wl.dt, wl.ssm_pool, b, p)
+    y_snap, sp_snap, _ = _gpu_scan_snap(gpu, wl, xa_g, 1024, b, p)
+    same_y = np.array_equal(y_plain, y_snap)
+    same_states = np.array_equal(sp_plain, sp_snap)
+    say("[%s] plain vs stored segment states: y bit-identical %s, slots bit-identical %s" % (wl.name, same_y,
+                                                                                            same_states))
+    assert same_y and same_states
