@@ -84,16 +84,24 @@ __global__ __launch_bounds__(256) void scan_pass_kernel(const int2* __restrict__
                                                         int f4, int S) {
   const int f = blockIdx.x * blockDim.x + threadIdx.x;
   const int h = blockIdx.y;
-  if (f >= f4) return;
+  const bool live = f < f4;  // lanes past the state only take part in the wave's test below
   for (int s = blockIdx.z; s < S; s += gridDim.z) {
     const int2 si = seq_info[s];
     if (si.y < 2) continue;
     auto at = [&](int k) -> float4& { return seg_state[((size_t)(si.x + k) * H + h) * f4 + f]; };
     float4 Sr = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (!fresh[s]) {
+    if (live && !fresh[s]) {
       Sr = pool[((size_t)slots[s] * H + h) * f4 + f];
       at(0) = Sr;
     }
+    // no segment with a nonzero factor (every carried state dropped): nothing to chain.  All
+    // 64 lanes of the wave read the factors, 64 at a time, so the wave leaves after one round
+    bool any = false;
+    for (int k0 = 0; k0 + 1 < si.y && !any; k0 += 64) {
+      const int k = k0 + (int)(threadIdx.x & 63);
+      any = __ballot(k + 1 < si.y && seg_decay[(int64_t)(si.x + k) * H + h] != 0.f) != 0;
+    }
+    if (!any || !live) continue;
     bool valid = true;  // Sr holds S_in(k) of the step below
     for (int k0 = 0; k0 + 1 < si.y; k0 += kBatch) {
       float4 loc[kBatch];

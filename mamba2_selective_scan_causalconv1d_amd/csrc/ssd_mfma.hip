@@ -477,7 +477,8 @@ __device__ __forceinline__ void walk_local_state(f32x4 (&S)[2][8], const bf16_t*
   __syncthreads();  // every wave has read its frame scale: the decay slots are free
 }
 
-// Log-decay sums of every chunk of every segment but a sequence's last, per head: the sum of
+// Log-decay sums of every chunk of every segment, per head (those of a sequence's last segment
+// are not used; computing them spares a dependent load of the sequence table): the sum of
 // a_t = -exp(A_log) softplus(dt_t + dt_bias) over the chunk's rows.  One wave per (segment,
 // chunk), lane = head (heads in blocks of 64), so that each load of dt is one contiguous row
 // and the softplus work is spread over the whole chip; cpb workgroups of four waves per
@@ -490,7 +491,7 @@ __global__ __launch_bounds__(256) void chunk_sums_kernel(const bf16_t* __restric
   const int q = (blockIdx.x % cpb) * 4 + ((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int4 si0 = sp.seg_info[seg];
   const int4 si = make_int4(uniform(si0.x), uniform(si0.y), uniform(si0.z), uniform(si0.w));
-  if (si.w == uniform(sp.seq_info[si.x].y) - 1 || q * kQ >= si.z) return;  // wave-uniform; no barriers
+  if (q * kQ >= si.z) return;  // wave-uniform; no barriers
   const int nr = min(kQ, si.z - q * kQ);
   // rows past the chunk's end read as zero and are not summed; lanes past H are unused
   const Rsrc r = make_rsrc(dt + (size_t)(si.y + q * kQ) * H, (int64_t)nr * H * 2);
