@@ -198,7 +198,7 @@ struct RowLds<true> {
 };
 
 template <bool kCS>
-__device__ void chunk_rows(const M3Ptrs& P, int c, const int4& ci, int h, RowLds<kCS>& L) {
+__device__ __forceinline__ void chunk_rows(const M3Ptrs& P, int c, const int4& ci, int h, RowLds<kCS>& L) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, nw = blockDim.x >> 6;
   const int r = ci.y + lane;
   const bool on = lane < ci.z;
@@ -273,7 +273,7 @@ __device__ __forceinline__ void fetch_rows(RowUnits& u, const bf16_t* src, const
 }
 // rotary(src_i + bias, phi_i) from the fetched units, as bf16 hi and lo planes [i * ld + n]
 // (zeros past the chunk's end and, along the width, up to the next multiple of 32).
-__device__ void rotate_rows(const RowUnits& u, const RowLds<true>& L, const int4& ci, int DK, int NA, bf16_t* dh,
+__device__ __forceinline__ void rotate_rows(const RowUnits& u, const RowLds<true>& L, const int4& ci, int DK, int NA, bf16_t* dh,
                             bf16_t* dl, int ld) {
   const int npair = DK / 2, np = pad32(DK) / 2, nfill = kC * np;  // np as in the fetch
 #pragma unroll
@@ -317,7 +317,7 @@ __device__ __forceinline__ void fetch_rows_t(RowUnits& u, const bf16_t* src, con
 }
 // kh^T as hi and lo planes [n][j] (zeros past the chunk's end) from fetch_rows_t's units; fin
 // (may be null): the fp32 values of row il.
-__device__ void rotate_rows_t(const RowUnits& u, const RowLds<false>& L, const int4& ci, int DK, int NA, bf16_t* dh,
+__device__ __forceinline__ void rotate_rows_t(const RowUnits& u, const RowLds<false>& L, const int4& ci, int DK, int NA, bf16_t* dh,
                               bf16_t* dl, int ld, float* fin, int il) {
   const int npair = DK / 2, n = (kC / 2) * npair;
 #pragma unroll
@@ -381,7 +381,14 @@ constexpr int kLdT = kC + 8;      // LDS row pitch of transposed tiles (a chunk'
 // completes); the chunk's decay factor; for a sequence's last chunk, its final K, V and angle.
 // S_loc [DV][DK] = (w o V)^T K on 16 x 16 tiles dealt over the waves, the chunk's rows as k
 // (two 32-row steps), both operands transposed in LDS as bf16 hi / lo planes.
+// KDK, KDV: the query / key and value widths when fixed at compile time (the address
+// arithmetic then has no run-time divisions), else 0.
+template <int KDK, int KDV>
 __global__ __launch_bounds__(kBlock) void m3_chunk_state_kernel(M3Ptrs P, int nch) {
+  if constexpr (KDK != 0) {
+    P.DK = KDK;
+    P.DV = KDV;
+  }
   __shared__ __attribute__((aligned(16))) bf16_t sKt[2][kMaxDK * kLdT];  // kh^T [n][j], hi and lo
   __shared__ __attribute__((aligned(16))) bf16_t sVt[2][kMaxDV * kLdT];  // (w v)^T [e][j], hi and lo
   __shared__ RowLds<false> L;
@@ -492,10 +499,14 @@ __global__ __launch_bounds__(256) void m3_pass_kernel(M3Ptrs P, int S) {
 // diagonal, dt_i p_i and d on it, zero above), in LDS as hi / lo planes; (3) the state entering
 // the chunk over the keys' LDS, as hi / lo planes; (4) Y = exp(cs_i) qh S_in^T + M v on 16 x 16
 // tiles (rows x value columns), the gate, bf16 stores.
-// NKS: the query / key width in 32-column steps when fixed at compile time (4: width 128),
-// else 0 (counted at run time).
-template <int NKS>
+// KDK, KDV: the query / key and value widths when fixed at compile time (the address
+// arithmetic then has no run-time divisions and the k steps are unrolled), else 0.
+template <int KDK, int KDV>
 __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch) {
+  if constexpr (KDK != 0) {
+    P.DK = KDK;
+    P.DV = KDV;
+  }
   __shared__ __attribute__((aligned(16))) bf16_t sQ[2][kC * kLdB];     // qh [i][n], hi and lo
   __shared__ __attribute__((aligned(16))) bf16_t sKS[2][kC * kLdB];    // kh [j][n], then S_in [e][n]
   __shared__ __attribute__((aligned(16))) bf16_t sVt[kMaxDV * kLdT];   // v^T [e][j]
@@ -537,7 +548,7 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
   __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
   const float dh = P.d[h];
-  const int nks = NKS ? NKS : pad32(P.DK) / 32;
+  const int nks = pad32(P.DK) / 32;
   const int nib = (ci.z + 15) / 16;  // 16-row blocks holding rows of the chunk
   // M on the lower-triangular tiles (ib, jb), jb <= ib; tiles dealt round robin over the waves
   const int nwv = blockDim.x >> 6;
@@ -546,7 +557,7 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
     const int jb = t - ib * (ib + 1) / 2;
     f32x4 g = {0.f, 0.f, 0.f, 0.f};
     if (ib < nib) {
-for (int ks = 0; ks < nks; ++ks) {
+      for (int ks = 0; ks < nks; ++ks) {
         const int ao = (ib * 16 + lr) * kLdB + 32 * ks + 8 * lg, bo = (jb * 16 + lr) * kLdB + 32 * ks + 8 * lg;
         g = mfma3(lds16(sQ[0] + ao), lds16(sQ[1] + ao), lds16(sKS[0] + bo), lds16(sKS[1] + bo), g);
       }
@@ -600,7 +611,7 @@ for (int ks = 0; ks < nks; ++ks) {
     }
     f32x4 y = {0.f, 0.f, 0.f, 0.f};
     if (has_in) {
-for (int ks = 0; ks < nks; ++ks) {
+      for (int ks = 0; ks < nks; ++ks) {
         const int ao = (ib * 16 + lr) * kLdB + 32 * ks + 8 * lg, bo = (eb * 16 + lr) * kLdB + 32 * ks + 8 * lg;
         y = mfma3(lds16(sQ[0] + ao), lds16(sQ[1] + ao), lds16(sKS[0] + bo), lds16(sKS[1] + bo), y);
       }
@@ -724,14 +735,23 @@ hipError_t launch_mamba3_forward(const M3Args& a, const M3Layout& lay, char* ws,
     M2_LAUNCH("m3_angle_prefix", m3_angle_prefix_kernel, dim3((unsigned)S, (unsigned)((P.H * P.NA + 255) / 256)),
               dim3(256), 0, st, P, S);
   }
-  M2_LAUNCH("m3_chunk_state", m3_chunk_state_kernel, dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P, nch);
+  const bool fixed = P.DK == 128 && P.DV == 64;  // the widths of the workloads' shape
+  if (fixed) {
+    M2_LAUNCH("m3_chunk_state", (m3_chunk_state_kernel<128, 64>), dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock),
+              0, st, P, nch);
+  } else {
+    M2_LAUNCH("m3_chunk_state", (m3_chunk_state_kernel<0, 0>), dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0,
+              st, P, nch);
+  }
   const int f4 = P.DV * P.DK / 4;
   M2_LAUNCH("m3_pass", m3_pass_kernel, dim3((unsigned)((f4 + 255) / 256), (unsigned)P.H, (unsigned)(S < 65535 ? S : 65535)),
             dim3(256), 0, st, P, S);
-  if (P.DK == 128) {
-    M2_LAUNCH("m3_chunk_out", m3_chunk_out_kernel<4>, dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P, nch);
+  if (fixed) {
+    M2_LAUNCH("m3_chunk_out", (m3_chunk_out_kernel<128, 64>), dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st,
+              P, nch);
   } else {
-    M2_LAUNCH("m3_chunk_out", m3_chunk_out_kernel<0>, dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P, nch);
+    M2_LAUNCH("m3_chunk_out", (m3_chunk_out_kernel<0, 0>), dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P,
+              nch);
   }
   return hipSuccess;
 }
