@@ -27,6 +27,7 @@
 // v_mfma_f32_16x16x32_bf16 (~2^-16 relative, well inside the output and state bars; v, exact
 // in bf16, takes M's two halves directly).  The rotary angles entering each chunk are summed in
 // double (their running sum covers whole sequences); within a chunk (at most 64 terms) in fp32.
+#include <algorithm>
 #include <initializer_list>
 
 #include "common.h"
@@ -44,6 +45,21 @@ constexpr int kBlock = 1024;  // threads of the chunk-state and output workgroup
 
 __device__ __forceinline__ float bf(const bf16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
+// Entries of the chunk and sequence tables at a wave-uniform index, read through the constant
+// address space so that they are scalar loads: a vector load made uniform would wait for
+// every vector load issued before it.
+typedef const __attribute__((address_space(4))) int* ConstInts;
+__device__ __forceinline__ int4 load_scalar(const int4* p, int i) {
+  const ConstInts q = (ConstInts)p + 4 * i;
+  return make_int4(q[0], q[1], q[2], q[3]);
+}
+__device__ __forceinline__ int2 load_scalar(const int2* p, int i) {
+  const ConstInts q = (ConstInts)p + 2 * i;
+  return make_int2(q[0], q[1]);
+}
+// A compiler-level fence: no memory access is moved across it (the loads before it are
+// issued before those after it; waits are still placed only where values are used).
+__device__ __forceinline__ void issue_order() { asm volatile("" ::: "memory"); }
 // The rotary angles are summed in double: the running sum covers up to thousands of tokens,
 // and fp32 rounding of its partial sums would add up to ~1e-4 radian.
 constexpr double kTwoPiD = 6.283185307179586476925287;
@@ -119,6 +135,7 @@ struct M3Ptrs {
   float* decay;           // [nch][H] exp(sum of adt over the chunk)
   float* state;           // [nch][H][DV][DK]: at chunk c + 1 the local state of chunk c, then S_in(c + 1)
   int H, DK, DV, NA;
+  int T;  // rows of the batch
 };
 
 // ------------------------------------------------------------------ rotary-angle totals
@@ -197,48 +214,75 @@ struct RowLds<true> {
   float cosv[kC][kMaxNA], sinv[kC][kMaxNA];
 };
 
-template <bool kCS>
-__device__ __forceinline__ void chunk_rows(const M3Ptrs& P, int c, const int4& ci, int h, RowLds<kCS>& L) {
+
+// The loads of the row scalars and angles, issued on their own so that a caller can order them
+// against other loads (a wave waits for its loads in issue order), at addresses clamped into
+// the chunk and the batch, with no branch around a load and no use of a loaded value here: a
+// guarded load would be waited for inside its branch, and a select right after a load waits
+// for it.  The values are raw; rows_from keeps those of valid rows.  The next row's dt and trap
+// are fetched wherever the batch has that row; they are used only where it belongs to the same
+// sequence.
+// kIt: rotary pairs per wave the caller covers (NA <= kIt * kBlock / 64).
+template <int kIt>
+struct RowFetch {
+  float dt, adt, dtn;
+  bf16_t trap, trapn;
+  float base_f[kIt];
+  bf16_t ang[kIt];
+};
+template <int kIt>
+__device__ __forceinline__ void fetch_row_scalars(RowFetch<kIt>& f, const M3Ptrs& P, int c, const int4& ci, int h) {
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, nw = blockDim.x >> 6;
-  const int r = ci.y + lane;
+  const int r = ci.y + min(lane, ci.z - 1);  // a row of the chunk for every lane
+  const int rn = min(r + 1, P.T - 1);
+  f.dt = P.dt[(size_t)r * P.H + h];
+  f.adt = P.adt[(size_t)r * P.H + h];  // these four for wave 0 only, fetched by every wave
+  f.trap = P.trap[(size_t)r * P.H + h];
+  f.dtn = P.dt[(size_t)rn * P.H + h];
+  f.trapn = P.trap[(size_t)rn * P.H + h];
+  if (P.NA > 0) {
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+      const int ac = min(w + it * nw, P.NA - 1);
+      f.base_f[it] = P.ang_tot[((size_t)c * P.H + h) * P.NA + ac];
+      f.ang[it] = P.angles[(size_t)r * P.NA + ac];
+    }
+  }
+}
+// The row scalars and angles from the fetched values, into L:
+//   cs[i] = sum of adt over rows <= i of the chunk; sc[i] = scale_i; dp[i] = dt_i p_i;
+//   the rotary angle of row i, pair a: the angle entering the chunk (the prefix kernel's), then
+//   the running sum over this chunk's rows (at most 64 terms: fp32, by DPP), reduced mod 2 pi in
+//   double; kept as its cosine and sine (kCS) or as the angle.
+template <bool kCS, int kIt>
+__device__ __forceinline__ void rows_from(const RowFetch<kIt>& f, const M3Ptrs& P, const int4& ci, const int2& si,
+                                          RowLds<kCS>& L) {
+  const int tid = threadIdx.x, w = tid >> 6, nw = blockDim.x >> 6;
+  int lane = tid & 63;
+  asm volatile("" : "+v"(lane));  // the table addresses are recomputed here, not kept live across a caller's loop
   const bool on = lane < ci.z;
-  const int2 si = P.seq_info[ci.x];
+  const float dtv = on ? f.dt : 0.f;
   if (w == 0) {
     // decay prefix, p, scale (the next row may lie in the next chunk of the same sequence)
-    const float cs = wave_scan(on ? P.adt[(size_t)r * P.H + h] : 0.f);
+    const float cs = wave_scan(on ? f.adt : 0.f);
     const bool last_chunk = ci.w == si.y - 1;
     const bool has_next = on && (lane + 1 < ci.z || !last_chunk);
-    const float dtv = on ? P.dt[(size_t)r * P.H + h] : 0.f;
-    const float p = on ? sigmoidf_(bf(P.trap + (size_t)r * P.H + h)) : 0.f;
+    const float p = on ? sigmoidf_(bf16_to_f32(f.trap)) : 0.f;
     float sg = 0.f;
     if (has_next) {
-      const float dtn = P.dt[(size_t)(r + 1) * P.H + h];
-      const float pn = sigmoidf_(bf(P.trap + (size_t)(r + 1) * P.H + h));
-      sg = dtn * (1.f - pn);
+      const float pn = sigmoidf_(bf16_to_f32(f.trapn));
+      sg = f.dtn * (1.f - pn);
     }
     L.cs[lane] = cs;
     L.sc[lane] = dtv * p + sg;
     L.dp[lane] = dtv * p;
   }
-  // rotary angles: the angle entering the chunk (the prefix kernel's), then the running sum
-  // over this chunk's rows (at most 64 terms: fp32, by DPP), reduced mod 2 pi in double;
-  // every load of the wave's pairs issued before the first is used
-  const float dtv = on ? P.dt[(size_t)r * P.H + h] : 0.f;
-  constexpr int kItA = kMaxNA / (kBlock / 64);
-  float base_f[kItA];
-  bf16_t ang[kItA];
 #pragma unroll
-  for (int it = 0; it < kItA; ++it) {
-    const int a = w + it * nw;
-    base_f[it] = a < P.NA ? P.ang_tot[((size_t)c * P.H + h) * P.NA + a] : 0.f;
-    ang[it] = a < P.NA && on ? P.angles[(size_t)r * P.NA + a] : (bf16_t)0;
-  }
-#pragma unroll
-  for (int it = 0; it < kItA; ++it) {
+  for (int it = 0; it < kIt; ++it) {
     const int a = w + it * nw;
     if (a >= P.NA) break;
-    const float v = wave_scan(on ? tanh_fast(bf16_to_f32(ang[it])) * (float)kPiD * dtv : 0.f);
-    const float ph = (float)mod2pi((double)base_f[it] + (double)v);
+    const float v = wave_scan(on ? tanh_fast(bf16_to_f32(f.ang[it])) * (float)kPiD * dtv : 0.f);
+    const float ph = (float)mod2pi((double)f.base_f[it] + (double)v);
     if constexpr (kCS) {
       L.cosv[lane][a] = __cosf(ph);
       L.sinv[lane][a] = __sinf(ph);
@@ -259,22 +303,12 @@ struct RowUnits {
   float2 bias[kRowIt];
 };
 // np: component pairs per row of the staging (DK / 2, or more for zero padding); unit e is
-// row e / np, pair e % np.
-__device__ __forceinline__ void fetch_rows(RowUnits& u, const bf16_t* src, const float* bias, const int4& ci, int DK,
-                                           int np) {
-  const int npair = DK / 2, n = kC * np;
-#pragma unroll
-  for (int it = 0; it < kRowIt; ++it) {
-    const int e = (int)threadIdx.x + it * kBlock, i = e / np, a = e - i * np;
-    const bool on = e < n && i < ci.z && a < npair;
-    u.raw[it] = on ? *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + i) * DK + 2 * a) : 0u;
-    u.bias[it] = on ? *reinterpret_cast<const float2*>(bias + 2 * a) : make_float2(0.f, 0.f);
-  }
-}
+// row e / np, pair e % np (fetch_raw and fetch_bias below).
 // rotary(src_i + bias, phi_i) from the fetched units, as bf16 hi and lo planes [i * ld + n]
 // (zeros past the chunk's end and, along the width, up to the next multiple of 32).
-__device__ __forceinline__ void rotate_rows(const RowUnits& u, const RowLds<true>& L, const int4& ci, int DK, int NA, bf16_t* dh,
-                            bf16_t* dl, int ld) {
+// raw: the fetched pairs (fetch_raw); bias: the head's bias, DK floats (in LDS).
+__device__ __forceinline__ void rotate_rows(const uint32_t (&raw)[kRowIt], const float* bias, const RowLds<true>& L,
+                                            const int4& ci, int DK, int NA, bf16_t* dh, bf16_t* dl, int ld) {
   const int npair = DK / 2, np = pad32(DK) / 2, nfill = kC * np;  // np as in the fetch
 #pragma unroll
   for (int it = 0; it < kRowIt; ++it) {
@@ -283,9 +317,10 @@ __device__ __forceinline__ void rotate_rows(const RowUnits& u, const RowLds<true
     const int i = e / np, a = e - i * np;
     float x0 = 0.f, x1 = 0.f;
     if (i < ci.z && a < npair) {
-      const uint32_t two = u.raw[it];
-      x0 = bf16_to_f32(two & 0xffffu) + u.bias[it].x;
-      x1 = bf16_to_f32(two >> 16) + u.bias[it].y;
+      const uint32_t two = raw[it];
+      const float2 b = *reinterpret_cast<const float2*>(bias + 2 * a);
+      x0 = bf16_to_f32(two & 0xffffu) + b.x;
+      x1 = bf16_to_f32(two >> 16) + b.y;
       if (a < NA) {
         const float cs = L.cosv[i][a], sn = L.sinv[i][a];
         const float r0 = x0 * cs - x1 * sn, r1 = x0 * sn + x1 * cs;
@@ -300,19 +335,20 @@ __device__ __forceinline__ void rotate_rows(const RowUnits& u, const RowLds<true
 }
 // Transposed staging in row pairs: unit e is rows 2 (e / npair) and + 1, component pair
 // e % npair, so that each plane takes one 4-byte store per unit and column.  u.raw[2 it + r]
-// holds row 2 ip + r of unit it; u.bias[it] the pair's bias.
+// holds row 2 ip + r of unit it (raw: rows past the chunk's end hold its last row's values);
+// u.bias[it] the pair's bias.
 __device__ __forceinline__ void fetch_rows_t(RowUnits& u, const bf16_t* src, const float* bias, const int4& ci,
                                              int DK) {
-  const int npair = DK / 2, n = (kC / 2) * npair;
+  const int npair = DK / 2;
 #pragma unroll
   for (int it = 0; it < kRowIt / 2; ++it) {
     const int e = (int)threadIdx.x + it * kBlock, ip = e / npair, a = e - ip * npair;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int i = 2 * ip + r;
-      u.raw[2 * it + r] = e < n && i < ci.z ? *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + i) * DK + 2 * a) : 0u;
+      const int i = 2 * ip + r;  // loaded at a row clamped into the chunk (used for rows of it only)
+      u.raw[2 * it + r] = *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + min(i, ci.z - 1)) * DK + 2 * a);
     }
-    u.bias[it] = e < n ? *reinterpret_cast<const float2*>(bias + 2 * a) : make_float2(0.f, 0.f);
+    u.bias[it] = *reinterpret_cast<const float2*>(bias + 2 * a);
   }
 }
 // kh^T as hi and lo planes [n][j] (zeros past the chunk's end) from fetch_rows_t's units; fin
@@ -358,7 +394,7 @@ __device__ __forceinline__ void rotate_rows_t(const RowUnits& u, const RowLds<fa
   }
 }
 // The chunk's rows of head h's values in row pairs: unit e is rows 2 (e / DV) and + 1, column
-// e % DV (vv[2 it + r]: row 2 jp + r), zero past the chunk's end.
+// e % DV (vv[2 it + r]: row 2 jp + r; raw: rows past the chunk's end hold its last row's values).
 constexpr int kValIt = kC * kMaxDV / kBlock;
 __device__ __forceinline__ void fetch_values_t(bf16_t (&vv)[kValIt], const M3Ptrs& P, const int4& ci, int h) {
 #pragma unroll
@@ -366,11 +402,40 @@ __device__ __forceinline__ void fetch_values_t(bf16_t (&vv)[kValIt], const M3Ptr
     const int e = (int)threadIdx.x + it * kBlock, jp = e / P.DV, f = e - jp * P.DV;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-      const int j = 2 * jp + r;
-      vv[2 * it + r] = e < (kC / 2) * P.DV && j < ci.z ? P.v[((size_t)(ci.y + j) * P.H + h) * P.DV + f] : (bf16_t)0;
+      const int j = 2 * jp + r;  // loaded at a row clamped into the chunk (used for rows of it only)
+      vv[2 * it + r] = P.v[((size_t)(ci.y + min(j, ci.z - 1)) * P.H + h) * P.DV + f];
     }
   }
 }
+// A chunk's queries and keys (raw pairs, in rotate_rows' unit order; the biases are the head's
+// and fetched once), values (fetch_values_t's order) and entering state, in registers, as
+// loaded (no select: each use keeps the valid entries).
+struct ChunkData {
+  uint32_t q[kRowIt], k[kRowIt];
+  bf16_t v[kValIt];
+  float4 s[kMaxDV * kMaxDK / 4 / kBlock];
+};
+__device__ __forceinline__ void fetch_raw(uint32_t (&raw)[kRowIt], const bf16_t* src, const int4& ci, int DK, int np) {
+  const int npair = DK / 2;
+#pragma unroll
+  for (int it = 0; it < kRowIt; ++it) {
+    const int e = (int)threadIdx.x + it * kBlock, i = e / np, a = e - i * np;
+    // loaded at a row and pair clamped into the chunk (rotate_rows uses units of it only)
+    raw[it] = *reinterpret_cast<const uint32_t*>(src + (size_t)(ci.y + min(i, ci.z - 1)) * DK + 2 * min(a, npair - 1));
+  }
+}
+__device__ __forceinline__ void fetch_chunk(ChunkData& d, const M3Ptrs& P, int c, const int4& ci, int h, int np) {
+  fetch_raw(d.q, P.q, ci, P.DK, np);
+  fetch_raw(d.k, P.k, ci, P.DK, np);
+  fetch_values_t(d.v, P, ci, h);
+  const int n4s = P.DV * (P.DK / 4);
+  const float4* sin = reinterpret_cast<const float4*>(P.state + ((size_t)c * P.H + h) * (size_t)P.DV * P.DK);
+  // every chunk's slot lies in the workspace (a sequence's first chunk's is not written: its
+  // values are loaded and not used)
+#pragma unroll
+  for (int it = 0; it < kMaxDV * kMaxDK / 4 / kBlock; ++it) d.s[it] = sin[min((int)threadIdx.x + it * kBlock, n4s - 1)];
+}
+
 // ------------------------------------------------------------------ chunk states
 
 constexpr int kLdB = kMaxDK + 8;  // LDS row pitch of query / key / state rows (bf16 elements)
@@ -382,8 +447,9 @@ constexpr int kLdT = kC + 8;      // LDS row pitch of transposed tiles (a chunk'
 // S_loc [DV][DK] = (w o V)^T K on 16 x 16 tiles dealt over the waves, the chunk's rows as k
 // (two 32-row steps), both operands transposed in LDS as bf16 hi / lo planes.
 // KDK, KDV: the query / key and value widths when fixed at compile time (the address
-// arithmetic then has no run-time divisions), else 0.
-template <int KDK, int KDV>
+// arithmetic then has no run-time divisions), else 0; KNA: the most rotary pairs covered (64
+// when the widths are not fixed).
+template <int KDK, int KDV, int KNA>
 __global__ __launch_bounds__(kBlock) void m3_chunk_state_kernel(M3Ptrs P, int nch) {
   if constexpr (KDK != 0) {
     P.DK = KDK;
@@ -397,12 +463,15 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_state_kernel(M3Ptrs P, int nc
   const int4 ci = P.chunk_info[c];
   const int2 si = P.seq_info[ci.x];
   const bool last = ci.w == si.y - 1;
-  chunk_rows(P, c, ci, h, L);
-  // the chunk's keys and values, fetched together (the row scalars' own loads go first)
+  // the row scalars' loads, then the chunk's keys and values, then the row scalars' arithmetic
+  // (which waits for its own loads only)
+  RowFetch<(KNA + kBlock / 64 - 1) / (kBlock / 64)> rf;
+  fetch_row_scalars(rf, P, c, ci, h);
   RowUnits ku;
   fetch_rows_t(ku, P.k, P.k_bias + (size_t)h * P.DK, ci, P.DK);
   bf16_t vv[kValIt];
   fetch_values_t(vv, P, ci, h);
+  rows_from(rf, P, ci, si, L);
   __syncthreads();
   const int il = ci.z - 1;
   rotate_rows_t(ku, L, ci, P.DK, P.NA, sKt[0], sKt[1], kLdT, last ? P.fin_k + ((size_t)ci.x * P.H + h) * P.DK : nullptr,
@@ -492,16 +561,21 @@ __global__ __launch_bounds__(256) void m3_pass_kernel(M3Ptrs P, int S) {
 
 // ------------------------------------------------------------------ outputs
 
-// grid (chunk, head), kBlock threads (four waves per SIMD at one workgroup per CU, which the
-// LDS allows).  (1) rotated queries and keys of the chunk in LDS (rows, bf16 hi / lo planes,
-// zero-padded to a multiple of 32 columns), the values transposed (bf16, exact); (2) G = qh kh^T
-// on the ten lower-triangular 16 x 16 tiles, turned into M (exp(cs_i - cs_j) scale_j below the
-// diagonal, dt_i p_i and d on it, zero above), in LDS as hi / lo planes; (3) the state entering
-// the chunk over the keys' LDS, as hi / lo planes; (4) Y = exp(cs_i) qh S_in^T + M v on 16 x 16
-// tiles (rows x value columns), the gate, bf16 stores.
+// grid (chunk group, head), kBlock threads (four waves per SIMD at one workgroup per CU, which
+// the LDS allows).  Workgroup (b, h) takes chunks b, b + gridDim.x, ... of head h; the next
+// chunk's queries, keys, values and entering state are fetched into registers while the current
+// one is computed (its own row scalars and gate inputs are fetched first, so that waiting for
+// them never waits for the prefetch).  Per chunk: (1) rotated queries and keys in LDS (rows,
+// bf16 hi / lo planes, zero-padded to a multiple of 32 columns), the values transposed (bf16,
+// exact); (2) G = qh kh^T on the ten lower-triangular 16 x 16 tiles, turned into M
+// (exp(cs_i - cs_j) scale_j below the diagonal, dt_i p_i and d on it; the tiles above are zero),
+// in LDS as hi / lo planes; (3) the state entering the chunk over the keys' LDS, as hi / lo
+// planes; (4) Y = exp(cs_i) qh S_in^T + M v on 16 x 16 tiles (rows x value columns), one per
+// wave, the gate, bf16 stores.
 // KDK, KDV: the query / key and value widths when fixed at compile time (the address
-// arithmetic then has no run-time divisions and the k steps are unrolled), else 0.
-template <int KDK, int KDV>
+// arithmetic then has no run-time divisions and the k steps are unrolled), else 0; KNA: the
+// most rotary pairs covered (64 when the widths are not fixed).
+template <int KDK, int KDV, int KNA>
 __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch) {
   if constexpr (KDK != 0) {
     P.DK = KDK;
@@ -512,69 +586,40 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
   __shared__ __attribute__((aligned(16))) bf16_t sVt[kMaxDV * kLdT];   // v^T [e][j]
   __shared__ __attribute__((aligned(16))) bf16_t sM[2][kC * kLdT];     // M [i][j], hi and lo
   __shared__ RowLds<true> L;
-  const int c = blockIdx.x, h = blockIdx.y;
+  __shared__ __attribute__((aligned(16))) float sBias[2][kMaxDK];        // the head's q and k biases
+  const int h = blockIdx.y, stride = (int)gridDim.x;
+  int c = blockIdx.x;
   if (c >= nch) return;
-  const int4 ci = P.chunk_info[c];
   const int npad = pad32(P.DK) / 2;  // component pairs per staged row, zero padding included
-  // the chunk's queries, keys and values are fetched before the row scalars are computed
-  RowUnits qu, ku;
-  fetch_rows(qu, P.q, P.q_bias + (size_t)h * P.DK, ci, P.DK, npad);
-  fetch_rows(ku, P.k, P.k_bias + (size_t)h * P.DK, ci, P.DK, npad);
-  bf16_t vv[kValIt];
-  fetch_values_t(vv, P, ci, h);
-  // and the state entering the chunk (written into the keys' LDS once the keys are done)
-  const bool has_in = ci.w > 0;
-  constexpr int kStIt = kMaxDV * kMaxDK / 4 / kBlock;
-  const int n4s = P.DV * (P.DK / 4);
-  float4 sv[kStIt];
-  {
-    const float4* sin = reinterpret_cast<const float4*>(P.state + ((size_t)c * P.H + h) * (size_t)P.DV * P.DK);
-#pragma unroll
-    for (int it = 0; it < kStIt; ++it) {
-      const int e = (int)threadIdx.x + it * kBlock;
-      sv[it] = has_in && e < n4s ? sin[e] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-  }
-  chunk_rows(P, c, ci, h, L);
-  __syncthreads();
-  rotate_rows(qu, L, ci, P.DK, P.NA, sQ[0], sQ[1], kLdB);
-  rotate_rows(ku, L, ci, P.DK, P.NA, sKS[0], sKS[1], kLdB);
-#pragma unroll
-  for (int it = 0; it < kValIt / 2; ++it) {
-    const int e = (int)threadIdx.x + it * kBlock, jp = e / P.DV, f = e - jp * P.DV;
-    if (e >= (kC / 2) * P.DV) break;
-    *reinterpret_cast<uint32_t*>(sVt + f * kLdT + 2 * jp) = (uint32_t)vv[2 * it] | ((uint32_t)vv[2 * it + 1] << 16);
-  }
-  __syncthreads();
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 15, lg = lane >> 4;
-  const float dh = P.d[h];
-  const int nks = pad32(P.DK) / 32;
-  const int nib = (ci.z + 15) / 16;  // 16-row blocks holding rows of the chunk
-  // M on the lower-triangular tiles (ib, jb), jb <= ib; tiles dealt round robin over the waves
   const int nwv = blockDim.x >> 6;
-  for (int t = w; t < 10; t += nwv) {
-    const int ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
-    const int jb = t - ib * (ib + 1) / 2;
-    f32x4 g = {0.f, 0.f, 0.f, 0.f};
-    if (ib < nib) {
-      for (int ks = 0; ks < nks; ++ks) {
-        const int ao = (ib * 16 + lr) * kLdB + 32 * ks + 8 * lg, bo = (jb * 16 + lr) * kLdB + 32 * ks + 8 * lg;
-        g = mfma3(lds16(sQ[0] + ao), lds16(sQ[1] + ao), lds16(sKS[0] + bo), lds16(sKS[1] + bo), g);
-      }
-    }
-    const int j = jb * 16 + lr;
+  const float dh = P.d[h];
+  for (int e = threadIdx.x; e < 2 * P.DK; e += blockDim.x)  // visible after the loop's first barrier
+    sBias[e / P.DK][e % P.DK] = (e < P.DK ? P.q_bias : P.k_bias)[(size_t)h * P.DK + e % P.DK];
+  // the wave's output tile of a chunk (16 waves cover its at most 4 x 4 tiles) and its gate
+  // inputs, loaded at rows clamped into the chunk (only rows of it are stored)
+  const int nks = pad32(P.DK) / 32;
+  const int neb = P.DV / 16;
+  auto fetch_gate = [&](float (&zf)[4], const int4& cq) {
+    const int tb = w / neb, te = w - tb * neb;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int i = ib * 16 + 4 * lg + r;
-      float m = 0.f;
-      if (j < i) m = g[r] * __expf(L.cs[i] - L.cs[j]) * L.sc[j];
-      else if (j == i) m = fmaf(g[r], L.dp[i], dh);
-      const uint32_t hi = bf_hi(m);
-      sM[0][i * kLdT + j] = (bf16_t)hi;
-      sM[1][i * kLdT + j] = (bf16_t)bf_lo(m, hi);
+      const int i = tb * 16 + 4 * lg + r;
+      zf[r] = bf(P.z + ((size_t)(cq.y + min(i, cq.z - 1)) * P.H + h) * P.DV + te * 16 + lr);
     }
-  }
-  // the tiles above the diagonal are zero
+  };
+  int4 ci = load_scalar(P.chunk_info, c);
+  int2 si = load_scalar(P.seq_info, ci.x);
+  RowFetch<(KNA + kBlock / 64 - 1) / (kBlock / 64)> rf;
+  fetch_row_scalars(rf, P, c, ci, h);
+  float zf[4];
+  fetch_gate(zf, ci);
+  issue_order();
+  ChunkData cur;
+  fetch_chunk(cur, P, c, ci, h, npad);
+  int cn = c + stride;
+  int4 cin = load_scalar(P.chunk_info, min(cn, nch - 1));
+  // the tiles of M above the diagonal are zero for every chunk
   for (int e = threadIdx.x; e < kC * kC; e += blockDim.x) {
     const int i = e / kC, j = e - i * kC;
     if ((j >> 4) > (i >> 4)) {
@@ -582,59 +627,126 @@ __global__ __launch_bounds__(kBlock) void m3_chunk_out_kernel(M3Ptrs P, int nch)
       sM[1][i * kLdT + j] = (bf16_t)0;
     }
   }
-  __syncthreads();  // M complete; the keys are no longer read
-  if (has_in) {
-    // S_in rows e, columns n (the columns from DK to the next multiple of 32 stay zero: the
-    // keys' padding)
+  for (;;) {
+    const int nib = (ci.z + 15) / 16;  // 16-row blocks holding rows of the chunk
+    const bool has_tile = w < nib * neb;
+    const int tib = w / neb, teb = w - tib * neb;
+    const int f = teb * 16 + lr;
+    // the next chunk's data (this chunk's again when there is none, so the loads stay
+    // unconditional), issued after this chunk's row scalars and gate inputs, so that waiting
+    // for those never waits for the prefetch
+    const bool more = cn < nch;
+    const int cl = more ? cn : c;
+    const int4 cil = more ? cin : ci;
+    issue_order();
+    ChunkData nxt;
+    fetch_chunk(nxt, P, cl, cil, h, npad);
+    issue_order();
+    const int2 sil = load_scalar(P.seq_info, cil.x);
+    const int cnn = cn + stride;
+    const int4 cinn = load_scalar(P.chunk_info, min(cnn, nch - 1));
+
+    rows_from(rf, P, ci, si, L);
+    __syncthreads();
+    rotate_rows(cur.q, sBias[0], L, ci, P.DK, P.NA, sQ[0], sQ[1], kLdB);
+    rotate_rows(cur.k, sBias[1], L, ci, P.DK, P.NA, sKS[0], sKS[1], kLdB);
 #pragma unroll
-    for (int it = 0; it < kStIt; ++it) {
-      const int e = (int)threadIdx.x + it * kBlock;
-      if (e >= n4s) break;
-      const int f = e / (P.DK / 4), n4 = e - f * (P.DK / 4);
-      const float4 v4 = sv[it];
-      const uint32_t h0 = bf_hi(v4.x), h1 = bf_hi(v4.y), h2 = bf_hi(v4.z), h3 = bf_hi(v4.w);
-      *reinterpret_cast<uint2*>(sKS[0] + f * kLdB + 4 * n4) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
-      *reinterpret_cast<uint2*>(sKS[1] + f * kLdB + 4 * n4) =
-          make_uint2(bf_lo(v4.x, h0) | (bf_lo(v4.y, h1) << 16), bf_lo(v4.z, h2) | (bf_lo(v4.w, h3) << 16));
+    for (int it = 0; it < kValIt / 2; ++it) {
+      const int e = (int)threadIdx.x + it * kBlock, jp = e / P.DV, fv = e - jp * P.DV;
+      if (e >= (kC / 2) * P.DV) break;
+      const uint32_t v0 = 2 * jp < ci.z ? cur.v[2 * it] : 0u, v1 = 2 * jp + 1 < ci.z ? cur.v[2 * it + 1] : 0u;
+      *reinterpret_cast<uint32_t*>(sVt + fv * kLdT + 2 * jp) = v0 | (v1 << 16);
     }
-  }
-  __syncthreads();
-  const int neb = P.DV / 16;
-  for (int t = w; t < nib * neb; t += nwv) {
-    const int ib = t / neb, eb = t - ib * neb;
-    const int f = eb * 16 + lr;
-    float zf[4];  // the gate's inputs, loaded before the products
+    __syncthreads();
+    // M on the lower-triangular tiles (ib, jb), jb <= ib; tiles dealt round robin over the waves
+    for (int t = w; t < 10; t += nwv) {
+      const int ib = t < 1 ? 0 : t < 3 ? 1 : t < 6 ? 2 : 3;
+      const int jb = t - ib * (ib + 1) / 2;
+      f32x4 g = {0.f, 0.f, 0.f, 0.f};
+      if (ib < nib) {
+        for (int ks = 0; ks < nks; ++ks) {
+          const int ao = (ib * 16 + lr) * kLdB + 32 * ks + 8 * lg, bo = (jb * 16 + lr) * kLdB + 32 * ks + 8 * lg;
+          g = mfma3(lds16(sQ[0] + ao), lds16(sQ[1] + ao), lds16(sKS[0] + bo), lds16(sKS[1] + bo), g);
+        }
+      }
+      const int j = jb * 16 + lr;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = ib * 16 + 4 * lg + r;
-      zf[r] = i < ci.z ? bf(P.z + ((size_t)(ci.y + i) * P.H + h) * P.DV + f) : 0.f;
+      for (int r = 0; r < 4; ++r) {
+        const int i = ib * 16 + 4 * lg + r;
+        float m = 0.f;
+        if (j < i) m = g[r] * __expf(L.cs[i] - L.cs[j]) * L.sc[j];
+        else if (j == i) m = fmaf(g[r], L.dp[i], dh);
+        const uint32_t hi = bf_hi(m);
+        sM[0][i * kLdT + j] = (bf16_t)hi;
+        sM[1][i * kLdT + j] = (bf16_t)bf_lo(m, hi);
+      }
     }
-    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+    __syncthreads();  // M complete; the keys are no longer read
+    const bool has_in = ci.w > 0;
     if (has_in) {
-      for (int ks = 0; ks < nks; ++ks) {
-        const int ao = (ib * 16 + lr) * kLdB + 32 * ks + 8 * lg, bo = (eb * 16 + lr) * kLdB + 32 * ks + 8 * lg;
-        y = mfma3(lds16(sQ[0] + ao), lds16(sQ[1] + ao), lds16(sKS[0] + bo), lds16(sKS[1] + bo), y);
-      }
+      // S_in rows e, columns n (the columns from DK to the next multiple of 32 stay zero: the
+      // keys' padding)
+      const int n4s = P.DV * (P.DK / 4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[r] *= __expf(L.cs[ib * 16 + 4 * lg + r]);
-    }
-    // both 32-column steps: M is zero above its diagonal tiles and v past the chunk's end; v is
-    // exact in bf16, so M's two halves take one product each
-#pragma unroll
-    for (int js = 0; js < kC / 32; ++js) {
-      const int ao = (ib * 16 + lr) * kLdT + 32 * js + 8 * lg;
-      const u32x4 vb = lds16(sVt + (eb * 16 + lr) * kLdT + 32 * js + 8 * lg);
-      y = mfma_bf(lds16(sM[0] + ao), vb, y);
-      y = mfma_bf(lds16(sM[1] + ao), vb, y);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = ib * 16 + 4 * lg + r;
-      if (i < ci.z) {
-        const size_t o = ((size_t)(ci.y + i) * P.H + h) * P.DV + f;
-        P.out[o] = (bf16_t)f32_to_bf16(y[r] * zf[r] * sigmoidf_(zf[r]));
+      for (int it = 0; it < kMaxDV * kMaxDK / 4 / kBlock; ++it) {
+        const int e = (int)threadIdx.x + it * kBlock;
+        if (e >= n4s) break;
+        const int fe = e / (P.DK / 4), n4 = e - fe * (P.DK / 4);
+        const float4 v4 = cur.s[it];
+        const uint32_t h0 = bf_hi(v4.x), h1 = bf_hi(v4.y), h2 = bf_hi(v4.z), h3 = bf_hi(v4.w);
+        *reinterpret_cast<uint2*>(sKS[0] + fe * kLdB + 4 * n4) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+        *reinterpret_cast<uint2*>(sKS[1] + fe * kLdB + 4 * n4) =
+            make_uint2(bf_lo(v4.x, h0) | (bf_lo(v4.y, h1) << 16), bf_lo(v4.z, h2) | (bf_lo(v4.w, h3) << 16));
       }
     }
+    __syncthreads();
+    // the next chunk's row scalars (this chunk's and its entering state are used up), ahead of
+    // this chunk's stores
+    if (more) {
+      issue_order();
+      fetch_row_scalars(rf, P, cn, cin, h);
+      issue_order();
+    }
+    if (has_tile) {
+      const int ib = tib, eb = teb;
+      f32x4 y = {0.f, 0.f, 0.f, 0.f};
+      if (has_in) {
+        for (int ks = 0; ks < nks; ++ks) {
+          const int ao = (ib * 16 + lr) * kLdB + 32 * ks + 8 * lg, bo = (eb * 16 + lr) * kLdB + 32 * ks + 8 * lg;
+          y = mfma3(lds16(sQ[0] + ao), lds16(sQ[1] + ao), lds16(sKS[0] + bo), lds16(sKS[1] + bo), y);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) y[r] *= __expf(L.cs[ib * 16 + 4 * lg + r]);
+      }
+      // both 32-column steps: M is zero above its diagonal tiles and v past the chunk's end; v
+      // is exact in bf16, so M's two halves take one product each
+#pragma unroll
+      for (int js = 0; js < kC / 32; ++js) {
+        const int ao = (ib * 16 + lr) * kLdT + 32 * js + 8 * lg;
+        const u32x4 vb = lds16(sVt + (eb * 16 + lr) * kLdT + 32 * js + 8 * lg);
+        y = mfma_bf(lds16(sM[0] + ao), vb, y);
+        y = mfma_bf(lds16(sM[1] + ao), vb, y);
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = ib * 16 + 4 * lg + r;
+        if (i < ci.z) {
+          const size_t o = ((size_t)(ci.y + i) * P.H + h) * P.DV + f;
+          P.out[o] = (bf16_t)f32_to_bf16(y[r] * zf[r] * sigmoidf_(zf[r]));
+        }
+      }
+    }
+    if (!more) break;
+    // the next chunk's gate inputs, ahead of the prefetch after it
+    issue_order();
+    fetch_gate(zf, cin);
+    __syncthreads();  // every wave is done with this chunk's LDS
+    c = cn;
+    ci = cin;
+    si = sil;
+    cur = nxt;
+    cn = cnn;
+    cin = cinn;
   }
 }
 
@@ -656,6 +768,7 @@ struct M3Args {
   const void* z;
   const int32_t* cu_seqlens;
   int32_t num_seqs;
+  int64_t num_rows;
   mamba3_dims dims;
 };
 
@@ -725,6 +838,7 @@ hipError_t launch_mamba3_forward(const M3Args& a, const M3Layout& lay, char* ws,
   P.DK = a.dims.qk_dim;
   P.DV = a.dims.v_dim;
   P.NA = a.dims.nangles;
+  P.T = (int)a.num_rows;
   const int S = a.num_seqs;
   const int nch = (int)lay.nch;
   hipError_t e = launch_segment_tables(a.cu_seqlens, S, kC, (int2*)(ws + lay.off_seq), (int4*)(ws + lay.off_chunk), st);
@@ -735,23 +849,26 @@ hipError_t launch_mamba3_forward(const M3Args& a, const M3Layout& lay, char* ws,
     M2_LAUNCH("m3_angle_prefix", m3_angle_prefix_kernel, dim3((unsigned)S, (unsigned)((P.H * P.NA + 255) / 256)),
               dim3(256), 0, st, P, S);
   }
-  const bool fixed = P.DK == 128 && P.DV == 64;  // the widths of the workloads' shape
+  const bool fixed = P.DK == 128 && P.DV == 64 && P.NA <= 32;  // the workloads' shape
   if (fixed) {
-    M2_LAUNCH("m3_chunk_state", (m3_chunk_state_kernel<128, 64>), dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock),
-              0, st, P, nch);
+    M2_LAUNCH("m3_chunk_state", (m3_chunk_state_kernel<128, 64, 32>), dim3((unsigned)nch, (unsigned)P.H),
+              dim3(kBlock), 0, st, P, nch);
   } else {
-    M2_LAUNCH("m3_chunk_state", (m3_chunk_state_kernel<0, 0>), dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0,
-              st, P, nch);
+    M2_LAUNCH("m3_chunk_state", (m3_chunk_state_kernel<0, 0, kMaxNA>), dim3((unsigned)nch, (unsigned)P.H),
+              dim3(kBlock), 0, st, P, nch);
   }
   const int f4 = P.DV * P.DK / 4;
   M2_LAUNCH("m3_pass", m3_pass_kernel, dim3((unsigned)((f4 + 255) / 256), (unsigned)P.H, (unsigned)(S < 65535 ? S : 65535)),
             dim3(256), 0, st, P, S);
+  // output workgroups: one per CU (their LDS) over the 256 CUs, each taking every ngrp-th chunk
+  // of its head
+  const int ngrp = (int)std::min<int64_t>(nch, std::max<int64_t>(1, (256 + P.H - 1) / P.H));
   if (fixed) {
-    M2_LAUNCH("m3_chunk_out", (m3_chunk_out_kernel<128, 64>), dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st,
-              P, nch);
+    M2_LAUNCH("m3_chunk_out", (m3_chunk_out_kernel<128, 64, 32>), dim3((unsigned)ngrp, (unsigned)P.H),
+              dim3(kBlock), 0, st, P, nch);
   } else {
-    M2_LAUNCH("m3_chunk_out", (m3_chunk_out_kernel<0, 0>), dim3((unsigned)nch, (unsigned)P.H), dim3(kBlock), 0, st, P,
-              nch);
+    M2_LAUNCH("m3_chunk_out", (m3_chunk_out_kernel<0, 0, kMaxNA>), dim3((unsigned)ngrp, (unsigned)P.H),
+              dim3(kBlock), 0, st, P, nch);
   }
   return hipSuccess;
 }
@@ -810,7 +927,7 @@ mamba2_status mamba3_siso_forward(void* out, void* final_angle, float* final_ssm
   if (!workspace || workspace_bytes < lay.total) return MAMBA2_WORKSPACE_TOO_SMALL;
   if (((uintptr_t)workspace & 255) != 0) return MAMBA2_INVALID_ARGUMENT;
   M3Args a{out, final_angle, final_ssm, final_k, final_v, q, k, v, adt, dt, trap, q_bias, k_bias, angles, d, z,
-           batch->dev_cu_seqlens, batch->num_seqs, *dims};
+           batch->dev_cu_seqlens, batch->num_seqs, batch->num_rows, *dims};
   return launch_mamba3_forward(a, lay, (char*)workspace, (hipStream_t)stream) == hipSuccess ? MAMBA2_OK
                                                                                             : MAMBA2_HIP_ERROR;
 }
