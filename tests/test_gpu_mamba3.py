@@ -100,6 +100,17 @@ def test_mamba3_edges(gpu):
     compare(gpu, W.mamba3_varlen(13, lengths=[700], H=2, DK=128, DV=64, NA=64, name="mamba3_one_seq_64_pairs"))
 
 
+def test_mamba3_many_chunks_per_workgroup(gpu):
+    """Enough heads that each output workgroup walks several chunks of its head, crossing
+    sequence ends, ragged chunks and one-row sequences on the way: 256 heads at the smallest
+    widths (one workgroup per head takes all eight chunks) and 128 heads at the 128 / 64 widths
+    with 32 rotary pairs (two workgroups per head, every other chunk each)."""
+    compare(gpu, W.mamba3_varlen(15, lengths=[70, 5, 130, 64, 1], H=256, DK=16, DV=16, NA=4,
+                                 name="mamba3_many_chunks_small"))
+    compare(gpu, W.mamba3_varlen(16, lengths=[200, 65, 64, 1], H=128, DK=128, DV=64, NA=32,
+                                 name="mamba3_many_chunks_128x64"))
+
+
 def test_mamba3_rejections(gpu):
     """Misaligned outputs, a short workspace, a value width the tiles do not cover: refused
     before any launch, nothing written."""
