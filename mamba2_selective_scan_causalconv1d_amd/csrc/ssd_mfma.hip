@@ -488,7 +488,8 @@ __global__ __launch_bounds__(256) void chunk_sums_kernel(const bf16_t* __restric
                                                          const float* __restrict__ dt_bias, SegPtrs sp, int H,
                                                          int cpb) {
   const int seg = blockIdx.x / cpb;
-  const int q = (blockIdx.x % cpb) * 4 + ((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+  // wave-uniform (the buffer descriptor built from it must be, or each load becomes a loop)
+  const int q = uniform((int)(blockIdx.x % cpb) * 4 + ((int)threadIdx.x >> 6)), lane = threadIdx.x & 63;
   const int4 si0 = sp.seg_info[seg];
   const int4 si = make_int4(uniform(si0.x), uniform(si0.y), uniform(si0.z), uniform(si0.w));
   if (q * kQ >= si.z) return;  // wave-uniform; no barriers
