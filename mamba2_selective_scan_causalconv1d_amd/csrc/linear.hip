@@ -265,15 +265,27 @@ __global__ __launch_bounds__(512, 1) void linear_bf16_256_kernel(bf16_t* __restr
     wait_vm<0>();
     __syncthreads();  // stage kt visible; stage kt - 1's buffer no longer read
     issue(kt + 1);
+    u32x4 af[2][8], bf[2][4];
+    rd(af[0], bf[0], kt, 0);
+    rd(af[1], bf[1], kt, 1);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
-      u32x4 af[8], bf[4];
-      rd(af, bf, kt, kk);
 #pragma unroll
       for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = mfma(bf[j], af[i], acc[i][j]);
+        for (int j = 0; j < 4; ++j) acc[i][j] = mfma(bf[kk][j], af[kk][i], acc[i][j]);
     }
+    // instruction order: the first half's 12 fragment reads, then the second half's reads one
+    // after every two products, then the remaining products.  Left to itself the compiler reads
+    // each fragment just before its first product and waits for it there (LDS latency on every
+    // fourth product); this order measured 3.5-5 % faster on the layer's shapes.
+    __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // LDS reads
+#pragma unroll
+    for (int g = 0; g < 12; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 40, 0);
   }
   wait_vm<0>();  // the zero fill issued in the last step has landed
 
