@@ -20,7 +20,8 @@
 //   S_loc = sum_j exp(cs_last - cs_j) scale_j v_j kh_j^T,  S_in(next) = exp(cs_last) S_in + S_loc.
 // Launches: chunk tables; per (chunk, head block) the chunk's rotary-angle totals and per
 // (sequence, head) their running sums; per (chunk, head) the chunk state (and a sequence's
-// finals); the state pass per (sequence, head); per (chunk, head) the outputs.  The
+// finals); the state pass per (sequence, head); per (chunk group, head) the outputs, each
+// workgroup walking its group's chunks with the next one's inputs fetched ahead.  The
 // contractions (q.k over a chunk, the state's output term, M v and the chunk state) take fp32
 // operands (the queries and keys after the bias and the rotation, M, the states, w v): each is
 // split into bf16 hi and lo halves in LDS and multiplied as hi.hi + hi.lo + lo.hi on
