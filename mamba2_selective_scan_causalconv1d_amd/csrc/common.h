@@ -173,6 +173,7 @@ struct ScanArgs {
 };
 
 hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st);
+hipError_t launch_scan_setup(const ScanArgs& a, hipStream_t st);  // sequence and segment tables
 hipError_t launch_scan_pass(const ScanArgs& a, hipStream_t st);
 bool decode_supported(const mamba2_dims& dm);
 bool decode_grid_fits(const mamba2_dims& dm, int32_t num_seqs);

@@ -218,9 +218,9 @@ hipError_t launch_scan_generic(const ScanArgs& a, hipStream_t st);
 hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t st);
 
 hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st) {
+  if (scan_uses_mfma(&a.dims)) return launch_scan_mfma(a, st);  // builds the tables itself
   hipError_t e = launch_scan_setup(a, st);
   if (e != hipSuccess) return e;
-  if (scan_uses_mfma(&a.dims)) return launch_scan_mfma(a, st);
   return launch_scan_generic(a, st);
 }
 

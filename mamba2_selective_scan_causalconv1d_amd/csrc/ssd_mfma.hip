@@ -479,34 +479,90 @@ __device__ __forceinline__ void walk_local_state(f32x4 (&S)[2][8], const bf16_t*
 
 // Log-decay sums of every chunk of every segment, per head (those of a sequence's last segment
 // are not used; computing them spares a dependent load of the sequence table): the sum of
-// a_t = -exp(A_log) softplus(dt_t + dt_bias) over the chunk's rows.  One wave per (segment,
-// chunk), lane = head (heads in blocks of 64), so that each load of dt is one contiguous row
-// and the softplus work is spread over the whole chip; cpb workgroups of four waves per
-// segment.
+// a_t = -exp(A_log) softplus(dt_t + dt_bias) over the chunk's rows.  One workgroup per (segment,
+// chunk): wave w sums rows [16 w, 16 w + 16) with lane = head (heads in blocks of 64), so that
+// each load of dt is one contiguous row and each wave's chain of loads and softplus is a
+// quarter of the chunk; wave 0 adds the four partial sums in row order.
+constexpr int kSumRows = kQ / 4;
+
+// Batches of at most this many sequences get their sequence and segment tables from the
+// chunk-sum launch (one launch fewer); larger ones from the segment-table kernel first.
+constexpr int kTableSeqs = 256;
+
+// Segment `seg` of a batch of S <= 256 sequences (row offsets cu[0..S]) cut into segments of
+// L rows aligned to each sequence's first row, the sequences' segments numbered in order:
+// (sequence, first row, rows, index in its sequence), as the segment-table kernel writes it.
+// One thread per sequence; with `write` the workgroup also stores both tables.
+__device__ int4 own_segment(const int32_t* __restrict__ cu, int S, int L, int seg, int2* __restrict__ seq_info,
+                            int4* __restrict__ seg_info, bool write) {
+  __shared__ int wsum[4];
+  __shared__ int4 found;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int c0 = 0, len = 0, n = 0;
+  if (t < S) {
+    c0 = cu[t];
+    len = cu[t + 1] - c0;
+    n = (len + L - 1) / L;
+  }
+  int incl = n;  // inclusive prefix sum of the segment counts over the sequences
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  if (t == 0) found = make_int4(0, 0, 0, 0);  // an empty segment unless a sequence claims it
+  __syncthreads();
+  for (int i = 0; i < w; ++i) incl += wsum[i];
+  const int first = incl - n;
+  if (t < S && seg >= first && seg < first + n) {
+    const int k = seg - first;
+    found = make_int4(t, c0 + k * L, min(L, len - k * L), k);
+  }
+  if (write && t < S) {
+    seq_info[t] = make_int2(first, n);
+    for (int k = 0; k < n; ++k) seg_info[first + k] = make_int4(t, c0 + k * L, min(L, len - k * L), k);
+  }
+  __syncthreads();
+  return found;
+}
+
+template <bool kTables>
 __global__ __launch_bounds__(256) void chunk_sums_kernel(const bf16_t* __restrict__ dt,
                                                          const float* __restrict__ a_log,
                                                          const float* __restrict__ dt_bias, SegPtrs sp, int H,
-                                                         int cpb) {
+                                                         int cpb, const int32_t* __restrict__ cu, int S,
+                                                         int seg_len, int2* __restrict__ seq_out,
+                                                         int4* __restrict__ seg_out) {
+  __shared__ float part[4][64];
   const int seg = blockIdx.x / cpb;
   // wave-uniform (the buffer descriptor built from it must be, or each load becomes a loop)
-  const int q = uniform((int)(blockIdx.x % cpb) * 4 + ((int)threadIdx.x >> 6)), lane = threadIdx.x & 63;
-  const int4 si0 = sp.seg_info[seg];
+  const int q = uniform((int)(blockIdx.x % cpb));
+  const int w = uniform((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int4 si0 = kTables ? own_segment(cu, S, seg_len, seg, seq_out, seg_out, blockIdx.x == 0) : sp.seg_info[seg];
   const int4 si = make_int4(uniform(si0.x), uniform(si0.y), uniform(si0.z), uniform(si0.w));
-  if (q * kQ >= si.z) return;  // wave-uniform; no barriers
+  if (q * kQ >= si.z) return;  // uniform over the workgroup; no barrier reached yet
   const int nr = min(kQ, si.z - q * kQ);
+  const int r0 = w * kSumRows;
   // rows past the chunk's end read as zero and are not summed; lanes past H are unused
   const Rsrc r = make_rsrc(dt + (size_t)(si.y + q * kQ) * H, (int64_t)nr * H * 2);
-  for (int hb = 0; hb < H; hb += 64) {
+  for (int hb = 0; hb < H; hb += 64) {  // same trip count in every wave
     const int h = hb + lane;
     const float A = h < H ? __expf(a_log[h]) : 0.f, bias = h < H ? dt_bias[h] : 0.f;
-    uint32_t b[kQ];  // every row's load in flight before the first is used
+    uint32_t b[kSumRows];  // every row's load in flight before the first is used
 #pragma unroll
-    for (int i = 0; i < kQ; ++i) b[i] = __builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)((i * H + h) * 2), 0, 0);
+    for (int i = 0; i < kSumRows; ++i)
+      b[i] = __builtin_amdgcn_raw_buffer_load_b16(r, (uint32_t)(((r0 + i) * H + h) * 2), 0, 0);
     float sum = 0.f;
 #pragma unroll
-    for (int i = 0; i < kQ; ++i)
-      if (i < nr) sum += -A * softplus_f32(bf16_to_f32(b[i]) + bias);
-    if (h < H) sp.seg_chunk[((size_t)seg * kMaxSegChunks + q) * H + h] = sum;
+    for (int i = 0; i < kSumRows; ++i)
+      if (r0 + i < nr) sum += -A * softplus_f32(bf16_to_f32(b[i]) + bias);
+    part[w][lane] = sum;
+    __syncthreads();
+    if (w == 0 && h < H)
+      sp.seg_chunk[((size_t)seg * kMaxSegChunks + q) * H + h] =
+          ((part[0][lane] + part[1][lane]) + part[2][lane]) + part[3][lane];
+    __syncthreads();  // the partial sums are read before the next block of heads overwrites them
   }
 }
 
@@ -899,9 +955,19 @@ hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t st) {
   const int nitems = (int)(a.lay.nseg * (d.nheads / kHeadsPerBlock));
   if (nitems == 0) return hipSuccess;
   if (a.lay.seg_len > kMaxSegChunks * kQ) return hipErrorInvalidValue;  // the chunk-sum table
-  const int cpb = (a.lay.seg_len + 4 * kQ - 1) / (4 * kQ);  // workgroups of four chunks per segment
-  M2_LAUNCH("chunk_sums", chunk_sums_kernel, dim3((unsigned)(a.lay.nseg * cpb)), dim3(256), 0, st,
-            (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, cpb);
+  const int cpb = (a.lay.seg_len + kQ - 1) / kQ;  // one workgroup per chunk of a segment
+  const dim3 sums_grid((unsigned)(a.lay.nseg * cpb));
+  int2* seq_out = (int2*)(a.ws + a.lay.off_seq_info);
+  int4* seg_out = (int4*)(a.ws + a.lay.off_seg_info);
+  if (a.bd.num_seqs <= kTableSeqs) {
+    M2_LAUNCH("chunk_sums", chunk_sums_kernel<true>, sums_grid, dim3(256), 0, st, (const bf16_t*)a.dt, a.a_log,
+              a.dt_bias, sp, d.nheads, cpb, a.bd.cu_seqlens, a.bd.num_seqs, a.lay.seg_len, seq_out, seg_out);
+  } else {
+    hipError_t e = launch_scan_setup(a, st);
+    if (e != hipSuccess) return e;
+    M2_LAUNCH("chunk_sums", chunk_sums_kernel<false>, sums_grid, dim3(256), 0, st, (const bf16_t*)a.dt, a.a_log,
+              a.dt_bias, sp, d.nheads, cpb, a.bd.cu_seqlens, a.bd.num_seqs, a.lay.seg_len, seq_out, seg_out);
+  }
   M2_LAUNCH("ssd_state", ssd_state_kernel, dim3((unsigned)nitems), dim3(256), 0, st, (const bf16_t*)a.xbc,
             (const bf16_t*)a.dt, a.a_log, a.dt_bias, sp, d.nheads, d.ngroups, nitems);
   hipError_t e = launch_scan_pass(a, st);

@@ -188,6 +188,23 @@ def test_random_ragged_batches(gpu, seed):
     _prefill_parity(gpu, wl)
 
 
+@pytest.mark.parametrize("S", [256, 257, 300])
+def test_many_sequences(gpu, S):
+    """Batches of S sequences on the MFMA path's shapes, around the size up to which the
+    chunk-sum launch builds the sequence and segment tables itself (256; beyond it the table
+    kernel runs first): mostly 1 to 40 rows, five of 200 to 700 rows (several segments each),
+    random fresh flags over dirty slots of a 320-slot pool; every op against the oracle."""
+    rng = np.random.default_rng(950 + S)
+    lens = [int(v) for v in rng.integers(1, 41, S)]
+    for i in rng.permutation(S)[:5]:
+        lens[int(i)] = int(rng.integers(200, 701))
+    sh = W.Shape(nheads=8, headdim=64, d_state=128, ngroups=1, conv_kernel=4, chunk_size=256, norm_groups=2,
+                 pool_slots=320, act="bf16")
+    wl = W.random_prefill(960 + S, sh, lens, fresh=[int(v) for v in rng.integers(0, 2, S)],
+                          slots=[int(v) for v in rng.permutation(320)[:S]])
+    _prefill_parity(gpu, wl)
+
+
 def test_decode_64_steps(gpu):
     """256 one-row requests on 512 slots, 10% fresh over dirty slots, 64 successive steps.
     Each step: conv on the step's rows (both sides), the decode scan on the GPU's conv output,
