@@ -107,6 +107,52 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Batches of at most this many sequences get their sequence and segment tables from the first
+// launch that reads them (one launch fewer); larger ones from the segment-table kernel.
+constexpr int kTableSeqs = 256;
+
+// Segment `seg` of a batch of S <= kThreads sequences (row offsets cu[0..S]) cut into segments
+// of L rows aligned to each sequence's first row, the sequences' segments numbered in order:
+// (sequence, first row, rows, index in its sequence), as the segment-table kernel writes it;
+// an empty segment when no sequence has one of that number.  One thread per sequence, every
+// thread of the kThreads-thread workgroup taking part (two barriers); with `write` the
+// workgroup also stores both tables (seq_info: first segment, segments).
+template <int kThreads>
+__device__ int4 own_segment(const int32_t* __restrict__ cu, int S, int L, int seg, int2* __restrict__ seq_info,
+                            int4* __restrict__ seg_info, bool write) {
+  static_assert(kThreads % 64 == 0 && kThreads <= 1024, "whole waves");
+  __shared__ int wsum[kThreads / 64];
+  __shared__ int4 found;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int c0 = 0, len = 0, n = 0;
+  if (t < S) {
+    c0 = cu[t];
+    len = cu[t + 1] - c0;
+    n = (len + L - 1) / L;
+  }
+  int incl = n;  // inclusive prefix sum of the segment counts over the sequences
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wsum[w] = incl;
+  if (t == 0) found = make_int4(0, 0, 0, 0);
+  __syncthreads();
+  for (int i = 0; i < w; ++i) incl += wsum[i];
+  const int first = incl - n;
+  if (t < S && seg >= first && seg < first + n) {
+    const int k = seg - first;
+    found = make_int4(t, c0 + k * L, min(L, len - k * L), k);
+  }
+  if (write && t < S) {
+    seq_info[t] = make_int2(first, n);
+    for (int k = 0; k < n; ++k) seg_info[first + k] = make_int4(t, c0 + k * L, min(L, len - k * L), k);
+  }
+  __syncthreads();
+  return found;
+}
+
 // ------------------------------------------------------- chunked scan workspace
 //
 // Sequences are cut into segments of at most seg_len rows (aligned to each

@@ -143,14 +143,19 @@ struct M3Ptrs {
 
 // grid (chunk, head block of kAngHeads), 256 threads: theta = tanh(angles) pi for the chunk's
 // rows and the block's dt in LDS; then per (head, pair) the chunk's sum of theta dt, in double,
-// stored reduced into [0, 2 pi).
+// stored reduced into [0, 2 pi).  kTables (at most 256 sequences): each workgroup finds its
+// chunk from the row offsets and the first one stores the chunk tables for the later launches.
 constexpr int kAngHeads = 8;
-__global__ __launch_bounds__(256) void m3_angle_totals_kernel(M3Ptrs P, int nch) {
+template <bool kTables>
+__global__ __launch_bounds__(256) void m3_angle_totals_kernel(M3Ptrs P, int nch, const int32_t* __restrict__ cu,
+                                                              int S, int2* __restrict__ seq_out,
+                                                              int4* __restrict__ chunk_out) {
   __shared__ float sTh[kC][kMaxNA + 1];
   __shared__ float sDt[kC][65];
   const int c = blockIdx.x;
-  if (c >= nch) return;
-  const int4 ci = P.chunk_info[c];
+  if (c >= nch) return;  // uniform over the workgroup
+  const int4 ci = kTables ? own_segment<256>(cu, S, kC, c, seq_out, chunk_out, blockIdx.x == 0 && blockIdx.y == 0)
+                          : P.chunk_info[c];
   for (int e = threadIdx.x; e < kC * P.NA; e += blockDim.x) {
     const int j = e / P.NA, a = e - j * P.NA;
     sTh[j][a] = j < ci.z ? tanhf(bf(P.angles + (size_t)(ci.y + j) * P.NA + a)) : 0.f;
@@ -842,11 +847,22 @@ hipError_t launch_mamba3_forward(const M3Args& a, const M3Layout& lay, char* ws,
   P.T = (int)a.num_rows;
   const int S = a.num_seqs;
   const int nch = (int)lay.nch;
-  hipError_t e = launch_segment_tables(a.cu_seqlens, S, kC, (int2*)(ws + lay.off_seq), (int4*)(ws + lay.off_chunk), st);
-  if (e != hipSuccess) return e;
+  int2* seq_out = (int2*)(ws + lay.off_seq);
+  int4* chunk_out = (int4*)(ws + lay.off_chunk);
+  const bool own_tables = P.NA > 0 && S <= kTableSeqs;  // the angle-totals launch builds them
+  if (!own_tables) {
+    hipError_t e = launch_segment_tables(a.cu_seqlens, S, kC, seq_out, chunk_out, st);
+    if (e != hipSuccess) return e;
+  }
   if (P.NA > 0) {
-    M2_LAUNCH("m3_angle_totals", m3_angle_totals_kernel, dim3((unsigned)nch, (unsigned)((P.H + kAngHeads - 1) / kAngHeads)),
-              dim3(256), 0, st, P, nch);
+    const dim3 ag((unsigned)nch, (unsigned)((P.H + kAngHeads - 1) / kAngHeads));
+    if (own_tables) {
+      M2_LAUNCH("m3_angle_totals", m3_angle_totals_kernel<true>, ag, dim3(256), 0, st, P, nch, a.cu_seqlens, S,
+                seq_out, chunk_out);
+    } else {
+      M2_LAUNCH("m3_angle_totals", m3_angle_totals_kernel<false>, ag, dim3(256), 0, st, P, nch, a.cu_seqlens, S,
+                seq_out, chunk_out);
+    }
     M2_LAUNCH("m3_angle_prefix", m3_angle_prefix_kernel, dim3((unsigned)S, (unsigned)((P.H * P.NA + 255) / 256)),
               dim3(256), 0, st, P, S);
   }

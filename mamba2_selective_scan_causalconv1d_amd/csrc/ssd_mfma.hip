@@ -485,48 +485,6 @@ __device__ __forceinline__ void walk_local_state(f32x4 (&S)[2][8], const bf16_t*
 // quarter of the chunk; wave 0 adds the four partial sums in row order.
 constexpr int kSumRows = kQ / 4;
 
-// Batches of at most this many sequences get their sequence and segment tables from the
-// chunk-sum launch (one launch fewer); larger ones from the segment-table kernel first.
-constexpr int kTableSeqs = 256;
-
-// Segment `seg` of a batch of S <= 256 sequences (row offsets cu[0..S]) cut into segments of
-// L rows aligned to each sequence's first row, the sequences' segments numbered in order:
-// (sequence, first row, rows, index in its sequence), as the segment-table kernel writes it.
-// One thread per sequence; with `write` the workgroup also stores both tables.
-__device__ int4 own_segment(const int32_t* __restrict__ cu, int S, int L, int seg, int2* __restrict__ seq_info,
-                            int4* __restrict__ seg_info, bool write) {
-  __shared__ int wsum[4];
-  __shared__ int4 found;
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  int c0 = 0, len = 0, n = 0;
-  if (t < S) {
-    c0 = cu[t];
-    len = cu[t + 1] - c0;
-    n = (len + L - 1) / L;
-  }
-  int incl = n;  // inclusive prefix sum of the segment counts over the sequences
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) wsum[w] = incl;
-  if (t == 0) found = make_int4(0, 0, 0, 0);  // an empty segment unless a sequence claims it
-  __syncthreads();
-  for (int i = 0; i < w; ++i) incl += wsum[i];
-  const int first = incl - n;
-  if (t < S && seg >= first && seg < first + n) {
-    const int k = seg - first;
-    found = make_int4(t, c0 + k * L, min(L, len - k * L), k);
-  }
-  if (write && t < S) {
-    seq_info[t] = make_int2(first, n);
-    for (int k = 0; k < n; ++k) seg_info[first + k] = make_int4(t, c0 + k * L, min(L, len - k * L), k);
-  }
-  __syncthreads();
-  return found;
-}
-
 template <bool kTables>
 __global__ __launch_bounds__(256) void chunk_sums_kernel(const bf16_t* __restrict__ dt,
                                                          const float* __restrict__ a_log,
@@ -539,7 +497,7 @@ __global__ __launch_bounds__(256) void chunk_sums_kernel(const bf16_t* __restric
   // wave-uniform (the buffer descriptor built from it must be, or each load becomes a loop)
   const int q = uniform((int)(blockIdx.x % cpb));
   const int w = uniform((int)threadIdx.x >> 6), lane = threadIdx.x & 63;
-  const int4 si0 = kTables ? own_segment(cu, S, seg_len, seg, seq_out, seg_out, blockIdx.x == 0) : sp.seg_info[seg];
+  const int4 si0 = kTables ? own_segment<256>(cu, S, seg_len, seg, seq_out, seg_out, blockIdx.x == 0) : sp.seg_info[seg];
   const int4 si = make_int4(uniform(si0.x), uniform(si0.y), uniform(si0.z), uniform(si0.w));
   if (q * kQ >= si.z) return;  // uniform over the workgroup; no barrier reached yet
   const int nr = min(kQ, si.z - q * kQ);

@@ -111,6 +111,18 @@ def test_mamba3_many_chunks_per_workgroup(gpu):
                                  name="mamba3_many_chunks_128x64"))
 
 
+@pytest.mark.parametrize("S", [256, 257, 300])
+def test_mamba3_many_sequences(gpu, S):
+    """Batches of S short sequences (1 to 20 rows, five of 65 to 200) around the size up to
+    which the angle-totals launch builds the chunk tables itself (256; beyond it the table
+    kernel runs first)."""
+    rng = np.random.default_rng(1700 + S)
+    lens = [int(v) for v in rng.integers(1, 21, S)]
+    for i in rng.permutation(S)[:5]:
+        lens[int(i)] = int(rng.integers(65, 201))
+    compare(gpu, W.mamba3_varlen(1800 + S, lengths=lens, H=2, DK=16, DV=16, NA=4, name="mamba3_%d_seqs" % S))
+
+
 def test_mamba3_rejections(gpu):
     """Misaligned outputs, a short workspace, a value width the tiles do not cover: refused
     before any launch, nothing written."""
