@@ -187,30 +187,22 @@ __global__ __launch_bounds__(256) void conv1d_silu_kernel(
 }
 
 // Every sequence one row (a decode step: S == T, so row r is sequence r): one thread per
-// 16-byte channel vector of a row.  The slot's K-1 rows and the new row are read
-// together, the output is the window's dot product, and the slot is rewritten shifted
-// by one row.  No sequence lookup, so the only dependent load is the slot index.
+// 16-byte channel vector of a row, one wave per 64 vectors of a row (grid x), rows over grid y
+// (strided past the grid's y limit), so the row's slot index and fresh flag are uniform
+// scalar loads and no lane divides by the row width.  The slot's K-1 rows and the new row
+// are read together, the output is the window's dot product, and the slot is rewritten
+// shifted by one row.  The only dependent load is the slot's rows, after the slot index.
 template <typename T, int K>
-__global__ __launch_bounds__(256) void conv1d_silu_step_kernel(
+__global__ __launch_bounds__(64) void conv1d_silu_step_kernel(
     T* __restrict__ dst, const T* __restrict__ x, const float* __restrict__ w,
     const float* __restrict__ b, T* __restrict__ conv_state, const int32_t* __restrict__ slots,
     const uint8_t* __restrict__ fresh, int S, int Dc) {
   constexpr int V = Act<T>::kVec;
   constexpr int H1 = K - 1;
   const int NV = Dc / V;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= (int64_t)S * NV) return;
-  const int r = (int)(gid / NV);
-  const size_t col = (size_t)(gid % NV) * V;
-  uint4 raw[K];
-  raw[H1] = *reinterpret_cast<const uint4*>(x + (size_t)r * Dc + col);
-  const size_t sbase = (size_t)slots[r] * H1 * Dc + col;
-#pragma unroll
-  for (int i = 0; i < H1; ++i) raw[i] = make_uint4(0, 0, 0, 0);
-  if (!fresh[r]) {  // a fresh sequence never reads its slot
-#pragma unroll
-    for (int i = 0; i < H1; ++i) raw[i] = *reinterpret_cast<const uint4*>(conv_state + sbase + (size_t)i * Dc);
-  }
+  const int vec = blockIdx.x * 64 + threadIdx.x;
+  if (vec >= NV) return;
+  const size_t col = (size_t)vec * V;
   // weights of this thread's channels: V * K contiguous floats starting at col * K
   float wr[V * K];
   const float4* wp = reinterpret_cast<const float4*>(w + col * K);
@@ -232,20 +224,31 @@ __global__ __launch_bounds__(256) void conv1d_silu_step_kernel(
     br[4 * i + 2] = t4.z;
     br[4 * i + 3] = t4.w;
   }
+  for (int r = blockIdx.y; r < S; r += gridDim.y) {
+    uint4 raw[K];
+    raw[H1] = *reinterpret_cast<const uint4*>(x + (size_t)r * Dc + col);
+    const size_t sbase = (size_t)slots[r] * H1 * Dc + col;
 #pragma unroll
-  for (int i = 0; i < H1; ++i) *reinterpret_cast<uint4*>(conv_state + sbase + (size_t)i * Dc) = raw[i + 1];
-  float win[K][V];
+    for (int i = 0; i < H1; ++i) raw[i] = make_uint4(0, 0, 0, 0);
+    if (!fresh[r]) {  // a fresh sequence never reads its slot
 #pragma unroll
-  for (int k = 0; k < K; ++k) Act<T>::unpack(raw[k], win[k]);
-  float out[V];
+      for (int i = 0; i < H1; ++i) raw[i] = *reinterpret_cast<const uint4*>(conv_state + sbase + (size_t)i * Dc);
+    }
 #pragma unroll
-  for (int i = 0; i < V; ++i) {
-    float pre = br[i];
+    for (int i = 0; i < H1; ++i) *reinterpret_cast<uint4*>(conv_state + sbase + (size_t)i * Dc) = raw[i + 1];
+    float win[K][V];
 #pragma unroll
-    for (int k = 0; k < K; ++k) pre = fmaf(wr[i * K + k], win[k][i], pre);
-    out[i] = silu_f32(pre);
+    for (int k = 0; k < K; ++k) Act<T>::unpack(raw[k], win[k]);
+    float out[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) {
+      float pre = br[i];
+#pragma unroll
+      for (int k = 0; k < K; ++k) pre = fmaf(wr[i * K + k], win[k][i], pre);
+      out[i] = silu_f32(pre);
+    }
+    *reinterpret_cast<uint4*>(dst + (size_t)r * Dc + col) = Act<T>::pack(out);
   }
-  *reinterpret_cast<uint4*>(dst + (size_t)r * Dc + col) = Act<T>::pack(out);
 }
 
 template <typename T, int K>
@@ -254,9 +257,9 @@ hipError_t launch_t(void* dst, const void* x, const float* w, const float* b, vo
   constexpr int V = Act<T>::kVec;
   const int NV = Dc / V;
   if (bd.num_rows == bd.num_seqs) {
-    const int64_t n = (int64_t)bd.num_seqs * NV;
-    M2_LAUNCH("conv1d_silu", (conv1d_silu_step_kernel<T, K>), dim3((unsigned)((n + 255) / 256)), dim3(256), 0,
-              st, (T*)dst, (const T*)x, w, b, (T*)cs, bd.slots, bd.fresh, bd.num_seqs, Dc);
+    const dim3 grid((unsigned)((NV + 63) / 64), (unsigned)(bd.num_seqs < 65535 ? bd.num_seqs : 65535));
+    M2_LAUNCH("conv1d_silu", (conv1d_silu_step_kernel<T, K>), grid, dim3(64), 0, st, (T*)dst, (const T*)x, w, b,
+              (T*)cs, bd.slots, bd.fresh, bd.num_seqs, Dc);
     return hipSuccess;
   }
   const int64_t work = (int64_t)bd.num_rows * NV;

@@ -9,9 +9,11 @@
 // L = 64 / groups lanes, and its 16-byte vectors are dealt to those lanes round robin,
 // so every load instruction touches whole 128-byte lines and the group's sum of squares
 // is a DPP / swizzle reduction over L lanes.  The weights are loaded before the reduction.
-// Four rows per workgroup, rows streamed with non-temporal accesses; a launch of fewer than
-// 4096 rows (a decode step) uses one-wave workgroups and plain accesses.  Shapes that do not fit (groups not dividing 64, rows
-// not a multiple of 64 vectors) use the unit kernel: one wavefront per (row, group).
+// Four rows per workgroup, rows streamed with non-temporal accesses.  A launch of fewer than
+// 4096 rows (a decode step) is latency-bound: it takes one workgroup per row whose waves share
+// the row's vectors (each lane gates one vector), the waves' group sums added in wave order
+// through LDS.  Shapes that do not fit (groups not dividing 64, rows not a multiple of 64
+// vectors) use the unit kernel: one wavefront per (row, group).
 #include "common.h"
 
 namespace m2 {
@@ -112,10 +114,10 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_wide_kernel(T* __restrict__
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // The weight vectors are loaded before the row's reduction, so each wave waits on one round of
-// loads instead of two (203 -> 198 us on a 65536 x 3072 launch).  kShort: a short launch (few
-// rows) uses plain accesses; otherwise the rows are streamed: x, z and dst use non-temporal
-// accesses (each byte is touched once), which keeps the stream from displacing cached data.
-template <typename T, int NVPL, bool kShort>
+// loads instead of two (203 -> 198 us on a 65536 x 3072 launch).  The rows are streamed: x, z
+// and dst use non-temporal accesses (each byte is touched once), which keeps the stream from
+// displacing cached data.
+template <typename T, int NVPL>
 __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ dst, const T* __restrict__ x,
                                                                 const T* __restrict__ z,
                                                                 const float* __restrict__ w, int lanes_per_group,
@@ -145,7 +147,6 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ 
 #pragma unroll
   for (int k = 0; k < NVPL; ++k) load_w(k);
   auto load_row = [&](const T* p) -> uint4 {
-    if (kShort) return *reinterpret_cast<const uint4*>(p);
     const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
   };
@@ -172,12 +173,57 @@ __global__ __launch_bounds__(256) void gated_rmsnorm_row_kernel(T* __restrict__ 
 #pragma unroll
     for (int i = 0; i < V; ++i) out[i] = g[k][i] * inv * wf[k][i];
     const uint4 pv = Act<T>::pack(out);
-    if (kShort) {
-      *reinterpret_cast<uint4*>(dst + base + (size_t)vi * V) = pv;
-    } else {
-      __builtin_nontemporal_store(u32x4{pv.x, pv.y, pv.z, pv.w}, reinterpret_cast<u32x4*>(dst + base + (size_t)vi * V));
-    }
+    __builtin_nontemporal_store(u32x4{pv.x, pv.y, pv.z, pv.w}, reinterpret_cast<u32x4*>(dst + base + (size_t)vi * V));
   }
+}
+
+// A row per workgroup of NVPL waves (few rows): lane slot (q, jl) of wave k holds the vector
+// that the row kernel's lane holds as its k-th, so the lanes of a group are the same and
+// every wave's group sum is a reduction over them; the NVPL sums go through LDS and are added
+// in wave order (the same order in every lane of the group).
+template <typename T, int NVPL>
+__global__ __launch_bounds__(64 * NVPL) void gated_rmsnorm_split_kernel(T* __restrict__ dst, const T* __restrict__ x,
+                                                                       const T* __restrict__ z,
+                                                                       const float* __restrict__ w,
+                                                                       int lanes_per_group, int log2_lpg, float eps,
+                                                                       float inv_gs, int Di) {
+  constexpr int V = Act<T>::kVec;
+  __shared__ float part[NVPL][64];
+  const int lane = threadIdx.x & 63;
+  const int k = threadIdx.x >> 6;
+  const int q = lane >> log2_lpg;
+  const int jl = lane & (lanes_per_group - 1);
+  const int vi = q * NVPL * lanes_per_group + jl + lanes_per_group * k;
+  const size_t at = (size_t)blockIdx.x * Di + (size_t)vi * V;
+  float wf[V], xf[V], zf[V];
+  const float4* wp = reinterpret_cast<const float4*>(w + (size_t)vi * V);
+#pragma unroll
+  for (int i = 0; i < V / 4; ++i) {
+    const float4 t4 = wp[i];
+    wf[4 * i] = t4.x;
+    wf[4 * i + 1] = t4.y;
+    wf[4 * i + 2] = t4.z;
+    wf[4 * i + 3] = t4.w;
+  }
+  Act<T>::unpack(*reinterpret_cast<const uint4*>(x + at), xf);
+  Act<T>::unpack(*reinterpret_cast<const uint4*>(z + at), zf);
+  float g[V];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < V; ++i) {
+    g[i] = xf[i] * silu_f32(zf[i]);
+    ss = fmaf(g[i], g[i], ss);
+  }
+  part[k][lane] = group_sum(ss, lanes_per_group);
+  __syncthreads();
+  float tot = part[0][lane];
+#pragma unroll
+  for (int j = 1; j < NVPL; ++j) tot += part[j][lane];
+  const float inv = rsqrtf(tot * inv_gs + eps);
+  float out[V];
+#pragma unroll
+  for (int i = 0; i < V; ++i) out[i] = g[i] * inv * wf[i];
+  *reinterpret_cast<uint4*>(dst + at) = Act<T>::pack(out);
 }
 
 template <typename T, int NVPL>
@@ -188,13 +234,13 @@ hipError_t launch_row(void* dst, const void* x, const void* z, const float* w, i
   while ((1 << log2_lpg) < lpg) ++log2_lpg;
   const float inv_gs = 1.f / (float)(Di / groups);
   if (rows < 4096) {
-    // few rows (a decode step): one wave per workgroup
-    M2_LAUNCH("gated_rmsnorm", (gated_rmsnorm_row_kernel<T, NVPL, true>), dim3((unsigned)rows), dim3(64), 0, st,
-              (T*)dst, (const T*)x, (const T*)z, w, lpg, log2_lpg, eps, inv_gs, rows, Di);
+    // few rows (a decode step): a workgroup of NVPL waves per row
+    M2_LAUNCH("gated_rmsnorm", (gated_rmsnorm_split_kernel<T, NVPL>), dim3((unsigned)rows), dim3(64 * NVPL), 0, st,
+              (T*)dst, (const T*)x, (const T*)z, w, lpg, log2_lpg, eps, inv_gs, Di);
     return hipSuccess;
   }
   const dim3 grid((unsigned)((rows + 3) / 4));
-  M2_LAUNCH("gated_rmsnorm", (gated_rmsnorm_row_kernel<T, NVPL, false>), grid, dim3(256), 0, st, (T*)dst,
+  M2_LAUNCH("gated_rmsnorm", (gated_rmsnorm_row_kernel<T, NVPL>), grid, dim3(256), 0, st, (T*)dst,
             (const T*)x, (const T*)z, w, lpg, log2_lpg, eps, inv_gs, rows, Di);
   return hipSuccess;
 }
