@@ -293,6 +293,43 @@ def test_decode_shapes(gpu, shape):
     _check_pools(wl, wl.slots, gpu.ops.to_host(sp_g), sp_o, gpu.ops.to_host(cp_g), cp_o)
 
 
+def test_decode_past_grid_limit_and_unaligned_flags(gpu):
+    """A decode step of 65,600 one-row requests in a tiny fp32 shape (more rows than a grid
+    dimension holds: the conv step strides over its rows; the decode scan's item map deals
+    262,400 items over the XCDs), with the fresh flags at an odd byte offset of a larger buffer;
+    every op against the oracle on the same inputs, pools carried by each side."""
+    sh = DECODE_SHAPES["f32_p16n16"]
+    R = 65600
+    sh = W.Shape(sh.nheads, sh.headdim, sh.d_state, sh.ngroups, sh.conv_kernel, sh.chunk_size, sh.norm_groups,
+                 R + 7, sh.act)
+    bar = bar_for(sh.act)
+    wl = W.random_prefill(66, sh, [1] * R)
+    p = gpu.Params(wl)
+    dims = gpu.dims_of(sh)
+    b = gpu.batch_of(wl)
+    spill = torch.zeros(R + 3, dtype=torch.uint8, device="cuda")
+    spill[3:] = b.dev_fresh
+    b.c.dev_fresh = spill.data_ptr() + 3
+    cp_g, sp_g = gpu.ops.to_device(wl.conv_pool), gpu.ops.to_device(wl.ssm_pool)
+    x = gpu.ops.to_device(wl.xbc)
+    xa = torch.empty_like(x)
+    gpu.ops.conv1d(xa, x, p.conv_w, p.conv_b, cp_g, b, dims)
+    y = torch.empty((R, sh.d_inner), dtype=x.dtype, device="cuda")
+    gpu.ops.scan_decode(y, xa, gpu.ops.to_device(wl.dt), p.a_log, p.dt_bias, p.D, sp_g, b, dims)
+    torch.cuda.synchronize()
+    xa_h, y_h = gpu.ops.to_host(xa), gpu.ops.to_host(y)
+    xa_o, cp_o = oracle_conv(wl)
+    y_o, sp_o = oracle_scan(wl, xa_h, decode=True)
+    say("  %d requests: conv %.3g, y %.3g of bar" % (
+        R, assert_close(gpu.f32(xa_h), gpu.f32(xa_o), bar, "conv"), assert_close(gpu.f32(y_h), gpu.f32(y_o), bar, "y")))
+    sp_h, cp_h = gpu.ops.to_host(sp_g), gpu.ops.to_host(cp_g)
+    named = np.asarray(wl.slots)
+    assert_close(sp_h[named], sp_o[named], F32_BAR, "ssm slots")
+    assert np.array_equal(cp_h[named], cp_o[named]), "conv slots"
+    rest = np.setdiff1d(np.arange(sh.pool_slots), named)
+    assert sp_h[rest].tobytes() == wl.ssm_pool[rest].tobytes() and cp_h[rest].tobytes() == wl.conv_pool[rest].tobytes()
+
+
 # ------------------------------------------------------------ invariants and edge cases
 
 SMALL = W.Shape(nheads=4, headdim=8, d_state=8, ngroups=2, conv_kernel=4, chunk_size=16, norm_groups=2,
