@@ -141,10 +141,15 @@ __global__ __launch_bounds__(256) void scan_verify_kernel(
     const float* __restrict__ a_log, const float* __restrict__ dt_bias,
     const float* __restrict__ Dp, float* __restrict__ pool, float* __restrict__ snaps,
     const int32_t* __restrict__ cu, const int32_t* __restrict__ slots, const uint8_t* __restrict__ fresh,
-    int H, int P, int N, int G, int nblk) {
+    int S, int H, int P, int N, int G, int nblk) {
   extern __shared__ float lds[];
-  const int hb = blockIdx.x % (H * nblk);
-  const int r = blockIdx.x / (H * nblk);
+  // (sequence, head, block) items in XCD-contiguous order, as in the one-row kernel
+  const int J = H * nblk;
+  const int nitems = S * J;
+  const int b = blockIdx.x, xcd = b & 7;
+  const int item = xcd * (nitems >> 3) + min(xcd, nitems & 7) + (b >> 3);
+  const int r = item / J;
+  const int hb = item - r * J;
   const int h = hb / nblk;
   const int blk = hb - h * nblk;
   const int tid = threadIdx.x;
@@ -307,11 +312,11 @@ hipError_t launch_verify_t(void* y, const void* xbc, const void* dt, const float
   const size_t shmem = (size_t)max_rows * (2 * dm.d_state + rb + 2) * sizeof(float);
   if (sh.kp == 2) {
     M2_LAUNCH("scan_verify", (scan_verify_kernel<T, 2>), grid, dim3(sh.nthr), shmem, st, (T*)y, (const T*)xbc,
-              (const T*)dt, a_log, dt_bias, D, pool, snaps, bd.cu_seqlens, bd.slots, bd.fresh, dm.nheads,
+              (const T*)dt, a_log, dt_bias, D, pool, snaps, bd.cu_seqlens, bd.slots, bd.fresh, bd.num_seqs, dm.nheads,
               dm.headdim, dm.d_state, dm.ngroups, sh.nblk);
   } else {
     M2_LAUNCH("scan_verify", (scan_verify_kernel<T, 1>), grid, dim3(sh.nthr), shmem, st, (T*)y, (const T*)xbc,
-              (const T*)dt, a_log, dt_bias, D, pool, snaps, bd.cu_seqlens, bd.slots, bd.fresh, dm.nheads,
+              (const T*)dt, a_log, dt_bias, D, pool, snaps, bd.cu_seqlens, bd.slots, bd.fresh, bd.num_seqs, dm.nheads,
               dm.headdim, dm.d_state, dm.ngroups, sh.nblk);
   }
   return hipSuccess;
