@@ -650,6 +650,18 @@ def run_padded(torch, ops, W, dev, e0, e1):
         us = e0.elapsed_time(e1) / 20 * 1e3
         res[name + "_us"] = us
         res[name + "_GBs"] = nbytes / (us * 1e-6) / 1e9
+        # GPU time of the launches alone (HIP events around each launch): the calls above
+        # include the host's per-call cost, which the short launches do not cover
+        ops.timing_enable(64)
+        per_call = []
+        for _ in range(5):
+            fn()
+            torch.cuda.synchronize()
+            per_call.append(1e3 * sum(ms for _, ms in ops.timing_collect(64)))
+        ops.timing_enable(0)
+        kus = float(np.median(per_call))
+        res[name + "_kernel_us"] = kus
+        res[name + "_kernel_GBs"] = nbytes / (kus * 1e-6) / 1e9
     return res
 
 
