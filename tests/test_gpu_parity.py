@@ -205,6 +205,31 @@ def test_many_sequences(gpu, S):
     _prefill_parity(gpu, wl)
 
 
+GENERIC_SHAPES = {
+    # the VALU chunked scan (fp32, and bf16 shapes off the MFMA path) stages 64-wide tiles:
+    # these cover several n tiles, several p tiles with a partial last one, N not a multiple
+    # of 64, three heads per group, and chunks of 48 and 64 rows
+    "f32_p64n128": W.Shape(nheads=4, headdim=64, d_state=128, ngroups=2, conv_kernel=4, chunk_size=64,
+                           norm_groups=2, pool_slots=8, act="f32"),
+    "f32_p96n200": W.Shape(nheads=2, headdim=96, d_state=200, ngroups=1, conv_kernel=3, chunk_size=48,
+                           norm_groups=2, pool_slots=8, act="f32"),
+    "bf16_3hpg": W.Shape(nheads=6, headdim=64, d_state=128, ngroups=2, conv_kernel=4, chunk_size=256,
+                         norm_groups=2, pool_slots=8, act="bf16"),
+    "bf16_p128n64": W.Shape(nheads=2, headdim=128, d_state=64, ngroups=1, conv_kernel=4, chunk_size=256,
+                            norm_groups=1, pool_slots=8, act="bf16"),
+}
+
+
+@pytest.mark.parametrize("shape", list(GENERIC_SHAPES))
+def test_generic_scan_shapes(gpu, shape):
+    """The VALU chunked scan on shapes of several 64-wide tiles: runs of 1, 47, 64, 150 and 333
+    rows (one chunk, a partial chunk, several chunks), fresh and resumed slots; every op against
+    the oracle, final states and untouched slots."""
+    sh = GENERIC_SHAPES[shape]
+    wl = W.random_prefill(970 + len(shape), sh, [150, 1, 333, 47, 64], fresh=[1, 0, 0, 1, 0], slots=[5, 0, 7, 2, 3])
+    _prefill_parity(gpu, wl)
+
+
 def test_decode_64_steps(gpu):
     """256 one-row requests on 512 slots, 10% fresh over dirty slots, 64 successive steps.
     Each step: conv on the step's rows (both sides), the decode scan on the GPU's conv output,
