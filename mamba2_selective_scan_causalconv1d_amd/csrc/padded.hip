@@ -10,11 +10,12 @@
 // Both are byte copies.  The real rows of a batch row are contiguous in the padded layout as
 // well as in the packed one: packed unit e of batch row b (cu[b] units <= e < cu[b + 1] units,
 // counting row by row) is padded unit e + delta(b), delta(b) = (b Lmax + start(b) - cu[b]) units,
-// start(b) = Lmax - L(b) with left padding, else 0.  pack walks the packed units, unpack the
-// padded ones (zero outside [start(b), start(b) + L(b))), both flat over the whole tensor so the
-// work is spread evenly whatever the run lengths.  Units are 16, 8, 4, 2 or 1 bytes (the largest
-// that divides the row and the pointers), four per thread and step so that four loads are in
-// flight.
+// start(b) = Lmax - L(b) with left padding, else 0.  pack copies each batch row's run as one
+// contiguous span: workgroup (x, b) takes span chunk x of batch row b (grid y over the batch
+// rows, strided past the grid's limit), so the row is a uniform index and no lookup precedes
+// the loads.  unpack walks the padded units flat over the whole tensor (zero outside [start(b),
+// start(b) + L(b))).  Units are 16, 8, 4, 2 or 1 bytes (the largest that divides the row and the
+// pointers), four per thread and step so that four loads are in flight.
 #include "common.h"
 
 namespace m2 {
@@ -23,53 +24,30 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kPer = 4;  // units per thread and step
 
-// Batch row holding packed unit e, from a lower bound b (cu ascending).
-__device__ __forceinline__ int row_of(const int32_t* __restrict__ cu, int b, int64_t e, int64_t units) {
-  while ((int64_t)cu[b + 1] * units <= e) ++b;
-  return b;
-}
-// First batch row whose packed units reach past e (binary search, uniform over the workgroup).
-__device__ __forceinline__ int first_row(const int32_t* __restrict__ cu, int B, int64_t e, int64_t units) {
-  int lo = 0, hi = B - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if ((int64_t)cu[mid + 1] * units <= e) lo = mid + 1;
-    else hi = mid;
-  }
-  return lo;
-}
-
-// Offset from packed unit e to its padded unit in batch row b.
-__device__ __forceinline__ int64_t pack_delta(const int32_t* __restrict__ cu, int b, int Lmax, int left,
-                                              int64_t units) {
-  const int L = cu[b + 1] - cu[b];
-  return ((int64_t)b * Lmax + (left ? Lmax - L : 0) - cu[b]) * units;
-}
-
+// Batch row b's run: units [cu[b] units, cu[b + 1] units) of dst from the same count of units of
+// src starting at (b Lmax + start(b)) units.  Workgroup x copies chunks x, x + gridDim.x, ... of
+// kThreads * kPer units of each of its rows.
 template <typename U>
 __global__ __launch_bounds__(kThreads) void pack_kernel(U* __restrict__ dst, const U* __restrict__ src,
                                                        const int32_t* __restrict__ cu, int B, int Lmax,
                                                        int left, int64_t units) {
-  const int64_t n = (int64_t)cu[B] * units;
-  const int64_t stride = (int64_t)gridDim.x * kThreads * kPer;
-  for (int64_t c0 = (int64_t)blockIdx.x * kThreads * kPer; c0 < n; c0 += stride) {
-    // the batch row at the chunk's start (uniform); units past its end look theirs up
-    const int b0 = first_row(cu, B, c0, units);
-    const int64_t end0 = (int64_t)cu[b0 + 1] * units, d0 = pack_delta(cu, b0, Lmax, left, units);
-    U v[kPer];
+  for (int b = blockIdx.y; b < B; b += gridDim.y) {
+    const int c0 = cu[b], L = cu[b + 1] - c0;
+    const int64_t n = (int64_t)L * units;
+    const U* s = src + ((int64_t)b * Lmax + (left ? Lmax - L : 0)) * units;
+    U* d = dst + (int64_t)c0 * units;
+    for (int64_t e0 = (int64_t)blockIdx.x * kThreads * kPer; e0 < n; e0 += (int64_t)gridDim.x * kThreads * kPer) {
+      U v[kPer];
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int64_t e = c0 + threadIdx.x + (int64_t)k * kThreads;
-      if (e < n) {
-        int64_t d = d0;
-        if (e >= end0) d = pack_delta(cu, row_of(cu, b0 + 1, e, units), Lmax, left, units);
-        v[k] = src[e + d];
+      for (int k = 0; k < kPer; ++k) {
+        const int64_t e = e0 + threadIdx.x + (int64_t)k * kThreads;
+        if (e < n) v[k] = s[e];
       }
-    }
 #pragma unroll
-    for (int k = 0; k < kPer; ++k) {
-      const int64_t e = c0 + threadIdx.x + (int64_t)k * kThreads;
-      if (e < n) dst[e] = v[k];
+      for (int k = 0; k < kPer; ++k) {
+        const int64_t e = e0 + threadIdx.x + (int64_t)k * kThreads;
+        if (e < n) d[e] = v[k];
+      }
     }
   }
 }
@@ -122,15 +100,18 @@ template <typename U>
 hipError_t launch_u(bool pack, void* dst, const void* src, const BatchDev& bd, int32_t Lmax, int32_t left,
                     int64_t row_bytes, hipStream_t st) {
   const int64_t units = row_bytes / (int64_t)sizeof(U);
-  const int64_t n = pack ? (int64_t)bd.num_rows * units : (int64_t)bd.num_seqs * Lmax * units;
-  const dim3 grid(clamp_grid((n + kThreads * kPer - 1) / (kThreads * kPer), 4096));
   if (pack) {
+    // chunks of the longest possible run (Lmax rows) over x, batch rows over y
+    const int64_t per = (int64_t)kThreads * kPer;
+    const dim3 grid(clamp_grid(((int64_t)Lmax * units + per - 1) / per, 65535), clamp_grid(bd.num_seqs, 65535));
     M2_LAUNCH("pack_rows", pack_kernel<U>, grid, dim3(kThreads), 0, st, (U*)dst, (const U*)src, bd.cu_seqlens,
               bd.num_seqs, Lmax, left, units);
-  } else {
-    M2_LAUNCH("unpack_rows", unpack_kernel<U>, grid, dim3(kThreads), 0, st, (U*)dst, (const U*)src,
-              bd.cu_seqlens, bd.num_seqs, Lmax, left, units);
+    return hipSuccess;
   }
+  const int64_t n = (int64_t)bd.num_seqs * Lmax * units;
+  const dim3 grid(clamp_grid((n + kThreads * kPer - 1) / (kThreads * kPer), 4096));
+  M2_LAUNCH("unpack_rows", unpack_kernel<U>, grid, dim3(kThreads), 0, st, (U*)dst, (const U*)src, bd.cu_seqlens,
+            bd.num_seqs, Lmax, left, units);
   return hipSuccess;
 }
 
