@@ -86,8 +86,7 @@ def scan_flops(wl, T):
     return alg, dense
 
 
-SCAN_KERNELS = ("scan_setup", "chunk_sums", "ssd_state", "scan_pass", "ssd_scan", "ssd_generic_state", "ssd_generic_scan",
-                "scan_prep", "ssd_chain")
+SCAN_KERNELS = ("scan_setup", "chunk_sums", "ssd_state", "scan_pass", "ssd_scan", "ssd_generic_state", "ssd_generic_scan")
 
 
 def digest(torch, tensors):
