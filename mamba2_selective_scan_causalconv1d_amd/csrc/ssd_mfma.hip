@@ -141,16 +141,20 @@ __device__ __forceinline__ void bst8(Rsrc r, uint32_t voff, uint32_t soff, u32x2
   __builtin_amdgcn_raw_buffer_store_b64(v, r, voff, soff, 0);
 }
 // 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds wave-uniform): a
-// buffer load that writes LDS, over `bytes` bytes from `base` (lane offsets at or past the
-// end write zeros).  Issued from inline assembly so that the compiler, which cannot tell
-// these LDS writes apart from the tiles being read meanwhile, adds no waits of its own;
-// the copies are waited for (vmcnt 0) before the barrier that publishes them.
+// buffer load that writes LDS, through a descriptor over `bytes` bytes from `base` (dma_rsrc:
+// one per chunk and tile kind; lane offsets voff at or past `bytes` write zeros, the uniform
+// soff moves the address without entering the range check).  Issued from inline assembly so
+// that the compiler, which cannot tell these LDS writes apart from the tiles being read
+// meanwhile, adds no waits of its own; the copies are waited for (vmcnt 0) before the barrier
+// that publishes them.
 typedef uint32_t u32x4s __attribute__((ext_vector_type(4)));
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // m0 is set here and used by nothing else
-__device__ __forceinline__ void dma16(const char* base, int bytes, const bf16_t* lds, uint32_t voff, uint32_t soff) {
+__device__ __forceinline__ u32x4s dma_rsrc(const char* base, int bytes) {
   const uint64_t a = (uint64_t)base;
-  const u32x4s rsrc = {(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes <= 0 ? 0u : (uint32_t)bytes, 0x00020000u};
+  return u32x4s{(uint32_t)a, (uint32_t)(a >> 32) & 0xffffu, bytes <= 0 ? 0u : (uint32_t)bytes, 0x00020000u};
+}
+__device__ __forceinline__ void dma16(const u32x4s& rsrc, const bf16_t* lds, uint32_t voff, uint32_t soff) {
   const uint32_t m0 = (uint32_t)(uintptr_t)(const M2_LDS void*)lds;
   asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
                :
@@ -332,26 +336,24 @@ __device__ __forceinline__ void load_bc(const bf16_t* rows, int nrb, uint32_t ld
                                         bf16_t* const (&dst)[NT], const DmaOfs& o, int w) {
   constexpr int nW = 2 * HB;
   static_assert(16 % nW == 0, "instruction split");
-  const char* base = reinterpret_cast<const char*>(rows);
+  const u32x4s rs = dma_rsrc(reinterpret_cast<const char*>(rows), nrb);
 #pragma unroll
   for (int i = 0; i < 16 * NT / nW; ++i) {
     const int tile = nW * i / 16;  // compile time
     const int k = (w + nW * i) & 15;
-    const uint32_t off = (uint32_t)(4 * k) * ldb;
-    dma16(base + off, nrb - (int)off, dst[tile] + 512 * k, o.bc, 2u * col[tile]);  // k % 4 == w % 4
+    dma16(rs, dst[tile] + 512 * k, o.bc + (uint32_t)(4 * k) * ldb, 2u * col[tile]);  // k % 4 == w % 4
   }
 }
 template <int HB>
 __device__ __forceinline__ void load_x(const bf16_t* rows, int nrb, uint32_t ldb, uint32_t colX,
                                        bf16_t (*sX)[kQ * kP], const DmaOfs& o, int w) {
   constexpr int nW = 2 * HB;
-  const char* base = reinterpret_cast<const char*>(rows);
+  const u32x4s rs = dma_rsrc(reinterpret_cast<const char*>(rows), nrb);
 #pragma unroll
   for (int i = 0; i < 8 * HB / nW; ++i) {
     const int t = w + nW * i;
     const int hh = t >> 3, k = t & 7;
-    const uint32_t off = (uint32_t)(8 * k) * ldb;
-    dma16(base + off, nrb - (int)off, sX[hh] + 512 * k, o.x, 2u * (colX + (uint32_t)(hh * kP)));
+    dma16(rs, sX[hh] + 512 * k, o.x + (uint32_t)(8 * k) * ldb, 2u * (colX + (uint32_t)(hh * kP)));
   }
 }
 
