@@ -174,7 +174,7 @@ mamba2_status mamba2_scan_prefill(void* dst, const void* xbc, const void* dt, co
   const ScanLayout lay = scan_layout(rb, dims, scan_segment_length(rb, dims, mfma));
   if (!workspace || workspace_bytes < lay.total) return MAMBA2_WORKSPACE_TOO_SMALL;
   if (((uintptr_t)workspace & 255) != 0) return MAMBA2_INVALID_ARGUMENT;
-  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace};
+  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace, false, nullptr, 0};
   return from_hip(launch_scan_prefill(a, (hipStream_t)stream));
 }
 
@@ -203,7 +203,7 @@ mamba2_status mamba2_scan_prefill_static(void* dst, const void* xbc, const void*
   if (lay.total > kStaticScratchBytes) return MAMBA2_WORKSPACE_TOO_SMALL;
   char* ws = static_scratch();
   if (!ws) return MAMBA2_HIP_ERROR;
-  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, ws};
+  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, ws, false, nullptr, 0};
   return from_hip(launch_scan_prefill(a, (hipStream_t)stream));
 }
 
@@ -303,8 +303,15 @@ mamba2_status mamba2_scan_prefill_snap(void* dst, const void* xbc, const void* d
   const ScanLayout lay = scan_layout(rb, dims, seg_len);
   if (!workspace || workspace_bytes < lay.total) return MAMBA2_WORKSPACE_TOO_SMALL;
   if (((uintptr_t)workspace & 255) != 0) return MAMBA2_INVALID_ARGUMENT;
-  // the snapshots are copies of segment entering states: every one must be stored
-  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace, true};
+  // the snapshots are the states entering the segments that start at the boundaries: the MFMA
+  // path's output kernel writes them as it obtains them; the generic path keeps every segment's
+  // state and copies those afterwards
+  if (scan_uses_mfma(dims)) {
+    ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace, false,
+               n > 0 ? ssm_snaps : nullptr, snap_every};
+    return from_hip(launch_scan_prefill(a, (hipStream_t)stream));
+  }
+  ScanArgs a{dst, xbc, dt, a_log, dt_bias, d, ssm_state, batch_dev(rb), *dims, lay, (char*)workspace, true, nullptr, 0};
   hipError_t e = launch_scan_prefill(a, (hipStream_t)stream);
   if (e != hipSuccess) return MAMBA2_HIP_ERROR;
   return from_hip(launch_ssm_snapshots(a, ssm_snaps, snapshot_max_per_seq(rb, snap_every), snap_every,

@@ -216,6 +216,11 @@ struct ScanArgs {
   // every segment's entering state must be left in seg_state (read afterwards, e.g. for
   // snapshots): no local-state walk may be left to the output kernels
   bool keep_seg_states;
+  // snapshots written by the MFMA path's output kernel (null: none): the state entering each
+  // segment that starts at a positive multiple of snap_every rows of its sequence, packed
+  // sequence after sequence as [count][H][P][N]
+  float* snaps;
+  int32_t snap_every;
 };
 
 hipError_t launch_scan_prefill(const ScanArgs& a, hipStream_t st);

@@ -626,10 +626,11 @@ __global__ __launch_bounds__(256, 2) void ssd_scan_kernel(
     bf16_t* __restrict__ y, const bf16_t* __restrict__ xbc, const bf16_t* __restrict__ dt,
     const float* __restrict__ a_log, const float* __restrict__ dt_bias, const float* __restrict__ Dp,
     float* __restrict__ pool, const int32_t* __restrict__ slots, const uint8_t* __restrict__ fresh, SegPtrs sp,
-    int H, int G, int nitems) {
+    int H, int G, int nitems, const int32_t* __restrict__ cu, float* __restrict__ snaps, int snapE) {
   constexpr int HB = 2;
   __shared__ __attribute__((aligned(16))) bf16_t sB[kQ * kN];
   __shared__ __attribute__((aligned(16))) bf16_t sC[kQ * kN];
+  __shared__ int sRed[4];
   __shared__ __attribute__((aligned(16))) bf16_t sX[HB][kQ * kP];
   __shared__ __attribute__((aligned(16))) u32x4 sM[HB][kTiles][64];
   __shared__ __attribute__((aligned(16))) Decay sD[2][HB];
@@ -693,6 +694,27 @@ __global__ __launch_bounds__(256, 2) void ssd_scan_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) S[t][nb] = *reinterpret_cast<const f32x4*>(in + state_elem(ph, t, nb, lane));
+  }
+
+  // a segment starting at a positive multiple of snapE rows of its sequence: the state entering
+  // it (frame scale 1 here) is the snapshot at that boundary, the sequence's (offset / snapE)-th,
+  // after those of the sequences before it (each with (length - 1) / snapE)
+  if (snaps) {
+    const int off = si.y - uniform(cu[si.x]);
+    if (off > 0 && off % snapE == 0) {  // uniform over the workgroup
+      int before = 0;
+      for (int s2 = (int)threadIdx.x; s2 < si.x; s2 += 256) before += (cu[s2 + 1] - cu[s2] - 1) / snapE;
+#pragma unroll
+      for (int o = 32; o >= 1; o >>= 1) before += __shfl_xor(before, o, 64);
+      if (lane == 0) sRed[w] = before;
+      __syncthreads();
+      const int idx = uniform(sRed[0] + sRed[1] + sRed[2] + sRed[3]) + off / snapE - 1;
+      float* dst = snaps + ((size_t)idx * H + h) * (size_t)(kP * kN);
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) *reinterpret_cast<f32x4*>(dst + state_elem(ph, t, nb, lane)) = S[t][nb];
+    }
   }
 
   float lam = 1.f, lsum = 0.f;
@@ -934,7 +956,7 @@ hipError_t launch_scan_mfma(const ScanArgs& a, hipStream_t st) {
   if (e != hipSuccess) return e;
   M2_LAUNCH("ssd_scan", ssd_scan_kernel, dim3((unsigned)nitems), dim3(256), 0, st, (bf16_t*)a.y,
             (const bf16_t*)a.xbc, (const bf16_t*)a.dt, a.a_log, a.dt_bias, a.D, a.ssm_state, a.bd.slots,
-            a.bd.fresh, sp, d.nheads, d.ngroups, nitems);
+            a.bd.fresh, sp, d.nheads, d.ngroups, nitems, a.bd.cu_seqlens, a.snaps, a.snap_every);
   return hipSuccess;
 }
 

@@ -226,20 +226,22 @@ def test_snapshot_edge_cases(gpu):
 
 
 @pytest.mark.parametrize("make", ["long_prefill", "decay_span_prefill"])
-def test_tail_walk_matches_stored_segment_states(gpu, make):
-    """The plain prefill lets the output workgroup of a segment recompute a predecessor's local
-    state when that predecessor decays below e^-60 (nothing else reads it); the snapshot entry
-    stores, chains and reads every segment's state.  With snapshots every 1024 rows both take the
-    same 1024-row segments, so y and the final slots agree bit for bit: on the long prefill
-    (every segment decays that much) and on the decay-span batch (mixed per head pair)."""
+def test_long_snapshots_match_plain_run_and_oracle(gpu, make):
+    """Snapshots every 1024 rows on the long shapes: the snapshot entry takes the plain
+    prefill's 1024-row segments and kernels (a segment whose predecessor decays below e^-60
+    recomputes that predecessor's local state; the others read the chained segment states), so
+    y and the final slots agree with the plain run bit for bit; each snapshot, the state entering
+    its boundary segment, is compared with the oracle's (the long prefill: every segment decays
+    that much; the decay-span batch: mixed per head pair, two sequences resuming)."""
     wl = getattr(W, make)()
     b = gpu.batch_of(wl)
     p = gpu.Params(wl)
     xa_g, _ = gpu.gpu_conv(wl, wl.xbc, wl.conv_pool, b, p)
     y_plain, sp_plain = gpu.gpu_scan(wl, xa_g, wl.dt, wl.ssm_pool, b, p)
-    y_snap, sp_snap, _ = _gpu_scan_snap(gpu, wl, xa_g, 1024, b, p)
+    y_snap, sp_snap, ssn_g = _gpu_scan_snap(gpu, wl, xa_g, 1024, b, p)
     same_y = np.array_equal(y_plain, y_snap)
     same_states = np.array_equal(sp_plain, sp_snap)
-    say("[%s] plain vs stored segment states: y bit-identical %s, slots bit-identical %s" % (wl.name, same_y,
-                                                                                            same_states))
+    say("[%s] snapshot entry vs plain: y bit-identical %s, slots bit-identical %s" % (wl.name, same_y, same_states))
     assert same_y and same_states
+    _, _, ssn_o = oracle_scan_snap(wl, xa_g, 1024)
+    say("  %d ssm snapshots: %.3g of bar" % (len(ssn_o), assert_close(ssn_g, ssn_o, F32_BAR, "ssm snapshots")))
