@@ -26,26 +26,14 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Sum of v over the workgroup (every thread gets it).  Called once per loop iteration by
-// every thread of the workgroup.
-__device__ int block_sum(int v) {
-  __shared__ int red[kThreads / 64];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  __syncthreads();  // red may still be read by the previous call
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int i = 0; i < kThreads / 64; ++i) t += red[i];
-  return t;
-}
-
-// first(s): snapshots held by the sequences before s.
+// first(s): snapshots held by the sequences before s, summed by each wave on its own (no
+// barrier: every wave of the workgroup gets the same total).
 __device__ int snap_first(const int32_t* __restrict__ cu, int s, int E) {
   int v = 0;
-  for (int i = threadIdx.x; i < s; i += kThreads) v += (cu[i + 1] - cu[i] - 1) / E;
-  return block_sum(v);
+  for (int i = threadIdx.x & 63; i < s; i += 64) v += (cu[i + 1] - cu[i] - 1) / E;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
 }
 
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
