@@ -131,6 +131,10 @@ def test_entry_points_reject_before_launch(ops):
         _lib.WORKSPACE_TOO_SMALL
     # decode needs run lengths of 1
     assert L.mamba2_scan_decode(p, p, p, p, p, p, p, b.ref(), ctypes.byref(d), None) == _lib.RUN_LENGTHS
+    # decode launches past the grid's limits (4096 requests x 65536 heads x 8 blocks = 2^31 items)
+    wide = _dims(ops, nheads=65536, headdim=64, d_state=128, ngroups=1, pool_slots=4096)
+    many = ops.RecurrentBatch([1] * 4096, list(range(4096)), [0] * 4096, device=None)
+    assert L.mamba2_scan_decode(p, p, p, p, p, p, p, many.ref(), ctypes.byref(wide), None) == _lib.NOT_IMPLEMENTED
     # norm argument checks
     assert L.mamba2_gated_rmsnorm(p, p, p, p, 3, 1e-5, 4, 64, 1, None) == _lib.INVALID_ARGUMENT
     assert L.mamba2_gated_rmsnorm(p, p, p, p, 2, -1.0, 4, 64, 1, None) == _lib.INVALID_ARGUMENT
