@@ -602,7 +602,8 @@ def run_layer(args, torch, ops, dev, e0, e1, xbc, z, dt, xa, y, out, conv_w, con
     gemms = []
     for (n, k), us in zip(shapes, lin):
         fl = 2.0 * T * n * k
-        gemms.append({"N": n, "K": k, "us": us, "TFLOPs": fl / (us * 1e-6) / 1e12,
+        by = 2.0 * (T * k + n * k + T * n)  # x, w and dst once
+        gemms.append({"N": n, "K": k, "us": us, "TFLOPs": fl / (us * 1e-6) / 1e12, "GBs": by / (us * 1e-6) / 1e9,
                       "frac_mfma": fl / (us * 1e-6) / 1e12 / MFMA_BF16_PEAK_TFLOPS})
     tot_fl = sum(2.0 * T * n * k for n, k in shapes)
     tot_us = sum(lin)

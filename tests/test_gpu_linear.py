@@ -2,7 +2,8 @@
 
 dst = x . w^T in bf16 with fp32 accumulation against the oracle's double sum rounded once:
 element by element within the bf16 bar 2e-2 (1 + |ref|), on ragged shapes for both tilings
-(M, N not multiples of the 128 x 128 or 256 x 256 tile, K a multiple of 64 or not) and, at
+(M, N not multiples of the 128 x 128 or 256 x 256 tile, K a multiple of 64 or not; narrow
+outputs of 8 to 64 columns over long K) and, at
 the long-prefill layer's in_proj and out_proj shapes (65536 rows, model width 1536), on
 sampled rows.  The layer case
 runs in_proj (three calls on row slices of one weight) -> conv -> scan -> norm -> out_proj,
@@ -33,7 +34,8 @@ def _bf16(rng, shape, scale=1.0):
 
 @pytest.mark.parametrize("M,N,K", [(1, 8, 8), (37, 48, 64), (130, 136, 200), (257, 264, 72), (128, 128, 1536),
                                    (300, 3328, 96), (300, 264, 128), (257, 520, 64), (1000, 3328, 1536),
-                                   (512, 256, 3072)])
+                                   (512, 256, 3072), (37, 48, 1536), (1000, 64, 256), (1, 8, 128),
+                                   (130, 24, 384), (4099, 56, 640)])
 def test_linear_ragged_shapes(gpu, M, N, K):
     ops = gpu.ops
     rng = np.random.default_rng(100 + M)
